@@ -1,0 +1,199 @@
+"""Grouped expert MLP (gate_up -> ScaledSwiGLU -> down), CPU oracle.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What it computes [BioNeMo, section "GroupedLinear": every expert keeps its own
+weight, gate_up has 2 x intermediate outputs and no bias, and one call takes
+the rows of all experts with their split_sizes; section "MXFP8与融合MLP": the
+expert FFN is gate_up, then ScaledSwiGLU, which multiplies the SwiGLU output
+by the routing probabilities, then down; the fused operator has a matching
+backward; in MXFP8 the BF16 master weights and the activations are quantized
+before each low-precision GEMM].
+
+The loop over experts below is the structure of the naive per-expert
+baseline the pages contrast with the grouped call.  Per expert e with rows
+Xp_e (M_e rows), pp_e the permuted probabilities:
+
+  forward
+    A1  = Xp_e W1_e^T                          fp32 accumulate; saved as bf16
+    g, u = A1[:, :I], A1[:, I:]                (gate = first half: parity
+                                                unpinned, a convention)
+    A2  = pp_e * silu(g) * u                   fp32, from the fp32 A1
+    A2  -> bf16 (BF16 mode) / rowwise MXFP8 along I (MXFP8 mode)
+    Yp_e = bf16(A2 W2_e^T)
+
+  backward (dYp = permuted upstream gradient)
+    dA2  = dYp_e W2_e                          fp32
+    dW2_e = bf16(dYp_e^T A2_e)                 contraction over the rows of e
+    g, u from the saved bf16 A1; s = silu(g), sig = sigmoid(g)
+    dg  = dA2 pp u sig (1 + g (1 - sig)),  du = dA2 pp s
+    dpp = sum_i dA2 s u                        fp32 row sum
+    dA1 = [dg, du] -> bf16 / rowwise MXFP8 along 2I
+    dXp_e = bf16(dA1 W1_e)
+    dW1_e = bf16(dA1_e^T Xp_e)
+  experts with no rows: nothing in Yp, dW1_e = dW2_e = 0.
+
+MXFP8 mode quantizes every GEMM operand along that GEMM's contraction axis:
+forward Xp and W1 along H, A2 and W2 along I (rowwise); dgrad dYp along H
+(rowwise) with W2 along H (columnwise of [H, I]), dA1 along 2I with W1 along
+2I (columnwise of [2I, H]); the weight-gradient GEMMs contract over the rows of
+an expert, so dYp, A2, dA1, Xp enter them quantized in blocks of 32 rows that
+restart at the expert's first row.  dA2 is never quantized (it only feeds the
+SwiGLU backward).
+
+``exact=True`` keeps every intermediate in float64 with no rounding (BF16 mode
+only): the check mode the formula pins use against autograd.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import mx as _mx
+from . import route as _route
+
+
+def _silu(g: torch.Tensor) -> torch.Tensor:
+    return g / (1.0 + torch.exp(-g))
+
+
+def _sigmoid(g: torch.Tensor) -> torch.Tensor:
+    return 1.0 / (1.0 + torch.exp(-g))
+
+
+class _Mode:
+    def __init__(self, precision: str, exact: bool):
+        assert precision in ("bf16", "mxfp8")
+        assert not (exact and precision != "bf16")
+        self.mx = precision == "mxfp8"
+        self.exact = exact
+        self.acc = torch.float64 if exact else torch.float32
+
+    def store(self, t: torch.Tensor) -> torch.Tensor:
+        """Round a materialized tensor (bf16 storage unless exact)."""
+        return t if self.exact else t.to(torch.bfloat16)
+
+    def val(self, t: torch.Tensor) -> torch.Tensor:
+        return t.to(self.acc)
+
+    # operand preparation for each GEMM (along its contraction axis)
+    def rows_op(self, t):           # contraction axis = last dim
+        return _mx.qdq_rows(t).to(self.acc) if self.mx else self.val(t)
+
+    def cols_op(self, t):           # contraction axis = first dim (weights)
+        return _mx.qdq_cols(t).to(self.acc) if self.mx else self.val(t)
+
+    def group_cols_op(self, t):     # contraction over the rows of one expert
+        if not self.mx:
+            return self.val(t)
+        return _mx.qdq_cols_grouped(t, [t.shape[0]]).to(self.acc)
+
+
+def grouped_mlp_fwd(xp, split, w1, w2, pp, precision="bf16", exact=False) -> dict:
+    """Forward of all experts.  xp bf16 [A, H]; split int [E]; w1[e] bf16
+    [2I, H]; w2[e] bf16 [H, I]; pp fp32 [A].
+
+    Returns yp [A, H] and the saved tensors: a1 (bf16 [A, 2I]), a2 (operand of
+    the down GEMM as used), a2_w and xp_w (operands of the weight-gradient
+    GEMMs as used; dequantized values in MXFP8 mode).
+    """
+    m = _Mode(precision, exact)
+    split = np.asarray(split, dtype=np.int64)
+    A, H = xp.shape
+    I = w2[0].shape[1]
+    pp = torch.as_tensor(np.asarray(pp, dtype=np.float64 if exact else np.float32))
+    out_dt = torch.float64 if exact else torch.bfloat16
+    yp = torch.zeros((A, H), dtype=out_dt)
+    a1s = torch.zeros((A, 2 * I), dtype=out_dt)
+    a2s = torch.zeros((A, I), dtype=m.acc)
+    a2w = torch.zeros((A, I), dtype=m.acc)
+    xpw = torch.zeros((A, H), dtype=m.acc)
+    r0 = 0
+    for e, n in enumerate(split):
+        if n == 0:
+            continue
+        rs = slice(r0, r0 + n)
+        X = m.rows_op(xp[rs])
+        W1 = m.rows_op(w1[e])
+        A1 = X @ W1.T
+        g, u = A1[:, :I], A1[:, I:]
+        A2 = pp[rs].to(m.acc)[:, None] * _silu(g) * u
+        a1s[rs] = m.store(A1)
+        if m.mx:
+            a2op = m.rows_op(A2)
+            a2w[rs] = m.group_cols_op(A2)
+        else:
+            a2op = m.val(m.store(A2))
+            a2w[rs] = a2op
+        a2s[rs] = a2op
+        W2 = m.rows_op(w2[e])
+        yp[rs] = m.store(a2op @ W2.T)
+        xpw[rs] = m.group_cols_op(xp[rs])
+        r0 += n
+    return {"yp": yp, "a1": a1s, "a2": a2s, "a2_w": a2w, "xp_w": xpw}
+
+
+def grouped_mlp_bwd(dyp, xp, split, w1, w2, pp, saved, precision="bf16", exact=False) -> dict:
+    """Backward of all experts.  Returns dxp [A, H], dw1[e] [2I, H],
+    dw2[e] [H, I] (bf16 unless exact), dpp fp32 [A] and the dA1 operands."""
+    m = _Mode(precision, exact)
+    split = np.asarray(split, dtype=np.int64)
+    A, H = dyp.shape
+    I = w2[0].shape[1]
+    E = len(w1)
+    pp = torch.as_tensor(np.asarray(pp, dtype=np.float64 if exact else np.float32))
+    out_dt = torch.float64 if exact else torch.bfloat16
+    dxp = torch.zeros((A, H), dtype=out_dt)
+    dpp = torch.zeros(A, dtype=m.acc)
+    dw1 = [torch.zeros((2 * I, H), dtype=out_dt) for _ in range(E)]
+    dw2 = [torch.zeros((H, I), dtype=out_dt) for _ in range(E)]
+    r0 = 0
+    for e, n in enumerate(split):
+        if n == 0:
+            continue
+        rs = slice(r0, r0 + n)
+        dY = m.rows_op(dyp[rs])
+        dA2 = dY @ m.cols_op(w2[e])
+        dw2[e] = m.store(m.group_cols_op(dyp[rs]).T @ saved["a2_w"][rs].to(m.acc))
+        a1 = saved["a1"][rs].to(m.acc)
+        g, u = a1[:, :I], a1[:, I:]
+        s, sig = _silu(g), _sigmoid(g)
+        p = pp[rs].to(m.acc)[:, None]
+        dg = dA2 * p * u * sig * (1.0 + g * (1.0 - sig))
+        du = dA2 * p * s
+        dpp[rs] = (dA2 * s * u).sum(dim=1)
+        dA1 = torch.cat([dg, du], dim=1)
+        if m.mx:
+            dA1op = m.rows_op(dA1)
+            dA1w = m.group_cols_op(dA1)
+        else:
+            dA1op = m.val(m.store(dA1))
+            dA1w = dA1op
+        dxp[rs] = m.store(dA1op @ m.cols_op(w1[e]))
+        dw1[e] = m.store(dA1w.T @ saved["xp_w"][rs].to(m.acc))
+        r0 += n
+    return {"dxp": dxp, "dw1": dw1, "dw2": dw2, "dpp": dpp.to(torch.float32) if not exact else dpp}
+
+
+def layer_step(logits, x, w1, w2, dy, k, precision="bf16", exact=False,
+               softmax_all=False, with_backward=True) -> dict:
+    """One MoE layer step: route, permute, grouped MLP, unpermute; then the
+    backward: permute dY, grouped MLP backward, unpermute dXp, routing
+    backward."""
+    r = _route.route(logits, k, softmax_all, np.float64 if exact else np.float32)
+    xp = _route.permute(x, r["src_token"])
+    pp = _route.permute_probs(r["topk_prob"], r["dest_row"])
+    fwd = grouped_mlp_fwd(xp, r["split_sizes"], w1, w2, pp, precision, exact)
+    acc = torch.float64 if exact else torch.float32
+    out_dt = torch.float64 if exact else torch.bfloat16
+    y = _route.unpermute(fwd["yp"], r["dest_row"], out_dt, acc)
+    res = {"route": r, "xp": xp, "pp": pp, "fwd": fwd, "y": y}
+    if not with_backward:
+        return res
+    dyp = _route.permute(dy, r["src_token"])
+    bwd = grouped_mlp_bwd(dyp, xp, r["split_sizes"], w1, w2, pp, fwd, precision, exact)
+    dx = _route.unpermute(bwd["dxp"], r["dest_row"], out_dt, acc)
+    dprob = bwd["dpp"].numpy()[r["dest_row"].astype(np.int64)]
+    dlogits = _route.route_bwd(logits, r["topk_expert"], dprob, softmax_all)
+    res.update({"dyp": dyp, "bwd": bwd, "dx": dx, "dprob": dprob, "dlogits": dlogits})
+    return res

@@ -1,0 +1,181 @@
+"""Pins of the grouped-MLP oracle.
+
+* special case: one expert, top-1, probability 1 is a dense SwiGLU MLP,
+  checked against torch.nn.functional (float64);
+* an independent formulation: a loop over tokens and their picks (no
+  grouping, no permutation) in float64, differentiated by torch.autograd;
+  the oracle's hand-written backward (exact mode) must agree;
+* central finite differences on a 2-expert, 8-token, H = I = 32 case;
+* invariants: empty experts give exact zero weight gradients and do not
+  touch the output; doubling the probabilities doubles the output exactly
+  (BF16 and MXFP8); MXFP8 on operands already on the MXFP8 grid equals BF16.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import mlp, mx, route
+
+
+def _rand(shape, rng, std=1.0, dtype=torch.bfloat16):
+    return torch.from_numpy((rng.standard_normal(shape) * std).astype(np.float32)).to(dtype)
+
+
+def _case(T, H, I, E, seed, wstd=0.1):
+    rng = np.random.default_rng(seed)
+    return {
+        "logits": rng.standard_normal((T, E)).astype(np.float32),
+        "x": _rand((T, H), rng),
+        "w1": [_rand((2 * I, H), rng, wstd) for _ in range(E)],
+        "w2": [_rand((H, I), rng, wstd) for _ in range(E)],
+        "dy": _rand((T, H), rng),
+    }
+
+
+def test_dense_reduction():
+    c = _case(T=48, H=64, I=96, E=1, seed=21)
+    r = mlp.layer_step(c["logits"], c["x"], c["w1"], c["w2"], c["dy"], k=1, exact=True,
+                       with_backward=False)
+    assert np.all(r["route"]["topk_prob"] == 1.0)
+    x = c["x"].double()
+    w1, w2 = c["w1"][0].double(), c["w2"][0].double()
+    I = w2.shape[1]
+    ref = F.linear(F.silu(F.linear(x, w1[:I])) * F.linear(x, w1[I:]), w2)
+    assert torch.allclose(r["y"], ref, rtol=1e-12, atol=1e-12)
+    # default (bf16 materialization) stays within a few bf16 ulps of it
+    rb = mlp.layer_step(c["logits"], c["x"], c["w1"], c["w2"], c["dy"], k=1, with_backward=False)
+    rel = (rb["y"].double() - ref).norm() / ref.norm()
+    assert rel < 4e-3
+
+
+def _token_loop_forward(logits, x, w1, w2, k, softmax_all=False):
+    """Per token, per pick: y_t += p_tj * W2_e (silu(W1g_e x_t) * (W1u_e x_t))."""
+    T, E = logits.shape
+    sel = route.topk_select(logits.detach().numpy(), k)
+    I = w2[0].shape[1]
+    ys = []
+    for t in range(T):
+        s = torch.from_numpy(sel[t]).long()
+        if softmax_all:
+            p = torch.softmax(logits[t], 0)[s]
+        else:
+            p = torch.softmax(logits[t][s], 0)
+        acc = torch.zeros(x.shape[1], dtype=x.dtype)
+        for j in range(k):
+            e = int(sel[t, j])
+            h = w1[e] @ x[t]
+            acc = acc + p[j] * (w2[e] @ (F.silu(h[:I]) * h[I:]))
+        ys.append(acc)
+    return torch.stack(ys)
+
+
+@pytest.mark.parametrize("T,H,I,E,k,softmax_all", [(24, 32, 64, 4, 2, False),
+                                                   (20, 64, 32, 6, 3, True),
+                                                   (16, 32, 32, 3, 1, False)])
+def test_backward_vs_autograd(T, H, I, E, k, softmax_all):
+    c = _case(T, H, I, E, seed=T + E)
+    r = mlp.layer_step(c["logits"], c["x"], c["w1"], c["w2"], c["dy"], k, exact=True,
+                       softmax_all=softmax_all)
+    L = torch.from_numpy(c["logits"]).double().requires_grad_(True)
+    x = c["x"].double().requires_grad_(True)
+    w1 = [w.double().requires_grad_(True) for w in c["w1"]]
+    w2 = [w.double().requires_grad_(True) for w in c["w2"]]
+    y = _token_loop_forward(L, x, w1, w2, k, softmax_all)
+    assert torch.allclose(r["y"], y.detach(), rtol=1e-10, atol=1e-12)
+    (y * c["dy"].double()).sum().backward()
+    assert torch.allclose(r["dx"], x.grad, rtol=1e-9, atol=1e-11)
+    for e in range(E):
+        assert torch.allclose(r["bwd"]["dw1"][e], w1[e].grad, rtol=1e-9, atol=1e-11)
+        assert torch.allclose(r["bwd"]["dw2"][e], w2[e].grad, rtol=1e-9, atol=1e-11)
+    assert np.allclose(r["dlogits"], L.grad.numpy(), rtol=1e-4, atol=1e-6)
+
+
+def test_finite_differences():
+    c = _case(T=8, H=32, I=32, E=2, seed=31, wstd=0.2)
+    k = 1
+    r = mlp.layer_step(c["logits"], c["x"], c["w1"], c["w2"], c["dy"], k, exact=True)
+    dy = c["dy"].double()
+
+    def loss(x=None, w1=None, w2=None):
+        rr = mlp.layer_step(c["logits"], x if x is not None else c["x"].double(),
+                            w1 or [w.double() for w in c["w1"]],
+                            w2 or [w.double() for w in c["w2"]], c["dy"], k, exact=True,
+                            with_backward=False)
+        return float((rr["y"] * dy).sum())
+
+    h = 1e-6
+    for (t, i) in [(0, 0), (5, 17), (7, 31)]:
+        xp_, xm_ = c["x"].double().clone(), c["x"].double().clone()
+        xp_[t, i] += h
+        xm_[t, i] -= h
+        num = (loss(x=xp_) - loss(x=xm_)) / (2 * h)
+        assert abs(num - float(r["dx"][t, i])) < 1e-6 * max(1, abs(num))
+    for e in range(2):
+        if r["route"]["split_sizes"][e] == 0:
+            continue
+        for (a, b) in [(0, 0), (40, 3), (63, 31)]:
+            W = [w.double().clone() for w in c["w1"]]
+            Wm = [w.double().clone() for w in c["w1"]]
+            W[e][a, b] += h
+            Wm[e][a, b] -= h
+            num = (loss(w1=W) - loss(w1=Wm)) / (2 * h)
+            assert abs(num - float(r["bwd"]["dw1"][e][a, b])) < 1e-6 * max(1, abs(num))
+        for (a, b) in [(0, 0), (12, 30)]:
+            W = [w.double().clone() for w in c["w2"]]
+            Wm = [w.double().clone() for w in c["w2"]]
+            W[e][a, b] += h
+            Wm[e][a, b] -= h
+            num = (loss(w2=W) - loss(w2=Wm)) / (2 * h)
+            assert abs(num - float(r["bwd"]["dw2"][e][a, b])) < 1e-6 * max(1, abs(num))
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+def test_empty_expert(precision):
+    c = _case(T=40, H=64, I=64, E=4, seed=41)
+    c["logits"][:, 2] = -100.0           # expert 2 never picked
+    r = mlp.layer_step(c["logits"], c["x"], c["w1"], c["w2"], c["dy"], 2, precision)
+    assert r["route"]["split_sizes"][2] == 0
+    assert not r["bwd"]["dw1"][2].float().any() and not r["bwd"]["dw2"][2].float().any()
+    w1 = list(c["w1"])
+    w1[2] = w1[2] * 3
+    r2 = mlp.layer_step(c["logits"], c["x"], w1, c["w2"], c["dy"], 2, precision,
+                        with_backward=False)
+    assert torch.equal(r["y"], r2["y"])
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+def test_prob_scaling_is_exact(precision):
+    c = _case(T=32, H=64, I=64, E=3, seed=51)
+    r = route.route(c["logits"], 2)
+    xp = route.permute(c["x"], r["src_token"])
+    pp = route.permute_probs(r["topk_prob"], r["dest_row"])
+    a = mlp.grouped_mlp_fwd(xp, r["split_sizes"], c["w1"], c["w2"], pp, precision)
+    b = mlp.grouped_mlp_fwd(xp, r["split_sizes"], c["w1"], c["w2"], 2 * pp, precision)
+    assert torch.equal(b["yp"].float(), 2 * a["yp"].float())
+
+
+def _on_mx_grid(t, rng):
+    """Round a tensor to values that MXFP8 represents exactly along rows
+    (and, for 32x32 tiles with a common scale, along columns too)."""
+    q = mx.qdq_rows(t)
+    return q.to(torch.bfloat16)
+
+
+def test_mx_equals_bf16_on_representable_gate_up():
+    rng = np.random.default_rng(61)
+    xp = _on_mx_grid(_rand((64, 64), rng), rng)
+    w1 = [_on_mx_grid(_rand((128, 64), rng, 0.1), rng)]
+    assert torch.equal(mx.qdq_rows(xp), xp.float())
+    a_bf = xp.float() @ w1[0].float().T
+    a_mx = mx.qdq_rows(xp) @ mx.qdq_rows(w1[0]).T
+    assert torch.equal(a_bf, a_mx)
+
+
+def test_mx_close_to_bf16():
+    c = _case(T=64, H=64, I=128, E=4, seed=71)
+    rb = mlp.layer_step(c["logits"], c["x"], c["w1"], c["w2"], c["dy"], 2, "bf16")
+    rm = mlp.layer_step(c["logits"], c["x"], c["w1"], c["w2"], c["dy"], 2, "mxfp8")
+    for key in ("y", "dx"):
+        rel = (rm[key].float() - rb[key].float()).norm() / rb[key].float().norm()
+        assert 0 < rel < 0.15, (key, rel)
