@@ -1,0 +1,295 @@
+/*
+ * moe_mi355x.h -- C ABI of libmoe_mi355x.so: the MoE expert feed-forward as
+ * one grouped operation on an AMD Instinct MI355X (gfx950), in BF16 and
+ * MXFP8, forward and backward.
+ *
+ * Source pages (short tags used below):
+ *   [BioNeMo]   "NVIDIA发布BioNeMo MoE配方：八卡B200训练Mixtral-8x7B吞吐提升至
+ *               Hugging Face基线 2.21 倍" (scopeai.cc), sections
+ *               "MoE训练的瓶颈与TE的对应能力" (bottlenecks), "GroupedLinear",
+ *               "MXFP8与融合MLP" (MXFP8 and the fused MLP).
+ *   [AutoModel] "英伟达开源MoE加速神器：一行代码，微调快3.7倍"
+ *               (openai-hub.com), sections "MoE 微调的痛点" (sparse
+ *               activation) and "专家并行" (expert parallelism).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Types.  bf16 tensors are passed as uint16_t* (bfloat16 bit patterns);
+ * MXFP8 tensors are two uint8_t arrays: E4M3 codes and E8M0 scale bytes (one
+ * per 32 consecutive values along the stated axis).  All tensors are dense
+ * row-major unless stated otherwise.  Every pointer is a DEVICE pointer on the
+ * current HIP device, except the per-expert pointer tables of the grouped
+ * MLP calls, which are HOST arrays of device pointers.
+ *
+ * Ownership.  The caller owns every buffer, including the workspace, whose
+ * size moe_workspace_bytes() returns.  The library allocates no device or
+ * host memory in these calls and keeps no pointer after it returns; host
+ * pointer tables are copied into kernel arguments, so they may be freed on
+ * return.  Device buffers must stay valid until the stream has executed the
+ * work (ordinary stream semantics).
+ *
+ * Asynchrony.  Every call only enqueues kernels on `stream` (a hipStream_t;
+ * NULL = the default stream) and returns; none synchronizes the host.  The
+ * per-expert row counts (split sizes) stay on the device; buffers are sized
+ * from the total row count T*k on the host.
+ *
+ * Errors.  Every call returns a moe_status; it never aborts or throws.  All
+ * argument checks happen before any launch, so a call that returns an error
+ * has enqueued nothing.  Device-data preconditions (split sizes summing to
+ * the row count, expert ids below E, valid permutations) are the caller's
+ * duty and are not checked.  MOE_ERR_HIP reports a failed launch; the HIP
+ * error itself is left for the caller's next hipGetLastError().
+ *
+ * Alignment.  Tensor base pointers must be 16-byte aligned (MOE_ERR_ALIGN).
+ *
+ * Threading.  Stateless apart from a cached device-architecture check; calls
+ * may be made from several host threads on different streams, provided that
+ * they do not share output or workspace buffers.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,         /* a required pointer is NULL                       */
+    MOE_ERR_SHAPE = 2,        /* a size is out of range or not a needed multiple */
+    MOE_ERR_ALIGN = 3,        /* a tensor pointer is not 16-byte aligned          */
+    MOE_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required       */
+    MOE_ERR_UNSUPPORTED = 5,  /* current device is not gfx950, or unknown option  */
+    MOE_ERR_HIP = 6,          /* a HIP launch or query failed                     */
+    MOE_ERR_ARG = 7           /* an enum or flag argument has an invalid value    */
+} moe_status;
+
+typedef enum moe_precision {
+    MOE_BF16 = 0,             /* BF16 operands, fp32 accumulation                 */
+    MOE_MXFP8 = 1             /* E4M3 operands, E8M0 scale per 32 K-values        */
+} moe_precision;
+
+/* moe_route flags */
+#define MOE_ROUTE_RENORM 0u       /* softmax over the k picked logits (default) */
+#define MOE_ROUTE_SOFTMAX_ALL 1u  /* softmax over all E logits, taken at the picks */
+
+/* moe_workspace_bytes ops */
+typedef enum moe_op {
+    MOE_OP_ROUTE = 0,
+    MOE_OP_MLP_FWD = 1,
+    MOE_OP_MLP_BWD = 2
+} moe_op;
+
+/* Limits of this version. */
+#define MOE_MAX_EXPERTS 64
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(int status);
+
+/* 1 if the current HIP device is a gfx950 (MI355X / MI350 class), else 0. */
+int moe_device_supported(void);
+
+/*
+ * moe_route -- top-k routing, split sizes and the stable permutation.
+ * [AutoModel, "MoE 微调的痛点": each token activates only a few experts;
+ *  BioNeMo, "GroupedLinear": the grouped call takes per-expert token counts,
+ *  split_sizes.]
+ *
+ * logits       fp32 [T, E]  router logits.
+ * T            tokens, 0 <= T, T*k <= INT32_MAX.   E: experts, 1..64.
+ * k            picks per token, 1 <= k <= E.
+ * flags        MOE_ROUTE_RENORM or MOE_ROUTE_SOFTMAX_ALL.
+ * topk_expert  int32 [T, k] out: picked experts, largest logit first; equal
+ *              logits go to the lower expert index.  Selection uses the fp32
+ *              logits themselves.
+ * topk_prob    fp32 [T, k]  out: routing probability of each pick.
+ * split_sizes  int32 [E]    out: rows routed to each expert (sum = T*k).
+ * expert_offsets int32 [E+1] out: exclusive prefix sum of split_sizes.
+ * dest_row     int32 [T, k] out: row of pick (t, j) in the expert-grouped
+ *              order; inside an expert, rows follow ascending token index.
+ * src_token    int32 [T*k]  out: token of each grouped row.
+ * workspace    device scratch of moe_workspace_bytes(MOE_OP_ROUTE, ...) bytes.
+ * T = 0 is valid: split_sizes and expert_offsets are written as zeros.
+ */
+int moe_route(const float* logits, int64_t T, int E, int k, uint32_t flags,
+              int32_t* topk_expert, float* topk_prob, int32_t* split_sizes,
+              int32_t* expert_offsets, int32_t* dest_row, int32_t* src_token,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_route_bwd -- gradient of the router logits from the gradient of the
+ * grouped-row probabilities (backward of the probabilities moe_route made).
+ *
+ * topk_prob    fp32 [T, k]  probabilities from moe_route.
+ * dprob_perm   fp32 [T*k]   gradient per grouped row (from grouped_mlp_bwd).
+ * dest_row     int32 [T, k] from moe_route.
+ * topk_expert  int32 [T, k] from moe_route.
+ * logits       fp32 [T, E]  required with MOE_ROUTE_SOFTMAX_ALL, else may be NULL.
+ * dlogits      fp32 [T, E]  out.  Renormalized softmax: for pick j of token t,
+ *              p_j (dp_j - sum_i p_i dp_i); 0 for experts not picked.
+ *              Full softmax P: P_e (g_e - sum_j p_j dp_j), g = dp at the picks.
+ */
+int moe_route_bwd(const float* topk_prob, const float* dprob_perm, const int32_t* dest_row,
+                  const int32_t* topk_expert, const float* logits, int64_t T, int E, int k,
+                  uint32_t flags, float* dlogits, hipStream_t stream);
+
+/*
+ * moe_permute -- dispatch: copy each token row to the grouped row of every
+ * pick, and move the probabilities along.
+ * [AutoModel, "专家并行": tokens are sent to the experts that compute them.]
+ *
+ * x            bf16 [T, H].   H: multiple of 8.
+ * dest_row     int32 [T, k]   from moe_route.
+ * topk_prob    fp32 [T, k]    may be NULL (then prob_perm is not written).
+ * xp           bf16 [T*k, H]  out: xp[dest_row[t][j]] = x[t].
+ * prob_perm    fp32 [T*k]     out (may be NULL): prob_perm[dest_row[t][j]] = topk_prob[t][j].
+ */
+int moe_permute(const uint16_t* x, int64_t T, int H, int k, const int32_t* dest_row,
+                const float* topk_prob, uint16_t* xp, float* prob_perm, hipStream_t stream);
+
+/*
+ * moe_unpermute -- combine: y[t] = sum over j = 0..k-1 (in slot order, fp32)
+ * of w_tj * yp[dest_row[t][j]], rounded once to bf16.
+ * [AutoModel, "专家并行": results are sent back to their tokens.]
+ *
+ * topk_prob    fp32 [T, k] weights w_tj, or NULL for w = 1.  The grouped MLP
+ *              already applies the routing probability (ScaledSwiGLU), so the
+ *              layer passes NULL here; a non-NULL table serves a combine for
+ *              experts that did not apply it.
+ * yp           bf16 [T*k, H];  y: bf16 [T, H] out.  H: multiple of 8.
+ */
+int moe_unpermute(const uint16_t* yp, int64_t T, int H, int k, const int32_t* dest_row,
+                  const float* topk_prob, uint16_t* y, hipStream_t stream);
+
+/*
+ * mxfp8_quantize -- MXFP8 block quantization of a bf16 matrix.
+ * [BioNeMo, "MXFP8与融合MLP" and the bottleneck section: 8-bit values with one
+ *  scale per 32 consecutive values, made from BF16 before a low-precision GEMM.]
+ *
+ * Block scale: S = log2(X) + 127 for the smallest power of two X with
+ * amax <= 448 X, clamped to [0, 254]; S = 0 for an all-zero block.  Codes:
+ * E4M3 (bias 7, max 448, no infinities) of v / X, round to nearest even,
+ * sign kept (-0 -> 0x80).  NaN/Inf inputs are outside the contract.
+ *
+ * x        bf16 [rows, cols].
+ * axis=1   rowwise: blocks along the last dim; cols multiple of 32.
+ *          codes [rows, cols], scales [rows, cols/32].
+ * axis=0   grouped columnwise: the rows form ngroups consecutive groups of
+ *          group_sizes[g] rows (device int32 [ngroups]; NULL = one group of
+ *          all rows).  Inside a group, blocks of 32 consecutive rows start at
+ *          the group's first row; the last block is zero-padded.  Group g is
+ *          stored transposed as codes [cols, P_g], P_g = 32*ceil(n_g/32), at
+ *          byte offset cols*(P_0+..+P_{g-1}); its scales [cols, P_g/32] at
+ *          cols*(P_0+..+P_{g-1})/32.  cols multiple of 8.  The buffers must
+ *          hold mxfp8_colwise_bytes(); bytes past the used extent are not
+ *          written.
+ */
+int mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, int axis,
+                   const int32_t* group_sizes, int ngroups, uint8_t* codes, uint8_t* scales,
+                   hipStream_t stream);
+
+/* Inverse of mxfp8_quantize: out bf16 [rows, cols] = RNE_bf16(decode(code) * 2^(S-127)). */
+int mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                     int axis, const int32_t* group_sizes, int ngroups, uint16_t* out,
+                     hipStream_t stream);
+
+/* Capacity of the grouped columnwise layout: cols*(rows + 31*ngroups) code
+ * bytes and a 32nd of that in scale bytes (host-side, no launch). */
+void mxfp8_colwise_bytes(int64_t rows, int64_t cols, int ngroups, size_t* code_bytes,
+                         size_t* scale_bytes);
+
+/*
+ * Tensors the forward saves for the backward.  Caller-owned device buffers.
+ *   a1          bf16 [rows, 2I]: gate_up output before the activation (both modes).
+ *   a2          BF16 mode: bf16 [rows, I], the ScaledSwiGLU output.
+ *   a2_col_*    MXFP8 mode: grouped columnwise MXFP8 of the ScaledSwiGLU
+ *               output (groups = experts), mxfp8_colwise_bytes(rows, I, E).
+ *   xp_col_*    MXFP8 mode: grouped columnwise MXFP8 of xp, (rows, H, E).
+ * Members that the mode does not use may be NULL.
+ */
+typedef struct moe_saved {
+    uint16_t* a1;
+    uint16_t* a2;
+    uint8_t* a2_col_codes;
+    uint8_t* a2_col_scales;
+    uint8_t* xp_col_codes;
+    uint8_t* xp_col_scales;
+} moe_saved;
+
+/*
+ * grouped_mlp_fwd -- all experts' gate_up -> ScaledSwiGLU -> down in one call.
+ * [BioNeMo, "GroupedLinear": one grouped GEMM over all local experts, each
+ *  with its own weight, gate_up out_features = 2*intermediate, no bias, rows
+ *  given with split_sizes; "MXFP8与融合MLP": gate_up, ScaledSwiGLU (SwiGLU
+ *  times the routing probability), down, fused with quantization so that no
+ *  intermediate is dequantized to memory.]
+ *
+ * Per expert e with its M_e = split_sizes[e] consecutive rows of xp:
+ *   A1 = xp_e W1_e^T (fp32 accumulation); g = A1[:, :I], u = A1[:, I:]
+ *   A2 = prob * silu(g) * u;  yp_e = A2 W2_e^T (rounded to bf16).
+ * MXFP8 mode quantizes xp and W1 along H, A2 and W2 along I (rowwise, in the
+ * GEMM prologue/epilogue), and also saves the columnwise MXFP8 of xp and A2
+ * for the weight gradients.
+ *
+ * precision    MOE_BF16 or MOE_MXFP8.
+ * E            experts, 1..64.   H, I: hidden and intermediate sizes,
+ *              multiples of 128 (bf16) / 128 (mxfp8).
+ * rows         T*k, 0 <= rows <= INT32_MAX.
+ * xp           bf16 [rows, H], expert-grouped (moe_permute).
+ * split_sizes  int32 [E] device, sum = rows.
+ * w_gate_up    HOST array of E device pointers, each bf16 [2I, H] (rows
+ *              [0, I) gate, [I, 2I) up).
+ * w_down       HOST array of E device pointers, each bf16 [H, I].
+ * prob_perm    fp32 [rows] (moe_permute).
+ * yp           bf16 [rows, H] out.
+ * saved        caller-owned saved tensors (see moe_saved), written.
+ * workspace    moe_workspace_bytes(MOE_OP_MLP_FWD, ...) bytes.
+ */
+int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint16_t* xp,
+                    const int32_t* split_sizes, const uint16_t* const* w_gate_up,
+                    const uint16_t* const* w_down, const float* prob_perm, uint16_t* yp,
+                    const moe_saved* saved, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
+ * grouped_mlp_bwd -- backward of grouped_mlp_fwd.
+ * [BioNeMo, "MXFP8与融合MLP": the fused forward has a matching fused backward.]
+ *
+ * Per expert e (g, u from the saved bf16 A1; s = silu(g), sig = sigmoid(g)):
+ *   dA2 = dyp_e W2_e (fp32);  dW2_e = dyp_e^T A2_e
+ *   dg = dA2 p u sig (1 + g (1 - sig)),  du = dA2 p s,  dprob = sum_i dA2 s u
+ *   dA1 = [dg, du];  dxp_e = dA1 W1_e;  dW1_e = dA1^T xp_e
+ * Experts with no rows get exact zeros in dW1_e and dW2_e.  MXFP8 mode
+ * quantizes every GEMM operand along that GEMM's contraction axis.
+ *
+ * dyp          bf16 [rows, H] (moe_permute of the upstream gradient).
+ * xp, split_sizes, w_gate_up, w_down, prob_perm, saved: as in the forward.
+ * dxp          bf16 [rows, H] out.
+ * dw_gate_up   HOST array of E device pointers, each bf16 [2I, H] out.
+ * dw_down      HOST array of E device pointers, each bf16 [H, I] out.
+ * dprob_perm   fp32 [rows] out.
+ * workspace    moe_workspace_bytes(MOE_OP_MLP_BWD, ...) bytes.
+ */
+int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint16_t* dyp,
+                    const uint16_t* xp, const int32_t* split_sizes,
+                    const uint16_t* const* w_gate_up, const uint16_t* const* w_down,
+                    const float* prob_perm, const moe_saved* saved, uint16_t* dxp,
+                    uint16_t* const* dw_gate_up, uint16_t* const* dw_down, float* dprob_perm,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Workspace bytes for op (MOE_OP_ROUTE: T, E, k used; MLP ops: rows = T*k,
+ * H, I, E, precision used).  Returns 0 for an invalid op.
+ */
+size_t moe_workspace_bytes(int op, int64_t T, int H, int I, int E, int k, int precision);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

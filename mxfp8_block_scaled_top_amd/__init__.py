@@ -1,0 +1,270 @@
+"""Python binding of libmoe_mi355x (the grouped MoE expert MLP on MI355X / gfx950).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch provides device memory (output and workspace tensors) and
+the current HIP stream; no arithmetic of the method runs in Python or torch.
+There is no CPU fallback: calls fail when the library is not built or the
+device is not a gfx950.
+
+The functions carry the names of the C entry points (include/moe_mi355x.h):
+moe_route, moe_route_bwd, moe_permute, moe_unpermute, mxfp8_quantize,
+mxfp8_dequantize, grouped_mlp_fwd, grouped_mlp_bwd, moe_workspace_bytes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libmoe_mi355x.so")
+
+MOE_BF16, MOE_MXFP8 = 0, 1
+MOE_ROUTE_RENORM, MOE_ROUTE_SOFTMAX_ALL = 0, 1
+MOE_OP_ROUTE, MOE_OP_MLP_FWD, MOE_OP_MLP_BWD = 0, 1, 2
+MAX_EXPERTS = 64
+
+_lib = None
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+class _Saved(ctypes.Structure):
+    _fields_ = [("a1", ctypes.c_void_p), ("a2", ctypes.c_void_p),
+                ("a2_col_codes", ctypes.c_void_p), ("a2_col_scales", ctypes.c_void_p),
+                ("xp_col_codes", ctypes.c_void_p), ("xp_col_scales", ctypes.c_void_p)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoEError(f"{LIB_PATH} not built: run `python -m mxfp8_block_scaled_top_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, U32, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+        sig = {
+            "moe_status_string": (ctypes.c_char_p, [I32]),
+            "moe_device_supported": (I32, []),
+            "moe_workspace_bytes": (SZ, [I32, I64, I32, I32, I32, I32, I32]),
+            "moe_route": (I32, [P, I64, I32, I32, U32, P, P, P, P, P, P, P, SZ, P]),
+            "moe_route_bwd": (I32, [P, P, P, P, P, I64, I32, I32, U32, P, P]),
+            "moe_permute": (I32, [P, I64, I32, I32, P, P, P, P, P]),
+            "moe_unpermute": (I32, [P, I64, I32, I32, P, P, P, P]),
+            "mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, P, P, P]),
+            "mxfp8_dequantize": (I32, [P, P, I64, I64, I32, P, I32, P, P]),
+            "mxfp8_colwise_bytes": (None, [I64, I64, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+            "grouped_mlp_fwd": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P,
+                                      ctypes.POINTER(_Saved), P, SZ, P]),
+            "grouped_mlp_bwd": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P,
+                                      ctypes.POINTER(_Saved), P, P, P, P, P, SZ, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = lib().moe_status_string(status).decode()
+        raise MoEError(f"{what} failed: status {status} ({msg})")
+
+
+def _stream(device=None) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> None:
+    if not t.is_cuda:
+        raise MoEError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise MoEError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise MoEError(f"{name} must be contiguous")
+
+
+def device_supported() -> bool:
+    return bool(lib().moe_device_supported())
+
+
+def moe_workspace_bytes(op: int, T: int, H: int, I: int, E: int, k: int, precision: int) -> int:
+    return int(lib().moe_workspace_bytes(op, T, H, I, E, k, precision))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def moe_route(logits: torch.Tensor, k: int, softmax_all: bool = False) -> dict:
+    """Top-k routing.  Returns topk_expert, topk_prob, split_sizes,
+    expert_offsets, dest_row, src_token (device tensors)."""
+    _dev(logits, torch.float32, "logits")
+    T, E = logits.shape
+    dev = logits.device
+    out = {
+        "topk_expert": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "topk_prob": torch.empty((T, k), dtype=torch.float32, device=dev),
+        "split_sizes": torch.empty(E, dtype=torch.int32, device=dev),
+        "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "dest_row": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "src_token": torch.empty(T * k, dtype=torch.int32, device=dev),
+    }
+    ws_n = moe_workspace_bytes(MOE_OP_ROUTE, T, 0, 0, E, k, 0)
+    ws = _workspace(ws_n, dev)
+    _check(lib().moe_route(_ptr(logits), T, E, k, int(softmax_all), _ptr(out["topk_expert"]),
+                           _ptr(out["topk_prob"]), _ptr(out["split_sizes"]),
+                           _ptr(out["expert_offsets"]), _ptr(out["dest_row"]),
+                           _ptr(out["src_token"]), _ptr(ws), ws.numel(), _stream(dev)),
+           "moe_route")
+    return out
+
+
+def moe_route_bwd(topk_prob, dprob_perm, dest_row, topk_expert, E: int, logits=None,
+                  softmax_all: bool = False) -> torch.Tensor:
+    T, k = topk_prob.shape
+    dl = torch.empty((T, E), dtype=torch.float32, device=topk_prob.device)
+    _check(lib().moe_route_bwd(_ptr(topk_prob), _ptr(dprob_perm), _ptr(dest_row),
+                               _ptr(topk_expert), _ptr(logits), T, E, k, int(softmax_all),
+                               _ptr(dl), _stream(topk_prob.device)), "moe_route_bwd")
+    return dl
+
+
+def moe_permute(x: torch.Tensor, dest_row: torch.Tensor, topk_prob=None):
+    """Returns (xp [T*k, H] bf16, prob_perm [T*k] fp32 or None)."""
+    _dev(x, torch.bfloat16, "x")
+    T, H = x.shape
+    k = dest_row.shape[1]
+    xp = torch.empty((T * k, H), dtype=torch.bfloat16, device=x.device)
+    pp = torch.empty(T * k, dtype=torch.float32, device=x.device) if topk_prob is not None else None
+    _check(lib().moe_permute(_ptr(x), T, H, k, _ptr(dest_row), _ptr(topk_prob), _ptr(xp),
+                             _ptr(pp), _stream(x.device)), "moe_permute")
+    return xp, pp
+
+
+def moe_unpermute(yp: torch.Tensor, dest_row: torch.Tensor, topk_prob=None) -> torch.Tensor:
+    _dev(yp, torch.bfloat16, "yp")
+    T, k = dest_row.shape
+    H = yp.shape[1]
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=yp.device)
+    _check(lib().moe_unpermute(_ptr(yp), T, H, k, _ptr(dest_row), _ptr(topk_prob), _ptr(y),
+                               _stream(yp.device)), "moe_unpermute")
+    return y
+
+
+def colwise_bytes(rows: int, cols: int, ngroups: int):
+    c, s = ctypes.c_size_t(), ctypes.c_size_t()
+    lib().mxfp8_colwise_bytes(rows, cols, ngroups, ctypes.byref(c), ctypes.byref(s))
+    return c.value, s.value
+
+
+def mxfp8_quantize(x: torch.Tensor, axis: int = 1, group_sizes=None):
+    """Returns (codes uint8, scales uint8).  axis=1: [R, C] and [R, C/32];
+    axis=0: flat grouped columnwise buffers of mxfp8_colwise_bytes size."""
+    _dev(x, torch.bfloat16, "x")
+    R, C = x.shape
+    G = 0 if group_sizes is None else group_sizes.numel()
+    if axis == 1:
+        codes = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((R, C // 32), dtype=torch.uint8, device=x.device)
+    else:
+        cb, sb = colwise_bytes(R, C, max(G, 1))
+        codes = torch.zeros(cb, dtype=torch.uint8, device=x.device)
+        scales = torch.zeros(sb, dtype=torch.uint8, device=x.device)
+    _check(lib().mxfp8_quantize(_ptr(x), R, C, axis, _ptr(group_sizes), G, _ptr(codes),
+                                _ptr(scales), _stream(x.device)), "mxfp8_quantize")
+    return codes, scales
+
+
+def mxfp8_dequantize(codes, scales, rows: int, cols: int, axis: int = 1, group_sizes=None):
+    G = 0 if group_sizes is None else group_sizes.numel()
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=codes.device)
+    _check(lib().mxfp8_dequantize(_ptr(codes), _ptr(scales), rows, cols, axis, _ptr(group_sizes),
+                                  G, _ptr(out), _stream(codes.device)), "mxfp8_dequantize")
+    return out
+
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def alloc_saved(rows: int, H: int, I: int, E: int, precision: int, device) -> dict:
+    """Caller-owned tensors the forward saves for the backward."""
+    s = {"a1": torch.empty((rows, 2 * I), dtype=torch.bfloat16, device=device)}
+    if precision == MOE_BF16:
+        s["a2"] = torch.empty((rows, I), dtype=torch.bfloat16, device=device)
+    else:
+        cb, sb = colwise_bytes(rows, I, E)
+        s["a2_col_codes"] = torch.empty(cb, dtype=torch.uint8, device=device)
+        s["a2_col_scales"] = torch.empty(sb, dtype=torch.uint8, device=device)
+        cb, sb = colwise_bytes(rows, H, E)
+        s["xp_col_codes"] = torch.empty(cb, dtype=torch.uint8, device=device)
+        s["xp_col_scales"] = torch.empty(sb, dtype=torch.uint8, device=device)
+    return s
+
+
+def _saved_struct(s: dict) -> _Saved:
+    return _Saved(*[_ptr(s.get(n)) for n, _ in _Saved._fields_])
+
+
+def grouped_mlp_fwd(xp, split_sizes, w_gate_up, w_down, prob_perm, precision=MOE_BF16,
+                    saved=None, workspace=None):
+    """Returns (yp, saved).  w_gate_up / w_down: lists of E device tensors."""
+    _dev(xp, torch.bfloat16, "xp")
+    rows, H = xp.shape
+    E = len(w_gate_up)
+    I = w_down[0].shape[1]
+    if saved is None:
+        saved = alloc_saved(rows, H, I, E, precision, xp.device)
+    if workspace is None:
+        n = lib().moe_workspace_bytes(MOE_OP_MLP_FWD, rows, H, I, E, 1, precision)
+        workspace = _workspace(n, xp.device)
+    yp = torch.empty((rows, H), dtype=torch.bfloat16, device=xp.device)
+    w1, w2 = _ptr_array(w_gate_up), _ptr_array(w_down)
+    st = _saved_struct(saved)
+    _check(lib().grouped_mlp_fwd(precision, E, H, I, rows, _ptr(xp), _ptr(split_sizes),
+                                 ctypes.cast(w1, ctypes.c_void_p), ctypes.cast(w2, ctypes.c_void_p),
+                                 _ptr(prob_perm), _ptr(yp), ctypes.byref(st), _ptr(workspace),
+                                 workspace.numel(), _stream(xp.device)), "grouped_mlp_fwd")
+    return yp, saved
+
+
+def grouped_mlp_bwd(dyp, xp, split_sizes, w_gate_up, w_down, prob_perm, saved,
+                    precision=MOE_BF16, workspace=None, dw_gate_up=None, dw_down=None):
+    """Returns (dxp, dw_gate_up list, dw_down list, dprob_perm)."""
+    _dev(dyp, torch.bfloat16, "dyp")
+    rows, H = dyp.shape
+    E = len(w_gate_up)
+    I = w_down[0].shape[1]
+    dev = dyp.device
+    if workspace is None:
+        n = lib().moe_workspace_bytes(MOE_OP_MLP_BWD, rows, H, I, E, 1, precision)
+        workspace = _workspace(n, dev)
+    dxp = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    if dw_gate_up is None:
+        dw_gate_up = [torch.empty((2 * I, H), dtype=torch.bfloat16, device=dev) for _ in range(E)]
+    if dw_down is None:
+        dw_down = [torch.empty((H, I), dtype=torch.bfloat16, device=dev) for _ in range(E)]
+    dpp = torch.empty(rows, dtype=torch.float32, device=dev)
+    w1, w2 = _ptr_array(w_gate_up), _ptr_array(w_down)
+    d1, d2 = _ptr_array(dw_gate_up), _ptr_array(dw_down)
+    st = _saved_struct(saved)
+    _check(lib().grouped_mlp_bwd(precision, E, H, I, rows, _ptr(dyp), _ptr(xp), _ptr(split_sizes),
+                                 ctypes.cast(w1, ctypes.c_void_p), ctypes.cast(w2, ctypes.c_void_p),
+                                 _ptr(prob_perm), ctypes.byref(st), _ptr(dxp),
+                                 ctypes.cast(d1, ctypes.c_void_p), ctypes.cast(d2, ctypes.c_void_p),
+                                 _ptr(dpp), _ptr(workspace), workspace.numel(), _stream(dev)),
+           "grouped_mlp_bwd")
+    return dxp, dw_gate_up, dw_down, dpp

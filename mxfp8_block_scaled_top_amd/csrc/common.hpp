@@ -1,0 +1,114 @@
+// Device helpers shared by the gfx950 kernels of libmoe_mi355x.
+//
+// MXFP8 encoding follows the block rule of the BioNeMo MoE recipe page
+// (section on MXFP8 and the fused MLP): one scale for every 32 consecutive
+// values.  Element format E4M3 (bias 7, 3 mantissa bits, largest finite 448,
+// no infinities), scale format E8M0 (power of two, bias 127).  The scale of a
+// block is the smallest power of two X with amax <= 448 X, so no element is
+// clamped; elements round to nearest, ties to even.  All of it is integer /
+// exact arithmetic: the codes do not depend on any floating-point rounding
+// mode or on the order of operations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMxBlock = 32;
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// Round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// E8M0 scale byte of a block from its max magnitude (amax >= 0, finite):
+// smallest s with amax <= 448 * 2^s, i.e. 448 = 1.75 * 2^8 compared with the
+// significand of amax; S = s + 127 clamped to [0, 254]; amax = 0 gives 0.
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+    uint32_t b = __float_as_uint(amax);
+    int eb = (int)((b >> 23) & 0xffu);
+    int up = (b & 0x7fffffu) > 0x600000u ? 1 : 0;
+    int s = eb - 8 + up;
+    s = s < 0 ? 0 : (s > 254 ? 254 : s);
+    return b == 0u ? 0u : (uint32_t)s;
+}
+
+// Exact multiply by 2^(127 - S) for the magnitudes that matter: results at or
+// above 2^-126 are exact; smaller ones all encode to zero anyway.
+__device__ __forceinline__ float mx_unscale(float v, uint32_t S) {
+    return __builtin_ldexpf(v, 127 - (int)S);
+}
+
+// E4M3 code of v / 2^(S-127): sign bit kept, magnitude rounded to nearest
+// even on the E4M3 grid.  |v| / X <= 448 is guaranteed by the scale choice.
+__device__ __forceinline__ uint32_t mx_encode(float v, uint32_t S) {
+    uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    float y = mx_unscale(__builtin_fabsf(v), S);
+    uint32_t b = __float_as_uint(y);
+    uint32_t mag;
+    if (b < 0x3c800000u) {
+        // below 2^-6: subnormal steps of 2^-9 (exact product), rint = half-even
+        mag = (uint32_t)__builtin_rintf(y * 512.0f);
+    } else {
+        uint32_t e = (b >> 23) - 120u;       // E4M3 exponent field (bias 7)
+        uint32_t m = b & 0x7fffffu;
+        uint32_t keep = m >> 20;             // top 3 mantissa bits
+        uint32_t rest = m & 0xfffffu;
+        uint32_t up = (rest > 0x80000u) || (rest == 0x80000u && (keep & 1u));
+        mag = ((e << 3) | keep) + up;        // a carry moves into the exponent
+    }
+    return sign | mag;
+}
+
+// Value of an E4M3 code times 2^(S-127), exact in fp32.
+__device__ __forceinline__ float mx_decode(uint32_t code, uint32_t S) {
+    uint32_t e = (code >> 3) & 15u, m = code & 7u;
+    float mag = e == 0u ? (float)m * 0.001953125f                // m * 2^-9
+                        : __builtin_ldexpf((float)(8u + m), (int)e - 10);
+    float v = __builtin_ldexpf(mag, (int)S - 127);
+    return (code & 0x80u) ? -v : v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    int lane = threadIdx.x & 63;
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+}  // namespace moe

@@ -1,0 +1,48 @@
+// Internal launcher interface between the C ABI (capi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 64;
+constexpr int kMaxTopK = 64;
+
+typedef uint16_t bf16_t;
+
+// A table of per-matrix (per-expert) device pointers, passed by value in the
+// kernel arguments (64 x 8 B = 512 B).
+struct MatTable {
+    const void* p[kMaxExperts];
+};
+
+// ---- routing / permutation
+size_t route_workspace_bytes(int64_t T, int E, int k);
+hipError_t launch_route(const float* logits, int T, int E, int k, uint32_t flags,
+                        int32_t* topk_expert, float* topk_prob, int32_t* split_sizes,
+                        int32_t* expert_offsets, int32_t* dest_row, int32_t* src_token,
+                        void* ws, hipStream_t s);
+hipError_t launch_route_bwd(const float* topk_prob, const float* dprob_perm,
+                            const int32_t* dest_row, const int32_t* topk_expert,
+                            const float* logits, int T, int E, int k, uint32_t flags,
+                            float* dlogits, hipStream_t s);
+hipError_t launch_permute(const bf16_t* x, int T, int H, int k, const int32_t* dest_row,
+                          const float* topk_prob, bf16_t* xp, float* prob_perm, hipStream_t s);
+hipError_t launch_unpermute(const bf16_t* yp, int T, int H, int k, const int32_t* dest_row,
+                            const float* topk_prob, bf16_t* y, hipStream_t s);
+
+// ---- MXFP8
+int64_t colwise_block_bound(int64_t rows, int ngroups);
+hipError_t launch_quant_rows(const MatTable& src, const MatTable& codes, const MatTable& scales,
+                             int nmat, int64_t rows, int64_t cols, hipStream_t s);
+hipError_t launch_quant_cols(const MatTable& src, const MatTable& codes, const MatTable& scales,
+                             int nmat, const int32_t* sizes, int ngroups, int64_t rows,
+                             int64_t cols, hipStream_t s);
+hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                               int64_t cols, bf16_t* out, hipStream_t s);
+hipError_t launch_dequant_cols(const uint8_t* codes, const uint8_t* scales, const int32_t* sizes,
+                               int ngroups, int64_t rows, int64_t cols, bf16_t* out,
+                               hipStream_t s);
+
+}  // namespace moe

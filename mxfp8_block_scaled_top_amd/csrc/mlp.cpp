@@ -1,0 +1,461 @@
+// grouped_mlp_fwd / grouped_mlp_bwd: the launch sequences of the grouped
+// expert MLP and their workspace layouts.
+//
+// Forward (per expert e, all experts per launch):
+//   gate_up GEMM  A1 = Xp W1^T  + ScaledSwiGLU epilogue (A1 saved as bf16;
+//                 A2 = p silu(g) u written as bf16, or as rowwise + grouped
+//                 columnwise MXFP8)
+//   down GEMM     Yp = A2 W2^T
+// Backward:
+//   down dgrad    dA2 = dYp W2  + SwiGLU-backward epilogue (dA1 as bf16 or
+//                 MXFP8 row + column, per-tile probability-gradient partials)
+//   dprob reduce  fixed-order sum of the partials
+//   down wgrad    dW2 = dYp^T A2       (ragged K = rows of the expert)
+//   gate_up dgrad dXp = dA1 W1
+//   gate_up wgrad dW1 = dA1^T Xp       (ragged K)
+// MXFP8 mode first quantizes the GEMM operands that arrive in bf16 (Xp, dYp,
+// both weight sets) along the contraction axis of the GEMM that reads them.
+#include "moe_mi355x.h"
+
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "kernels.hpp"
+#include "mlp.hpp"
+
+using namespace moe;
+
+namespace {
+
+size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Carve {
+    uint8_t* p;
+    size_t off = 0;
+    explicit Carve(void* base) : p((uint8_t*)base) {}
+    uint8_t* take(size_t n) {
+        uint8_t* r = p ? p + off : nullptr;
+        off += al(n);
+        return r;
+    }
+};
+
+size_t colwise_codes(int64_t rows, int64_t cols, int E) {
+    size_t c = 0;
+    mxfp8_colwise_bytes(rows, cols, E, &c, nullptr);
+    return c;
+}
+
+struct FwdWs {
+    uint8_t *xq, *xq_s, *w1q, *w1q_s, *w2q, *w2q_s, *a2q, *a2q_s;
+    size_t bytes;
+};
+
+FwdWs carve_fwd(void* base, int64_t rows, int H, int I, int E, int precision) {
+    Carve c(base);
+    FwdWs w{};
+    if (precision == MOE_MXFP8) {
+        w.xq = c.take((size_t)rows * H);
+        w.xq_s = c.take((size_t)rows * H / 32);
+        w.w1q = c.take((size_t)E * 2 * I * H);
+        w.w1q_s = c.take((size_t)E * 2 * I * H / 32);
+        w.w2q = c.take((size_t)E * H * I);
+        w.w2q_s = c.take((size_t)E * H * I / 32);
+        w.a2q = c.take((size_t)rows * I);
+        w.a2q_s = c.take((size_t)rows * I / 32);
+    }
+    c.take(256);
+    w.bytes = c.off;
+    return w;
+}
+
+struct BwdWs {
+    uint8_t *da1;           // bf16 [rows, 2I] (BF16 mode)
+    uint8_t *dyq, *dyq_s;   // rowwise dYp
+    uint8_t *dyc, *dyc_s;   // grouped columnwise dYp
+    uint8_t *w2c, *w2c_s;   // W2 quantized along H: [E][I, H]
+    uint8_t *w1c, *w1c_s;   // W1 quantized along 2I: [E][H, 2I]
+    uint8_t *da1q, *da1q_s; // rowwise dA1 [rows, 2I]
+    uint8_t *da1c, *da1c_s; // grouped columnwise dA1
+    float* part;            // dprob partials [rows, ntiles]
+    size_t bytes;
+};
+
+BwdWs carve_bwd(void* base, int64_t rows, int H, int I, int E, int precision) {
+    Carve c(base);
+    BwdWs w{};
+    int ntn = gemm_n_tiles(EPI_SWIGLU_BWD, I, I);
+    w.part = (float*)c.take((size_t)rows * ntn * sizeof(float));
+    if (precision == MOE_BF16) {
+        w.da1 = c.take((size_t)rows * 2 * I * 2);
+    } else {
+        w.dyq = c.take((size_t)rows * H);
+        w.dyq_s = c.take((size_t)rows * H / 32);
+        size_t ch = colwise_codes(rows, H, E);
+        w.dyc = c.take(ch);
+        w.dyc_s = c.take(ch / 32);
+        w.w2c = c.take((size_t)E * H * I);
+        w.w2c_s = c.take((size_t)E * H * I / 32);
+        w.w1c = c.take((size_t)E * 2 * I * H);
+        w.w1c_s = c.take((size_t)E * 2 * I * H / 32);
+        w.da1q = c.take((size_t)rows * 2 * I);
+        w.da1q_s = c.take((size_t)rows * 2 * I / 32);
+        size_t ci = colwise_codes(rows, 2 * (int64_t)I, E);
+        w.da1c = c.take(ci);
+        w.da1c_s = c.take(ci / 32);
+    }
+    c.take(256);
+    w.bytes = c.off;
+    return w;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_common(int precision, int E, int H, int I, int64_t rows) {
+    if (precision != MOE_BF16 && precision != MOE_MXFP8) return MOE_ERR_ARG;
+    if (E < 1 || E > kMaxExperts) return MOE_ERR_SHAPE;
+    if (H < 128 || I < 128 || (H % 128) || (I % 128)) return MOE_ERR_SHAPE;
+    if (rows < 0 || rows > INT32_MAX) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+int device_check() { return moe_device_supported() ? MOE_OK : MOE_ERR_UNSUPPORTED; }
+
+}  // namespace
+
+namespace moe {
+size_t mlp_fwd_workspace_bytes(int64_t rows, int H, int I, int E, int precision) {
+    return carve_fwd(nullptr, rows, H, I, E, precision).bytes;
+}
+size_t mlp_bwd_workspace_bytes(int64_t rows, int H, int I, int E, int precision) {
+    return carve_bwd(nullptr, rows, H, I, E, precision).bytes;
+}
+}  // namespace moe
+
+#define MOE_TRY(x)                               \
+    do {                                         \
+        if ((x) != hipSuccess) return MOE_ERR_HIP; \
+    } while (0)
+
+extern "C" {
+
+int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint16_t* xp,
+                    const int32_t* split_sizes, const uint16_t* const* w_gate_up,
+                    const uint16_t* const* w_down, const float* prob_perm, uint16_t* yp,
+                    const moe_saved* saved, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+    int st = check_common(precision, E, H, I, rows);
+    if (st != MOE_OK) return st;
+    if (!split_sizes || !w_gate_up || !w_down || !saved || !workspace) return MOE_ERR_NULL;
+    for (int e = 0; e < E; ++e)
+        if (!w_gate_up[e] || !w_down[e]) return MOE_ERR_NULL;
+    if (rows > 0) {
+        if (!xp || !prob_perm || !yp || !saved->a1) return MOE_ERR_NULL;
+        if (precision == MOE_BF16 && !saved->a2) return MOE_ERR_NULL;
+        if (precision == MOE_MXFP8 && (!saved->a2_col_codes || !saved->a2_col_scales ||
+                                       !saved->xp_col_codes || !saved->xp_col_scales))
+            return MOE_ERR_NULL;
+    }
+    if (!aligned16(xp) || !aligned16(yp) || !aligned16(saved->a1) || !aligned16(saved->a2))
+        return MOE_ERR_ALIGN;
+    for (int e = 0; e < E; ++e)
+        if (!aligned16(w_gate_up[e]) || !aligned16(w_down[e])) return MOE_ERR_ALIGN;
+    if (workspace_bytes < mlp_fwd_workspace_bytes(rows, H, I, E, precision))
+        return MOE_ERR_WORKSPACE;
+    if ((st = device_check()) != MOE_OK) return st;
+    if (rows == 0) return MOE_OK;
+
+    FwdWs w = carve_fwd(workspace, rows, H, I, E, precision);
+    GemmArgs g{};
+    g.split = split_sizes;
+    g.E = E;
+    g.rows = rows;
+    g.prob = prob_perm;
+    g.I = I;
+    if (precision == MOE_BF16) {
+        g.a = xp;
+        g.lda = H;
+        for (int e = 0; e < E; ++e) g.b.p[e] = w_gate_up[e];
+        g.ldb = H;
+        g.N = 2 * I;
+        g.K = H;
+        g.a1 = saved->a1;
+        g.act = saved->a2;
+        MOE_TRY(launch_gemm(DT_BF16, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_FWD, g, stream));
+        GemmArgs d = g;
+        d.a = saved->a2;
+        d.lda = I;
+        for (int e = 0; e < E; ++e) d.b.p[e] = w_down[e];
+        d.ldb = I;
+        d.N = H;
+        d.K = I;
+        d.c = yp;
+        d.ldc = H;
+        MOE_TRY(launch_gemm(DT_BF16, L_KMAJ, L_KMAJ, G_M, EPI_STORE, d, stream));
+        return MOE_OK;
+    }
+    // MXFP8: quantize operands along their contraction axis
+    MatTable src{}, cd{}, sc{};
+    src.p[0] = xp;
+    cd.p[0] = w.xq;
+    sc.p[0] = w.xq_s;
+    MOE_TRY(launch_quant_rows(src, cd, sc, 1, rows, H, stream));
+    cd.p[0] = saved->xp_col_codes;
+    sc.p[0] = saved->xp_col_scales;
+    MOE_TRY(launch_quant_cols(src, cd, sc, 1, split_sizes, E, rows, H, stream));
+    MatTable w1t{}, w1c{}, w1s{}, w2t{}, w2c{}, w2s{};
+    for (int e = 0; e < E; ++e) {
+        w1t.p[e] = w_gate_up[e];
+        w1c.p[e] = w.w1q + (size_t)e * 2 * I * H;
+        w1s.p[e] = w.w1q_s + (size_t)e * 2 * I * H / 32;
+        w2t.p[e] = w_down[e];
+        w2c.p[e] = w.w2q + (size_t)e * H * I;
+        w2s.p[e] = w.w2q_s + (size_t)e * H * I / 32;
+    }
+    MOE_TRY(launch_quant_rows(w1t, w1c, w1s, E, 2 * (int64_t)I, H, stream));
+    MOE_TRY(launch_quant_rows(w2t, w2c, w2s, E, H, I, stream));
+
+    g.a = w.xq;
+    g.lda = H;
+    g.a_scale = w.xq_s;
+    g.lda_s = H / 32;
+    g.b = w1c;
+    g.ldb = H;
+    g.b_scale = w1s;
+    g.ldb_s = H / 32;
+    g.N = 2 * I;
+    g.K = H;
+    g.a1 = saved->a1;
+    g.q_row = w.a2q;
+    g.q_row_s = w.a2q_s;
+    g.q_col = saved->a2_col_codes;
+    g.q_col_s = saved->a2_col_scales;
+    MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_FWD, g, stream));
+    GemmArgs d{};
+    d.split = split_sizes;
+    d.E = E;
+    d.rows = rows;
+    d.I = I;
+    d.a = w.a2q;
+    d.lda = I;
+    d.a_scale = w.a2q_s;
+    d.lda_s = I / 32;
+    d.b = w2c;
+    d.ldb = I;
+    d.b_scale = w2s;
+    d.ldb_s = I / 32;
+    d.N = H;
+    d.K = I;
+    d.c = yp;
+    d.ldc = H;
+    MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_STORE, d, stream));
+    return MOE_OK;
+}
+
+int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint16_t* dyp,
+                    const uint16_t* xp, const int32_t* split_sizes,
+                    const uint16_t* const* w_gate_up, const uint16_t* const* w_down,
+                    const float* prob_perm, const moe_saved* saved, uint16_t* dxp,
+                    uint16_t* const* dw_gate_up, uint16_t* const* dw_down, float* dprob_perm,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int st = check_common(precision, E, H, I, rows);
+    if (st != MOE_OK) return st;
+    if (!split_sizes || !w_gate_up || !w_down || !saved || !workspace || !dw_gate_up ||
+        !dw_down)
+        return MOE_ERR_NULL;
+    for (int e = 0; e < E; ++e)
+        if (!w_gate_up[e] || !w_down[e] || !dw_gate_up[e] || !dw_down[e]) return MOE_ERR_NULL;
+    if (rows > 0) {
+        if (!dyp || !xp || !prob_perm || !dxp || !dprob_perm || !saved->a1) return MOE_ERR_NULL;
+        if (precision == MOE_BF16 && !saved->a2) return MOE_ERR_NULL;
+        if (precision == MOE_MXFP8 && (!saved->a2_col_codes || !saved->a2_col_scales ||
+                                       !saved->xp_col_codes || !saved->xp_col_scales))
+            return MOE_ERR_NULL;
+    }
+    if (!aligned16(dyp) || !aligned16(xp) || !aligned16(dxp) || !aligned16(saved->a1) ||
+        !aligned16(saved->a2))
+        return MOE_ERR_ALIGN;
+    for (int e = 0; e < E; ++e)
+        if (!aligned16(w_gate_up[e]) || !aligned16(w_down[e]) || !aligned16(dw_gate_up[e]) ||
+            !aligned16(dw_down[e]))
+            return MOE_ERR_ALIGN;
+    if (workspace_bytes < mlp_bwd_workspace_bytes(rows, H, I, E, precision))
+        return MOE_ERR_WORKSPACE;
+    if ((st = device_check()) != MOE_OK) return st;
+
+    BwdWs w = carve_bwd(workspace, rows, H, I, E, precision);
+    const int ntn = gemm_n_tiles(EPI_SWIGLU_BWD, I, I);
+    MatTable dw1{}, dw2{};
+    for (int e = 0; e < E; ++e) {
+        dw1.p[e] = dw_gate_up[e];
+        dw2.p[e] = dw_down[e];
+    }
+    // weight-gradient GEMMs run for every expert (empty experts get zeros),
+    // even when there are no rows at all
+    if (precision == MOE_BF16) {
+        GemmArgs g{};
+        g.split = split_sizes;
+        g.E = E;
+        g.rows = rows;
+        g.prob = prob_perm;
+        g.I = I;
+        if (rows > 0) {
+            // down dgrad + SwiGLU backward
+            g.a = dyp;
+            g.lda = H;
+            for (int e = 0; e < E; ++e) g.b.p[e] = w_down[e];
+            g.ldb = I;            // W2 [H, I] read as [K = H, N = I]
+            g.N = I;
+            g.K = H;
+            g.a1 = saved->a1;
+            g.act = (bf16_t*)w.da1;
+            g.dprob_part = w.part;
+            MOE_TRY(launch_gemm(DT_BF16, L_KMAJ, L_MNMAJ, G_M, EPI_SWIGLU_BWD, g, stream));
+            MOE_TRY(launch_dprob_reduce(w.part, rows, ntn, dprob_perm, stream));
+        }
+        // down wgrad: dW2 [H, I] = dYp^T A2
+        GemmArgs wg{};
+        wg.split = split_sizes;
+        wg.E = E;
+        wg.rows = rows;
+        wg.a = dyp;
+        wg.lda = H;
+        wg.b.p[0] = saved->a2;
+        wg.ldb = I;
+        wg.M = H;
+        wg.N = I;
+        wg.c_tab = dw2;
+        wg.ldc = I;
+        MOE_TRY(launch_gemm(DT_BF16, L_MNMAJ, L_MNMAJ, G_K, EPI_STORE, wg, stream));
+        if (rows > 0) {
+            // gate_up dgrad: dXp = dA1 W1
+            GemmArgs dg{};
+            dg.split = split_sizes;
+            dg.E = E;
+            dg.rows = rows;
+            dg.a = w.da1;
+            dg.lda = 2 * I;
+            for (int e = 0; e < E; ++e) dg.b.p[e] = w_gate_up[e];
+            dg.ldb = H;           // W1 [2I, H] read as [K = 2I, N = H]
+            dg.N = H;
+            dg.K = 2 * I;
+            dg.c = dxp;
+            dg.ldc = H;
+            MOE_TRY(launch_gemm(DT_BF16, L_KMAJ, L_MNMAJ, G_M, EPI_STORE, dg, stream));
+        }
+        // gate_up wgrad: dW1 [2I, H] = dA1^T Xp
+        GemmArgs wg1{};
+        wg1.split = split_sizes;
+        wg1.E = E;
+        wg1.rows = rows;
+        wg1.a = w.da1;
+        wg1.lda = 2 * I;
+        wg1.b.p[0] = xp;
+        wg1.ldb = H;
+        wg1.M = 2 * I;
+        wg1.N = H;
+        wg1.c_tab = dw1;
+        wg1.ldc = H;
+        MOE_TRY(launch_gemm(DT_BF16, L_MNMAJ, L_MNMAJ, G_K, EPI_STORE, wg1, stream));
+        return MOE_OK;
+    }
+
+    // ---- MXFP8
+    MatTable src{}, cd{}, sc{};
+    if (rows > 0) {
+        src.p[0] = dyp;
+        cd.p[0] = w.dyq;
+        sc.p[0] = w.dyq_s;
+        MOE_TRY(launch_quant_rows(src, cd, sc, 1, rows, H, stream));
+        cd.p[0] = w.dyc;
+        sc.p[0] = w.dyc_s;
+        MOE_TRY(launch_quant_cols(src, cd, sc, 1, split_sizes, E, rows, H, stream));
+    }
+    MatTable w1t{}, w1c{}, w1s{}, w2t{}, w2c{}, w2s{};
+    for (int e = 0; e < E; ++e) {
+        w2t.p[e] = w_down[e];
+        w2c.p[e] = w.w2c + (size_t)e * H * I;
+        w2s.p[e] = w.w2c_s + (size_t)e * H * I / 32;
+        w1t.p[e] = w_gate_up[e];
+        w1c.p[e] = w.w1c + (size_t)e * 2 * I * H;
+        w1s.p[e] = w.w1c_s + (size_t)e * 2 * I * H / 32;
+    }
+    if (rows > 0) {
+        // W2 [H, I] along H -> [I, H];  W1 [2I, H] along 2I -> [H, 2I]
+        MOE_TRY(launch_quant_cols(w2t, w2c, w2s, E, nullptr, 1, H, I, stream));
+        MOE_TRY(launch_quant_cols(w1t, w1c, w1s, E, nullptr, 1, 2 * (int64_t)I, H, stream));
+        GemmArgs g{};
+        g.split = split_sizes;
+        g.E = E;
+        g.rows = rows;
+        g.prob = prob_perm;
+        g.I = I;
+        g.a = w.dyq;
+        g.lda = H;
+        g.a_scale = w.dyq_s;
+        g.lda_s = H / 32;
+        g.b = w2c;
+        g.ldb = H;
+        g.b_scale = w2s;
+        g.ldb_s = H / 32;
+        g.N = I;
+        g.K = H;
+        g.a1 = saved->a1;
+        g.q_row = w.da1q;
+        g.q_row_s = w.da1q_s;
+        g.q_col = w.da1c;
+        g.q_col_s = w.da1c_s;
+        g.dprob_part = w.part;
+        MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_BWD, g, stream));
+        MOE_TRY(launch_dprob_reduce(w.part, rows, ntn, dprob_perm, stream));
+    }
+    // down wgrad: dW2 [H, I] = dYp^T A2 over grouped columnwise operands
+    GemmArgs wg{};
+    wg.split = split_sizes;
+    wg.E = E;
+    wg.rows = rows;
+    wg.a = w.dyc;
+    wg.a_scale = w.dyc_s;
+    wg.b.p[0] = saved->a2_col_codes;
+    wg.b_scale.p[0] = saved->a2_col_scales;
+    wg.M = H;
+    wg.N = I;
+    wg.c_tab = dw2;
+    wg.ldc = I;
+    MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_K, EPI_STORE, wg, stream));
+    if (rows > 0) {
+        GemmArgs dg{};
+        dg.split = split_sizes;
+        dg.E = E;
+        dg.rows = rows;
+        dg.a = w.da1q;
+        dg.lda = 2 * I;
+        dg.a_scale = w.da1q_s;
+        dg.lda_s = 2 * I / 32;
+        dg.b = w1c;
+        dg.ldb = 2 * I;
+        dg.b_scale = w1s;
+        dg.ldb_s = 2 * I / 32;
+        dg.N = H;
+        dg.K = 2 * I;
+        dg.c = dxp;
+        dg.ldc = H;
+        MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_STORE, dg, stream));
+    }
+    GemmArgs wg1{};
+    wg1.split = split_sizes;
+    wg1.E = E;
+    wg1.rows = rows;
+    wg1.a = w.da1c;
+    wg1.a_scale = w.da1c_s;
+    wg1.b.p[0] = saved->xp_col_codes;
+    wg1.b_scale.p[0] = saved->xp_col_scales;
+    wg1.M = 2 * I;
+    wg1.N = H;
+    wg1.c_tab = dw1;
+    wg1.ldc = H;
+    MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_K, EPI_STORE, wg1, stream));
+    return MOE_OK;
+}
+
+}  // extern "C"

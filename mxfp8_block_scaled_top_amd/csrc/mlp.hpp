@@ -1,0 +1,61 @@
+// Grouped GEMM launcher interface and the grouped-MLP orchestration.
+#pragma once
+
+#include "kernels.hpp"
+
+namespace moe {
+
+enum GemmDType { DT_BF16 = 0, DT_MX = 1 };
+enum GemmLayout { L_KMAJ = 0, L_MNMAJ = 1 };   // operand contiguous along K / along M or N
+enum GemmGroup { G_M = 0, G_K = 1 };           // ragged rows (fwd, dgrad) / ragged K (wgrad)
+enum GemmEpi { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };
+
+constexpr int kGemmBM = 256, kGemmBN = 256, kGemmThreads = 512;
+
+// Arguments of one grouped GEMM C_e = A_e B_e^T over all experts e.
+//
+// G_M: expert e owns rows [row0_e, row0_e + M_e) of A and C (row-major, K
+//      contiguous in A); B_e = b.p[e] is [N, K] (L_KMAJ) or [K, N] (L_MNMAJ).
+// G_K: expert e owns rows [row0_e, row0_e + M_e) of two row-major matrices
+//      and C_e (= c_tab.p[e], [M, N]) = A_rows^T B_rows, contracting over them
+//      (bf16: both L_MNMAJ); MXFP8: both operands are the grouped columnwise
+//      layouts, [M, P_e] and [N, P_e] at the group's offset (L_KMAJ).
+// Strides are in elements for bf16 operands and in bytes for MXFP8 codes.
+struct GemmArgs {
+    const void* a;
+    int64_t lda;
+    const uint8_t* a_scale;
+    int64_t lda_s;
+    MatTable b;
+    int64_t ldb;
+    MatTable b_scale;
+    int64_t ldb_s;
+    const int32_t* split;
+    int E;
+    int64_t rows;       // total grouped rows
+    int M, N, K;        // G_M: N and K; G_K: M and N (K ragged)
+    void* c;            // G_M output base (bf16)
+    int64_t ldc;
+    MatTable c_tab;     // G_K per-expert outputs (bf16 [M, N])
+    // epilogue
+    const float* prob;  // prob_perm [rows]
+    bf16_t* a1;         // SWIGLU_FWD: out [rows, 2I]; SWIGLU_BWD: in
+    bf16_t* act;        // SWIGLU_FWD: A2 bf16 [rows, I]; SWIGLU_BWD: dA1 bf16 [rows, 2I]
+    uint8_t* q_row;     // MXFP8 rowwise codes of the epilogue output
+    uint8_t* q_row_s;
+    uint8_t* q_col;     // MXFP8 grouped columnwise codes of the epilogue output
+    uint8_t* q_col_s;
+    float* dprob_part;  // SWIGLU_BWD: [rows, n_tiles]
+    int I;              // intermediate size (SwiGLU epilogues)
+};
+
+hipError_t launch_gemm(int dtype, int la, int lb, int grp, int epi, const GemmArgs& g,
+                       hipStream_t s);
+hipError_t launch_dprob_reduce(const float* part, int64_t rows, int ntiles, float* dprob,
+                               hipStream_t s);
+int gemm_n_tiles(int epi, int N, int I);
+
+size_t mlp_fwd_workspace_bytes(int64_t rows, int H, int I, int E, int precision);
+size_t mlp_bwd_workspace_bytes(int64_t rows, int H, int I, int E, int precision);
+
+}  // namespace moe

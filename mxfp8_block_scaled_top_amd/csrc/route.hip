@@ -1,0 +1,209 @@
+// Top-k routing, per-expert counts (split_sizes) and the stable grouped-row
+// permutation, for gfx950.
+//
+// Each token goes to a few experts only [AutoModel page, section on the pain
+// points of MoE fine-tuning: sparse activation]; the grouped GEMM takes the
+// rows of all experts in one call with the number of rows of each expert
+// [BioNeMo MoE recipe page, section GroupedLinear].
+//
+// Three launches, all deterministic (integer atomics are not used):
+//   1. route_topk:    one thread per token.  Picks the k largest fp32 logits
+//                     (ties -> lower expert), softmax over the picks, and the
+//                     token's rank among the block's earlier tokens that
+//                     picked the same expert (wave ballots + a per-wave count
+//                     table in LDS).  Writes per-block expert counts.
+//   2. route_scan:    one wave.  Per expert, exclusive scan of the block counts
+//                     (the blocks' base rows), split_sizes and offsets.
+//   3. route_scatter: one thread per pick: dest_row and src_token.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kRouteThreads = 512;          // tokens per block (8 waves)
+constexpr int kRouteWaves = kRouteThreads / kWave;
+
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
+    const float* __restrict__ logits, int T, int E, int k, uint32_t flags,
+    int32_t* __restrict__ topk_expert, float* __restrict__ topk_prob,
+    int32_t* __restrict__ local_rank, int32_t* __restrict__ block_counts) {
+    __shared__ int wave_cnt[kRouteWaves][kMaxExperts];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int t = blockIdx.x * kRouteThreads + tid;
+    const bool valid = t < T;
+
+    uint64_t picked = 0;
+    if (valid) {
+        const float* row = logits + (size_t)t * E;
+        int32_t* sel = topk_expert + (size_t)t * k;
+        float* prob = topk_prob + (size_t)t * k;
+        // k scans of the row: strict '>' keeps the lowest index among equals.
+        float top = 0.f, denom = 0.f;
+        for (int j = 0; j < k; ++j) {
+            float bv = 0.f;
+            int be = -1;
+            for (int e = 0; e < E; ++e) {
+                if ((picked >> e) & 1ull) continue;
+                float v = row[e];
+                if (be < 0 || v > bv) { bv = v; be = e; }
+            }
+            picked |= 1ull << be;
+            sel[j] = be;
+            if (j == 0) top = bv;
+            denom += expf(bv - top);
+        }
+        if (flags & 1u) {
+            // softmax over all experts, taken at the picks
+            float mx = top;                  // the first pick is the row maximum
+            float s = 0.f;
+            for (int e = 0; e < E; ++e) s += expf(row[e] - mx);
+            for (int j = 0; j < k; ++j) prob[j] = expf(row[sel[j]] - mx) / s;
+        } else {
+            for (int j = 0; j < k; ++j) prob[j] = expf(row[sel[j]] - top) / denom;
+        }
+    }
+
+    // Per-wave counts of each expert, then block-level prefix over waves.
+    for (int e = 0; e < E; ++e) {
+        uint64_t bal = __ballot((picked >> e) & 1ull);
+        if (lane == 0) wave_cnt[wave][e] = __popcll(bal);
+    }
+    __syncthreads();
+    if (tid < E) {
+        int run = 0;
+        for (int w = 0; w < kRouteWaves; ++w) {
+            int c = wave_cnt[w][tid];
+            wave_cnt[w][tid] = run;          // exclusive prefix over waves
+            run += c;
+        }
+        block_counts[(size_t)blockIdx.x * E + tid] = run;
+    }
+    __syncthreads();
+    const uint64_t lt = lanemask_lt();
+    for (int e = 0; e < E; ++e) {
+        bool mine = (picked >> e) & 1ull;
+        uint64_t bal = __ballot(mine);
+        if (mine) {
+            int r = wave_cnt[wave][e] + __popcll(bal & lt);
+            for (int j = 0; j < k; ++j)
+                if (topk_expert[(size_t)t * k + j] == e) local_rank[(size_t)t * k + j] = r;
+        }
+    }
+}
+
+// One wave: lane e owns expert e.
+__global__ __launch_bounds__(64) void route_scan_kernel(
+    const int32_t* __restrict__ block_counts, int nblocks, int E,
+    int32_t* __restrict__ block_base, int32_t* __restrict__ split_sizes,
+    int32_t* __restrict__ expert_offsets) {
+    const int e = threadIdx.x;
+    int total = 0;
+    if (e < E)
+        for (int b = 0; b < nblocks; ++b) total += block_counts[(size_t)b * E + e];
+    int incl = wave_incl_scan(e < E ? total : 0);
+    int off = incl - (e < E ? total : 0);
+    if (e < E) {
+        split_sizes[e] = total;
+        expert_offsets[e] = off;
+        int run = off;
+        for (int b = 0; b < nblocks; ++b) {
+            int c = block_counts[(size_t)b * E + e];
+            block_base[(size_t)b * E + e] = run;
+            run += c;
+        }
+    }
+    if (e == E - 1) expert_offsets[E] = incl;
+}
+
+__global__ void route_scatter_kernel(const int32_t* __restrict__ topk_expert,
+                                     const int32_t* __restrict__ local_rank,
+                                     const int32_t* __restrict__ block_base, int T, int E, int k,
+                                     int32_t* __restrict__ dest_row,
+                                     int32_t* __restrict__ src_token) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)T * k) return;
+    int t = (int)(i / k);
+    int e = topk_expert[i];
+    int row = block_base[(size_t)(t / kRouteThreads) * E + e] + local_rank[i];
+    dest_row[i] = row;
+    src_token[row] = t;
+}
+
+// Backward of the routing probabilities; one thread per token.
+__global__ void route_bwd_kernel(const float* __restrict__ topk_prob,
+                                 const float* __restrict__ dprob_perm,
+                                 const int32_t* __restrict__ dest_row,
+                                 const int32_t* __restrict__ topk_expert,
+                                 const float* __restrict__ logits, int T, int E, int k,
+                                 uint32_t flags, float* __restrict__ dlogits) {
+    int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    const size_t base = (size_t)t * k;
+    float* out = dlogits + (size_t)t * E;
+    if (flags & 1u) {
+        const float* row = logits + (size_t)t * E;
+        float mx = row[0];
+        for (int e = 1; e < E; ++e) mx = fmaxf(mx, row[e]);
+        float s = 0.f;
+        for (int e = 0; e < E; ++e) s += expf(row[e] - mx);
+        float inv = 1.f / s;
+        float dot = 0.f;
+        for (int j = 0; j < k; ++j) {
+            float p = expf(row[topk_expert[base + j]] - mx) * inv;
+            dot += p * dprob_perm[dest_row[base + j]];
+        }
+        for (int e = 0; e < E; ++e) {
+            float g = 0.f;
+            for (int j = 0; j < k; ++j)
+                if (topk_expert[base + j] == e) g = dprob_perm[dest_row[base + j]];
+            out[e] = expf(row[e] - mx) * inv * (g - dot);
+        }
+        return;
+    }
+    float dot = 0.f;
+    for (int j = 0; j < k; ++j) dot += topk_prob[base + j] * dprob_perm[dest_row[base + j]];
+    for (int e = 0; e < E; ++e) out[e] = 0.f;
+    for (int j = 0; j < k; ++j) {
+        float p = topk_prob[base + j];
+        out[topk_expert[base + j]] = p * (dprob_perm[dest_row[base + j]] - dot);
+    }
+}
+
+size_t route_workspace_bytes(int64_t T, int E, int k) {
+    size_t nb = (size_t)((T + kRouteThreads - 1) / kRouteThreads);
+    size_t bytes = 2 * nb * (size_t)E * sizeof(int32_t)      // counts + bases
+                   + (size_t)T * k * sizeof(int32_t);         // local ranks
+    return (bytes + 255) & ~(size_t)255;
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int k, uint32_t flags,
+                        int32_t* topk_expert, float* topk_prob, int32_t* split_sizes,
+                        int32_t* expert_offsets, int32_t* dest_row, int32_t* src_token,
+                        void* ws, hipStream_t s) {
+    int nb = (T + kRouteThreads - 1) / kRouteThreads;
+    int32_t* counts = (int32_t*)ws;
+    int32_t* bases = counts + (size_t)nb * E;
+    int32_t* ranks = bases + (size_t)nb * E;
+    if (nb > 0)
+        route_topk_kernel<<<nb, kRouteThreads, 0, s>>>(logits, T, E, k, flags, topk_expert,
+                                                       topk_prob, ranks, counts);
+    route_scan_kernel<<<1, 64, 0, s>>>(counts, nb, E, bases, split_sizes, expert_offsets);
+    size_t n = (size_t)T * k;
+    if (n > 0)
+        route_scatter_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+            topk_expert, ranks, bases, T, E, k, dest_row, src_token);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_bwd(const float* topk_prob, const float* dprob_perm,
+                            const int32_t* dest_row, const int32_t* topk_expert,
+                            const float* logits, int T, int E, int k, uint32_t flags,
+                            float* dlogits, hipStream_t s) {
+    if (T > 0)
+        route_bwd_kernel<<<(T + 255) / 256, 256, 0, s>>>(topk_prob, dprob_perm, dest_row,
+                                                         topk_expert, logits, T, E, k, flags,
+                                                         dlogits);
+    return hipGetLastError();
+}
+
+}  // namespace moe

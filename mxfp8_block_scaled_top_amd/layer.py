@@ -1,0 +1,50 @@
+"""One MoE expert-layer step through the C ABI: route, permute, grouped MLP
+forward, unpermute; then the backward: permute dY, grouped MLP backward,
+unpermute dXp, routing backward.  Only calls into libmoe_mi355x; the
+buffers are torch device tensors allocated once per shape (``LayerBuffers``)
+so that a timed loop allocates nothing.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (MOE_BF16, MOE_OP_MLP_BWD, MOE_OP_MLP_FWD, alloc_saved, grouped_mlp_bwd,
+               grouped_mlp_fwd, moe_permute, moe_route, moe_route_bwd, moe_unpermute,
+               moe_workspace_bytes)
+
+
+class LayerBuffers:
+    def __init__(self, T, H, I, E, k, precision, device):
+        rows = T * k
+        self.saved = alloc_saved(rows, H, I, E, precision, device)
+        self.ws_fwd = torch.empty(max(256, moe_workspace_bytes(MOE_OP_MLP_FWD, T, H, I, E, k, precision)),
+                                  dtype=torch.uint8, device=device)
+        self.ws_bwd = torch.empty(max(256, moe_workspace_bytes(MOE_OP_MLP_BWD, T, H, I, E, k, precision)),
+                                  dtype=torch.uint8, device=device)
+        self.dw1 = [torch.empty((2 * I, H), dtype=torch.bfloat16, device=device) for _ in range(E)]
+        self.dw2 = [torch.empty((H, I), dtype=torch.bfloat16, device=device) for _ in range(E)]
+
+
+def layer_step(logits, x, w1, w2, dy, k, precision=MOE_BF16, bufs: LayerBuffers | None = None,
+               with_backward=True, softmax_all=False) -> dict:
+    T, H = x.shape
+    E = len(w1)
+    I = w2[0].shape[1]
+    if bufs is None:
+        bufs = LayerBuffers(T, H, I, E, k, precision, x.device)
+    r = moe_route(logits, k, softmax_all)
+    xp, pp = moe_permute(x, r["dest_row"], r["topk_prob"])
+    yp, saved = grouped_mlp_fwd(xp, r["split_sizes"], w1, w2, pp, precision, bufs.saved, bufs.ws_fwd)
+    y = moe_unpermute(yp, r["dest_row"])
+    out = {"route": r, "xp": xp, "pp": pp, "yp": yp, "saved": saved, "y": y}
+    if not with_backward:
+        return out
+    dyp, _ = moe_permute(dy, r["dest_row"])
+    dxp, dw1, dw2, dpp = grouped_mlp_bwd(dyp, xp, r["split_sizes"], w1, w2, pp, saved, precision,
+                                         bufs.ws_bwd, bufs.dw1, bufs.dw2)
+    dx = moe_unpermute(dxp, r["dest_row"])
+    dlogits = moe_route_bwd(r["topk_prob"], dpp, r["dest_row"], r["topk_expert"], E,
+                            logits if softmax_all else None, softmax_all)
+    out.update({"dyp": dyp, "dxp": dxp, "dw1": dw1, "dw2": dw2, "dpp": dpp, "dx": dx,
+                "dlogits": dlogits})
+    return out

@@ -1,0 +1,118 @@
+"""GPU parity of the grouped expert MLP (forward and backward, BF16 and
+MXFP8) and of the whole layer step against the oracle.
+
+Tolerance: relative Frobenius error 1e-2 (BF16) and 2e-2 (MXFP8, the oracle
+applying the same quantization); routing and the MXFP8 codes of operands
+that both sides quantize from identical bf16 inputs are compared bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_block_scaled_top_amd as moe
+from mxfp8_block_scaled_top_amd import synth
+from mxfp8_block_scaled_top_amd.layer import layer_step
+from oracle import mlp as omlp
+from oracle import mx as omx
+from oracle import route as oroute
+from tests.helpers import need_gpu, np_, rel_frob, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = {moe.MOE_BF16: 1e-2, moe.MOE_MXFP8: 2e-2}
+PREC = {moe.MOE_BF16: "bf16", moe.MOE_MXFP8: "mxfp8"}
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _inputs(T, H, I, E, seed, wstd=0.05, dead=()):
+    rng = np.random.default_rng(seed)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    for e in dead:
+        L[:, e] -= 100.0
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    return {"logits": torch.from_numpy(L), "x": bf(rng.standard_normal((T, H))),
+            "w1": [bf(rng.standard_normal((2 * I, H)) * wstd) for _ in range(E)],
+            "w2": [bf(rng.standard_normal((H, I)) * wstd) for _ in range(E)],
+            "dy": bf(rng.standard_normal((T, H)))}
+
+
+def _layer_compare(inp, k, precision, tag):
+    say(f"layer {tag} prec={PREC[precision]} T={inp['x'].shape[0]} H={inp['x'].shape[1]} "
+        f"I={inp['w2'][0].shape[1]} E={len(inp['w1'])} k={k}")
+    dev = {n: (v.cuda() if isinstance(v, torch.Tensor) else [w.cuda() for w in v])
+           for n, v in inp.items()}
+    got = layer_step(dev["logits"], dev["x"], dev["w1"], dev["w2"], dev["dy"], k, precision)
+    torch.cuda.synchronize()
+    ref = omlp.layer_step(inp["logits"], inp["x"], inp["w1"], inp["w2"], inp["dy"], k,
+                          PREC[precision])
+    r = ref["route"]
+    assert np.array_equal(np_(got["route"]["split_sizes"]), r["split_sizes"])
+    assert np.array_equal(np_(got["route"]["dest_row"]), r["dest_row"])
+    tol = TOL[precision]
+    errs = {"y": rel_frob(got["y"], ref["y"]), "dx": rel_frob(got["dx"], ref["dx"]),
+            "a1": rel_frob(got["saved"]["a1"], ref["fwd"]["a1"]),
+            "dpp": rel_frob(got["dpp"], ref["bwd"]["dpp"]),
+            "dlogits": rel_frob(got["dlogits"], ref["dlogits"])}
+    E = len(inp["w1"])
+    for e in range(E):
+        if r["split_sizes"][e] == 0:
+            assert not got["dw1"][e].any() and not got["dw2"][e].any(), f"empty expert {e}"
+            continue
+        errs[f"dw1_{e}"] = rel_frob(got["dw1"][e], ref["bwd"]["dw1"][e])
+        errs[f"dw2_{e}"] = rel_frob(got["dw2"][e], ref["bwd"]["dw2"][e])
+    say("  errors: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, bad
+    if precision == moe.MOE_MXFP8:
+        H = inp["x"].shape[1]
+        xc, xs = omx.quantize_cols_grouped(ref["xp"], r["split_sizes"])
+        assert np.array_equal(np_(got["saved"]["xp_col_codes"])[: xc.size], xc)
+        assert np.array_equal(np_(got["saved"]["xp_col_scales"])[: xs.size], xs)
+    return got, ref
+
+
+@pytest.mark.parametrize("precision", [moe.MOE_BF16, moe.MOE_MXFP8], ids=["bf16", "mxfp8"])
+def test_tiny_workload(precision):
+    sh = synth.SHAPES["tiny"]
+    inp = synth.layer_inputs(sh)
+    _layer_compare(inp, sh.k, precision, "tiny")
+
+
+@pytest.mark.parametrize("precision", [moe.MOE_BF16, moe.MOE_MXFP8], ids=["bf16", "mxfp8"])
+def test_ragged_tiles(precision):
+    # several 256-row tiles per expert, ragged tails, an empty expert, an
+    # expert with a single row, N not a multiple of 256
+    inp = _inputs(T=700, H=384, I=640, E=6, seed=1, dead=(4,))
+    L = inp["logits"].numpy()
+    L[:, 5] -= 50.0
+    L[0, 5] += 200.0           # exactly one token picks expert 5
+    _layer_compare(inp, 2, precision, "ragged")
+
+
+@pytest.mark.parametrize("precision", [moe.MOE_BF16, moe.MOE_MXFP8], ids=["bf16", "mxfp8"])
+def test_single_expert_dense(precision):
+    inp = _inputs(T=300, H=256, I=256, E=1, seed=2)
+    _layer_compare(inp, 1, precision, "dense")
+
+
+@pytest.mark.parametrize("precision", [moe.MOE_BF16, moe.MOE_MXFP8], ids=["bf16", "mxfp8"])
+def test_many_experts_topk8(precision):
+    inp = _inputs(T=512, H=256, I=384, E=64, seed=3)
+    _layer_compare(inp, 8, precision, "e64k8")
+
+
+def test_deterministic_bf16_and_mx():
+    inp = _inputs(T=400, H=256, I=256, E=4, seed=4)
+    dev = {n: (v.cuda() if isinstance(v, torch.Tensor) else [w.cuda() for w in v]) for n, v in inp.items()}
+    for prec in (moe.MOE_BF16, moe.MOE_MXFP8):
+        a = layer_step(dev["logits"], dev["x"], dev["w1"], dev["w2"], dev["dy"], 2, prec)
+        a = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in a.items()}
+        a_dw1 = [w.clone() for w in a["dw1"]]
+        b = layer_step(dev["logits"], dev["x"], dev["w1"], dev["w2"], dev["dy"], 2, prec)
+        for key in ("y", "dx", "dpp", "dlogits"):
+            assert torch.equal(a[key], b[key]), (prec, key)
+        for e in range(4):
+            assert torch.equal(a_dw1[e], b["dw1"][e])
