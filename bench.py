@@ -1,0 +1,265 @@
+"""Benchmark of the grouped MoE expert-MLP layer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--precision mxfp8|bf16|both]
+                    [--no-cpu] [--workload mixtral|skewed|tiny]
+
+One step = the whole hot path on one batch: route, permute, grouped MLP
+forward (with in-call MXFP8 quantization of activations and the BF16 master
+weights), unpermute; permute dY, grouped MLP backward, unpermute dXp, routing
+backward.  Inputs are synthetic (seeded; the Mixtral-8x7B layer shape:
+T = 8192 tokens, hidden 4096, intermediate 14336, 8 experts, top-2) and
+resident in HBM before the timed region.  Prints one JSON line.
+
+value           tokens/s of the MXFP8 layer step (T / step time)
+roofline        the dominant kernel (largest total time in the step): its
+                algorithmic FLOPs per launch / its mean launch duration,
+                measured with HIP events recorded by the library around each
+                launch on the launch stream during the timed steps
+cpu_baseline    the CPU oracle (tests only otherwise) timed on a bounded
+                sample of the same workload on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"mxfp8": 5000.0, "bf16": 2500.0}   # MI355X dense MFMA (published)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--precision", default="both", choices=["mxfp8", "bf16", "both"])
+    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "skewed", "tiny"])
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--cpu-inter", type=int, default=128)
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_work(name: str, T: int, H: int, I: int, E: int, k: int):
+    """(algorithmic FLOPs, algorithmic HBM bytes) of one launch of a kernel."""
+    A = T * k
+    mx = 1 + 1 / 32      # bytes per element of an MXFP8 tensor (codes + scales)
+    table = {
+        "gemm_mx_gateup_fwd_swiglu": (2 * A * 2 * I * H, 0),
+        "gemm_bf16_gateup_fwd_swiglu": (2 * A * 2 * I * H, 0),
+        "gemm_mx_down_fwd": (2 * A * H * I, 0),
+        "gemm_bf16_down_fwd": (2 * A * H * I, 0),
+        "gemm_mx_down_dgrad_swiglu_bwd": (2 * A * I * H, 0),
+        "gemm_bf16_down_dgrad_swiglu_bwd": (2 * A * I * H, 0),
+        "gemm_mx_down_wgrad": (2 * H * I * A, 0),
+        "gemm_bf16_down_wgrad": (2 * H * I * A, 0),
+        "gemm_mx_gateup_dgrad": (2 * A * 2 * I * H, 0),
+        "gemm_bf16_gateup_dgrad": (2 * A * 2 * I * H, 0),
+        "gemm_mx_gateup_wgrad": (2 * 2 * I * H * A, 0),
+        "gemm_bf16_gateup_wgrad": (2 * 2 * I * H * A, 0),
+        "route_topk": (0, T * E * 4 + A * 12),
+        "route_scan": (0, 0),
+        "route_scatter": (0, A * 16),
+        "route_bwd": (0, A * 16 + T * E * 4),
+        "permute": (0, T * H * 2 + A * H * 2 + A * 8),
+        "unpermute": (0, A * H * 2 + T * H * 2),
+        "mx_quant_rows_xp": (0, A * H * (2 + mx)),
+        "mx_quant_cols_xp": (0, A * H * (2 + mx)),
+        "mx_quant_rows_dyp": (0, A * H * (2 + mx)),
+        "mx_quant_cols_dyp": (0, A * H * (2 + mx)),
+        "mx_quant_rows_w1": (0, E * 2 * I * H * (2 + mx)),
+        "mx_quant_cols_w1": (0, E * 2 * I * H * (2 + mx)),
+        "mx_quant_rows_w2": (0, E * H * I * (2 + mx)),
+        "mx_quant_cols_w2": (0, E * H * I * (2 + mx)),
+        "dprob_reduce": (0, A * ((I + 255) // 256) * 4 + A * 4),
+    }
+    return table.get(name, (0, 0))
+
+
+def run_gpu(args, prec_name, inp_dev, shape):
+    import torch
+    import mxfp8_block_scaled_top_amd as moe
+    from mxfp8_block_scaled_top_amd.layer import LayerBuffers, layer_step
+
+    prec = moe.MOE_MXFP8 if prec_name == "mxfp8" else moe.MOE_BF16
+    T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
+    bufs = LayerBuffers(T, H, I, E, k, prec, "cuda")
+
+    def step():
+        return layer_step(inp_dev["logits"], inp_dev["x"], inp_dev["w1"], inp_dev["w2"],
+                          inp_dev["dy"], k, prec, bufs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    moe.trace_enable(max(64, 64 * args.steps))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    trace = moe.trace_read()
+    moe.trace_disable()
+    ms = (t1 - t0) * 1e3 / args.steps
+    per = {}
+    for name, d in trace:
+        p = per.setdefault(name, {"launches": 0, "total_ms": 0.0})
+        p["launches"] += 1
+        p["total_ms"] += d
+    kernels = {}
+    for name, p in per.items():
+        mean = p["total_ms"] / p["launches"]
+        fl, by = kernel_work(name, T, H, I, E, k)
+        kernels[name] = {"mean_ms": round(mean, 4), "per_step": p["launches"] / args.steps,
+                         "share": round(p["total_ms"] / (ms * args.steps), 4)}
+        if fl:
+            kernels[name]["tflops"] = round(fl / (mean * 1e-3) / 1e12, 1)
+        if by:
+            kernels[name]["gbs"] = round(by / (mean * 1e-3) / 1e9, 1)
+    dom = max(per, key=lambda n: per[n]["total_ms"])
+    dom_mean = per[dom]["total_ms"] / per[dom]["launches"]
+    fl, by = kernel_work(dom, T, H, I, E, k)
+    if fl:
+        roof = {"bound": "mfma", "achieved": round(fl / (dom_mean * 1e-3) / 1e12, 1),
+                "peak": PEAK_TFLOPS[prec_name], "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(by / (dom_mean * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["mean_ms"] = round(dom_mean, 4)
+    flops = 18.0 * H * I * T * k
+    gemm_ms = sum(p["total_ms"] for n, p in per.items() if n.startswith("gemm")) / args.steps
+    return {
+        "tokens_per_s": T / (ms * 1e-3),
+        "ms_per_step": ms,
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "frac_of_peak": flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[prec_name],
+        "gemm_ms": gemm_ms,
+        "gemm_tflops": flops / (gemm_ms * 1e-3) / 1e12,
+        "kernel_ms_sum": sum(p["total_ms"] for p in per.values()) / args.steps,
+        "roofline": roof,
+        "kernels": kernels,
+    }
+
+
+def cpu_baseline(args, inp_host, shape, prec_name):
+    """The oracle on a bounded sample: the first `cpu_tokens` tokens and the
+    first `cpu_inter` intermediate columns (gate rows [0, Is), up rows
+    [I, I+Is) of W1, columns [0, Is) of W2) of every expert; the whole layer
+    step in the same precision.  Every part of the step except the activation
+    quantization scales with the intermediate width, so the full-layer rate is
+    taken as sample_tokens * (Is / I) / time."""
+    import torch
+    from oracle import mlp as omlp
+
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    Ts, Is = min(args.cpu_tokens, shape.T), min(args.cpu_inter, shape.I)
+    I = shape.I
+    w1 = [torch.cat([w[:Is], w[I:I + Is]]).contiguous() for w in inp_host["w1"]]
+    w2 = [w[:, :Is].contiguous() for w in inp_host["w2"]]
+    t0 = time.perf_counter()
+    omlp.layer_step(inp_host["logits"][:Ts], inp_host["x"][:Ts], w1, w2, inp_host["dy"][:Ts],
+                    shape.k, prec_name)
+    t = time.perf_counter() - t0
+    return {"value": round(Ts * (Is / I) / t, 3), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": (f"oracle layer step ({prec_name}, fwd+bwd) on the first {Ts} tokens and "
+                       f"the first {Is} of {I} intermediate columns of all {shape.E} experts "
+                       f"(H={shape.H}, k={shape.k}); took {t:.1f} s; full-layer rate "
+                       f"extrapolated by the intermediate fraction"),
+            "seconds": round(t, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import mxfp8_block_scaled_top_amd as moe
+    from mxfp8_block_scaled_top_amd import synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(3)
+    moe.lib()
+    if not moe.device_supported():
+        print(json.dumps({"error": "device is not gfx950"}))
+        sys.exit(3)
+    torch.cuda.set_device(0)
+    shape = synth.SHAPES[args.workload]
+    t0 = time.perf_counter()
+    inp = synth.layer_inputs(shape)
+    log(args, f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    dev = {n: (v.cuda() if isinstance(v, torch.Tensor) else [w.cuda() for w in v])
+           for n, v in inp.items()}
+    torch.cuda.synchronize()
+
+    precs = ["mxfp8", "bf16"] if args.precision == "both" else [args.precision]
+    res = {}
+    for p in precs:
+        res[p] = run_gpu(args, p, dev, shape)
+        log(args, f"{p}: {res[p]['ms_per_step']:.3f} ms/step, {res[p]['tokens_per_s']:.0f} tokens/s, "
+                  f"{res[p]['tflops']:.1f} TFLOP/s, dominant {res[p]['roofline']['kernel']} "
+                  f"{res[p]['roofline']['achieved']} {res[p]['roofline']['unit']}")
+    head = precs[0]
+    r = res[head]
+    out = {
+        "metric": "grouped expert-MLP tokens/s + TFLOP/s per layer at Mixtral shape, % MFMA peak",
+        "value": round(r["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3" if head == "mxfp8" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{shape.name} layer fwd+bwd, {head}", "T": shape.T, "H": shape.H,
+                   "I": shape.I, "E": shape.E, "k": shape.k, "precision": head},
+        "tflops_per_layer": round(r["tflops"], 1),
+        "frac_of_mfma_peak": round(r["frac_of_peak"], 4),
+        "roofline": r["roofline"],
+        "gemm_only": {"ms": round(r["gemm_ms"], 3), "tflops": round(r["gemm_tflops"], 1),
+                      "frac_of_mfma_peak": round(r["gemm_tflops"] / PEAK_TFLOPS[head], 4)},
+        "kernels": r["kernels"],
+    }
+    for p in precs[1:]:
+        q = res[p]
+        out[p] = {"value": round(q["tokens_per_s"], 1), "unit": "tokens/s",
+                  "ms_per_step": round(q["ms_per_step"], 4), "tflops_per_layer": round(q["tflops"], 1),
+                  "frac_of_mfma_peak": round(q["frac_of_peak"], 4), "roofline": q["roofline"],
+                  "gemm_only": {"ms": round(q["gemm_ms"], 3), "tflops": round(q["gemm_tflops"], 1)},
+                  "kernels": q["kernels"]}
+    if not args.no_cpu:
+        del dev
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(args, inp, shape, head)
+        log(args, f"cpu baseline: {out['cpu_baseline']}")
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

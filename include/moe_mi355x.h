@@ -288,6 +288,22 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
  */
 size_t moe_workspace_bytes(int op, int64_t T, int H, int I, int E, int k, int precision);
 
+
+/*
+ * Launch trace (measurement aid).  moe_trace_enable(capacity) creates, once,
+ * 2*capacity HIP events and starts recording: every kernel launch made by the
+ * calls above is then bracketed by a start and a stop event recorded on the
+ * launch's stream (at most `capacity` launches; later ones are not traced).
+ * After the stream has passed them, moe_trace_read(i, &name, &ms) returns the
+ * i-th launch's kernel name (static string) and duration.  Enabling again
+ * resets the count.  Not for concurrent use from several host threads.
+ * Returns MOE_OK, MOE_ERR_ARG (bad capacity/index) or MOE_ERR_HIP.
+ */
+int moe_trace_enable(int capacity);
+void moe_trace_disable(void);
+int moe_trace_count(void);
+int moe_trace_read(int i, const char** name, float* ms);
+
 #ifdef __cplusplus
 }
 #endif

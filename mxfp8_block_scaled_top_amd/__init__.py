@@ -61,6 +61,10 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(_Saved), P, SZ, P]),
             "grouped_mlp_bwd": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P,
                                       ctypes.POINTER(_Saved), P, P, P, P, P, SZ, P]),
+            "moe_trace_enable": (I32, [I32]),
+            "moe_trace_disable": (None, []),
+            "moe_trace_count": (I32, []),
+            "moe_trace_read": (I32, [I32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -268,3 +272,24 @@ def grouped_mlp_bwd(dyp, xp, split_sizes, w_gate_up, w_down, prob_perm, saved,
                                  _ptr(dpp), _ptr(workspace), workspace.numel(), _stream(dev)),
            "grouped_mlp_bwd")
     return dxp, dw_gate_up, dw_down, dpp
+
+
+def trace_enable(capacity: int) -> None:
+    """Start recording one (name, duration) pair per kernel launch."""
+    _check(lib().moe_trace_enable(capacity), "moe_trace_enable")
+
+
+def trace_disable() -> None:
+    lib().moe_trace_disable()
+
+
+def trace_read() -> list:
+    """[(kernel name, milliseconds)] of the recorded launches; the caller must
+    have synchronized the streams they ran on."""
+    n = lib().moe_trace_count()
+    out = []
+    name, ms = ctypes.c_char_p(), ctypes.c_float()
+    for i in range(n):
+        _check(lib().moe_trace_read(i, ctypes.byref(name), ctypes.byref(ms)), "moe_trace_read")
+        out.append((name.value.decode(), float(ms.value)))
+    return out

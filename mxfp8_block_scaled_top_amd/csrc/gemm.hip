@@ -34,6 +34,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mlp.hpp"
+#include "trace.hpp"
 
 namespace moe {
 
@@ -621,6 +622,7 @@ static hipError_t run(const GemmArgs& g, hipStream_t s) {
     }
     if (tiles == 0) return hipSuccess;
     int64_t grid = (tiles + 7) / 8 * 8;
+    TraceScope ts(g.name ? g.name : "gemm", s);
     gemm_kernel<DT, LA, LB, GRP, EPI><<<(unsigned)grid, kGemmThreads, 0, s>>>(g, ntn, mtm);
     return hipGetLastError();
 }
@@ -648,6 +650,7 @@ hipError_t launch_gemm(int dtype, int la, int lb, int grp, int epi, const GemmAr
 hipError_t launch_dprob_reduce(const float* part, int64_t rows, int ntiles, float* dprob,
                                hipStream_t s) {
     if (rows == 0) return hipSuccess;
+    TraceScope ts("dprob_reduce", s);
     dprob_reduce_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(part, rows, ntiles, dprob);
     return hipGetLastError();
 }

@@ -35,10 +35,11 @@ hipError_t launch_unpermute(const bf16_t* yp, int T, int H, int k, const int32_t
 // ---- MXFP8
 int64_t colwise_block_bound(int64_t rows, int ngroups);
 hipError_t launch_quant_rows(const MatTable& src, const MatTable& codes, const MatTable& scales,
-                             int nmat, int64_t rows, int64_t cols, hipStream_t s);
+                             int nmat, int64_t rows, int64_t cols, hipStream_t s,
+                             const char* name = "mx_quant_rows");
 hipError_t launch_quant_cols(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, const int32_t* sizes, int ngroups, int64_t rows,
-                             int64_t cols, hipStream_t s);
+                             int64_t cols, hipStream_t s, const char* name = "mx_quant_cols");
 hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                int64_t cols, bf16_t* out, hipStream_t s);
 hipError_t launch_dequant_cols(const uint8_t* codes, const uint8_t* scales, const int32_t* sizes,

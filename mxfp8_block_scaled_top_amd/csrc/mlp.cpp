@@ -181,6 +181,7 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
         g.K = H;
         g.a1 = saved->a1;
         g.act = saved->a2;
+        g.name = "gemm_bf16_gateup_fwd_swiglu";
         MOE_TRY(launch_gemm(DT_BF16, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_FWD, g, stream));
         GemmArgs d = g;
         d.a = saved->a2;
@@ -191,6 +192,7 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
         d.K = I;
         d.c = yp;
         d.ldc = H;
+        d.name = "gemm_bf16_down_fwd";
         MOE_TRY(launch_gemm(DT_BF16, L_KMAJ, L_KMAJ, G_M, EPI_STORE, d, stream));
         return MOE_OK;
     }
@@ -199,10 +201,10 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     src.p[0] = xp;
     cd.p[0] = w.xq;
     sc.p[0] = w.xq_s;
-    MOE_TRY(launch_quant_rows(src, cd, sc, 1, rows, H, stream));
+    MOE_TRY(launch_quant_rows(src, cd, sc, 1, rows, H, stream, "mx_quant_rows_xp"));
     cd.p[0] = saved->xp_col_codes;
     sc.p[0] = saved->xp_col_scales;
-    MOE_TRY(launch_quant_cols(src, cd, sc, 1, split_sizes, E, rows, H, stream));
+    MOE_TRY(launch_quant_cols(src, cd, sc, 1, split_sizes, E, rows, H, stream, "mx_quant_cols_xp"));
     MatTable w1t{}, w1c{}, w1s{}, w2t{}, w2c{}, w2s{};
     for (int e = 0; e < E; ++e) {
         w1t.p[e] = w_gate_up[e];
@@ -212,8 +214,8 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
         w2c.p[e] = w.w2q + (size_t)e * H * I;
         w2s.p[e] = w.w2q_s + (size_t)e * H * I / 32;
     }
-    MOE_TRY(launch_quant_rows(w1t, w1c, w1s, E, 2 * (int64_t)I, H, stream));
-    MOE_TRY(launch_quant_rows(w2t, w2c, w2s, E, H, I, stream));
+    MOE_TRY(launch_quant_rows(w1t, w1c, w1s, E, 2 * (int64_t)I, H, stream, "mx_quant_rows_w1"));
+    MOE_TRY(launch_quant_rows(w2t, w2c, w2s, E, H, I, stream, "mx_quant_rows_w2"));
 
     g.a = w.xq;
     g.lda = H;
@@ -230,6 +232,7 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     g.q_row_s = w.a2q_s;
     g.q_col = saved->a2_col_codes;
     g.q_col_s = saved->a2_col_scales;
+    g.name = "gemm_mx_gateup_fwd_swiglu";
     MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_FWD, g, stream));
     GemmArgs d{};
     d.split = split_sizes;
@@ -248,6 +251,7 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     d.K = I;
     d.c = yp;
     d.ldc = H;
+    d.name = "gemm_mx_down_fwd";
     MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_STORE, d, stream));
     return MOE_OK;
 }
@@ -310,6 +314,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
             g.a1 = saved->a1;
             g.act = (bf16_t*)w.da1;
             g.dprob_part = w.part;
+            g.name = "gemm_bf16_down_dgrad_swiglu_bwd";
             MOE_TRY(launch_gemm(DT_BF16, L_KMAJ, L_MNMAJ, G_M, EPI_SWIGLU_BWD, g, stream));
             MOE_TRY(launch_dprob_reduce(w.part, rows, ntn, dprob_perm, stream));
         }
@@ -326,6 +331,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         wg.N = I;
         wg.c_tab = dw2;
         wg.ldc = I;
+        wg.name = "gemm_bf16_down_wgrad";
         MOE_TRY(launch_gemm(DT_BF16, L_MNMAJ, L_MNMAJ, G_K, EPI_STORE, wg, stream));
         if (rows > 0) {
             // gate_up dgrad: dXp = dA1 W1
@@ -341,6 +347,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
             dg.K = 2 * I;
             dg.c = dxp;
             dg.ldc = H;
+            dg.name = "gemm_bf16_gateup_dgrad";
             MOE_TRY(launch_gemm(DT_BF16, L_KMAJ, L_MNMAJ, G_M, EPI_STORE, dg, stream));
         }
         // gate_up wgrad: dW1 [2I, H] = dA1^T Xp
@@ -356,6 +363,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         wg1.N = H;
         wg1.c_tab = dw1;
         wg1.ldc = H;
+        wg1.name = "gemm_bf16_gateup_wgrad";
         MOE_TRY(launch_gemm(DT_BF16, L_MNMAJ, L_MNMAJ, G_K, EPI_STORE, wg1, stream));
         return MOE_OK;
     }
@@ -366,10 +374,11 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         src.p[0] = dyp;
         cd.p[0] = w.dyq;
         sc.p[0] = w.dyq_s;
-        MOE_TRY(launch_quant_rows(src, cd, sc, 1, rows, H, stream));
+        MOE_TRY(launch_quant_rows(src, cd, sc, 1, rows, H, stream, "mx_quant_rows_dyp"));
         cd.p[0] = w.dyc;
         sc.p[0] = w.dyc_s;
-        MOE_TRY(launch_quant_cols(src, cd, sc, 1, split_sizes, E, rows, H, stream));
+        MOE_TRY(launch_quant_cols(src, cd, sc, 1, split_sizes, E, rows, H, stream,
+                                  "mx_quant_cols_dyp"));
     }
     MatTable w1t{}, w1c{}, w1s{}, w2t{}, w2c{}, w2s{};
     for (int e = 0; e < E; ++e) {
@@ -382,8 +391,9 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     }
     if (rows > 0) {
         // W2 [H, I] along H -> [I, H];  W1 [2I, H] along 2I -> [H, 2I]
-        MOE_TRY(launch_quant_cols(w2t, w2c, w2s, E, nullptr, 1, H, I, stream));
-        MOE_TRY(launch_quant_cols(w1t, w1c, w1s, E, nullptr, 1, 2 * (int64_t)I, H, stream));
+        MOE_TRY(launch_quant_cols(w2t, w2c, w2s, E, nullptr, 1, H, I, stream, "mx_quant_cols_w2"));
+        MOE_TRY(launch_quant_cols(w1t, w1c, w1s, E, nullptr, 1, 2 * (int64_t)I, H, stream,
+                                  "mx_quant_cols_w1"));
         GemmArgs g{};
         g.split = split_sizes;
         g.E = E;
@@ -406,6 +416,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         g.q_col = w.da1c;
         g.q_col_s = w.da1c_s;
         g.dprob_part = w.part;
+        g.name = "gemm_mx_down_dgrad_swiglu_bwd";
         MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_BWD, g, stream));
         MOE_TRY(launch_dprob_reduce(w.part, rows, ntn, dprob_perm, stream));
     }
@@ -422,6 +433,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     wg.N = I;
     wg.c_tab = dw2;
     wg.ldc = I;
+    wg.name = "gemm_mx_down_wgrad";
     MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_K, EPI_STORE, wg, stream));
     if (rows > 0) {
         GemmArgs dg{};
@@ -440,6 +452,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         dg.K = 2 * I;
         dg.c = dxp;
         dg.ldc = H;
+        dg.name = "gemm_mx_gateup_dgrad";
         MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_STORE, dg, stream));
     }
     GemmArgs wg1{};
@@ -454,6 +467,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     wg1.N = H;
     wg1.c_tab = dw1;
     wg1.ldc = H;
+    wg1.name = "gemm_mx_gateup_wgrad";
     MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_K, EPI_STORE, wg1, stream));
     return MOE_OK;
 }

@@ -47,6 +47,7 @@ struct GemmArgs {
     uint8_t* q_col_s;
     float* dprob_part;  // SWIGLU_BWD: [rows, n_tiles]
     int I;              // intermediate size (SwiGLU epilogues)
+    const char* name;   // kernel name in launch traces
 };
 
 hipError_t launch_gemm(int dtype, int la, int lb, int grp, int epi, const GemmArgs& g,

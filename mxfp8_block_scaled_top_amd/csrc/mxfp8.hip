@@ -16,6 +16,7 @@
 // quantized by one launch.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "trace.hpp"
 
 namespace moe {
 
@@ -225,19 +226,22 @@ int64_t colwise_block_bound(int64_t rows, int ngroups) {
 }
 
 hipError_t launch_quant_rows(const MatTable& src, const MatTable& codes, const MatTable& scales,
-                             int nmat, int64_t rows, int64_t cols, hipStream_t s) {
+                             int nmat, int64_t rows, int64_t cols, hipStream_t s,
+                             const char* name) {
     int64_t n = (int64_t)nmat * rows * (cols / kMxBlock);
     if (n == 0) return hipSuccess;
+    TraceScope ts(name, s);
     quant_rows_kernel<<<grid_1d(n, 256), 256, 0, s>>>(src, codes, scales, nmat, rows, cols);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_cols(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, const int32_t* sizes, int ngroups, int64_t rows,
-                             int64_t cols, hipStream_t s) {
+                             int64_t cols, hipStream_t s, const char* name) {
     if (rows == 0 || cols == 0 || nmat == 0) return hipSuccess;
     dim3 grid((unsigned)((cols + 1023) / 1024), (unsigned)colwise_block_bound(rows, ngroups),
               (unsigned)nmat);
+    TraceScope ts(name, s);
     quant_cols_kernel<<<grid, 256, 0, s>>>(src, codes, scales, sizes, ngroups, rows, cols);
     return hipGetLastError();
 }
@@ -246,6 +250,7 @@ hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, int6
                                int64_t cols, bf16_t* out, hipStream_t s) {
     int64_t nb = rows * (cols / kMxBlock);
     if (nb == 0) return hipSuccess;
+    TraceScope ts("mx_dequant_rows", s);
     dequant_rows_kernel<<<grid_1d(nb, 256), 256, 0, s>>>((const u32x4*)codes, scales, nb,
                                                          (u32x4*)out);
     return hipGetLastError();
@@ -256,6 +261,7 @@ hipError_t launch_dequant_cols(const uint8_t* codes, const uint8_t* scales, cons
                                hipStream_t s) {
     if (rows == 0 || cols == 0) return hipSuccess;
     dim3 grid((unsigned)((cols + 1023) / 1024), (unsigned)colwise_block_bound(rows, ngroups), 1);
+    TraceScope ts("mx_dequant_cols", s);
     dequant_cols_kernel<<<grid, 256, 0, s>>>(codes, scales, sizes, ngroups, rows, cols, out);
     return hipGetLastError();
 }

@@ -12,6 +12,7 @@
 // of a token and writes the fp32 sum once, rounded to bf16.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "trace.hpp"
 
 namespace moe {
 
@@ -79,6 +80,7 @@ hipError_t launch_permute(const bf16_t* x, int T, int H, int k, const int32_t* d
                           hipStream_t s) {
     size_t n = (size_t)T * (H / 8);
     if (n == 0) return hipSuccess;
+    TraceScope ts("permute", s);
     permute_kernel<<<grid_for(n, 256), 256, 0, s>>>((const u32x4*)x, T, H / 8, k, dest_row,
                                                     topk_prob, (u32x4*)xp,
                                                     topk_prob ? prob_perm : nullptr);
@@ -89,6 +91,7 @@ hipError_t launch_unpermute(const bf16_t* yp, int T, int H, int k, const int32_t
                             const float* topk_prob, bf16_t* y, hipStream_t s) {
     size_t n = (size_t)T * (H / 8);
     if (n == 0) return hipSuccess;
+    TraceScope ts("unpermute", s);
     unpermute_kernel<<<grid_for(n, 256), 256, 0, s>>>((const u32x4*)yp, T, H / 8, k, dest_row,
                                                       topk_prob, (u32x4*)y);
     return hipGetLastError();

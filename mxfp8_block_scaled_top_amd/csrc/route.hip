@@ -17,6 +17,7 @@
 //   3. route_scatter: one thread per pick: dest_row and src_token.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "trace.hpp"
 
 namespace moe {
 
@@ -184,14 +185,21 @@ hipError_t launch_route(const float* logits, int T, int E, int k, uint32_t flags
     int32_t* counts = (int32_t*)ws;
     int32_t* bases = counts + (size_t)nb * E;
     int32_t* ranks = bases + (size_t)nb * E;
-    if (nb > 0)
+    if (nb > 0) {
+        TraceScope ts("route_topk", s);
         route_topk_kernel<<<nb, kRouteThreads, 0, s>>>(logits, T, E, k, flags, topk_expert,
                                                        topk_prob, ranks, counts);
-    route_scan_kernel<<<1, 64, 0, s>>>(counts, nb, E, bases, split_sizes, expert_offsets);
+    }
+    {
+        TraceScope ts("route_scan", s);
+        route_scan_kernel<<<1, 64, 0, s>>>(counts, nb, E, bases, split_sizes, expert_offsets);
+    }
     size_t n = (size_t)T * k;
-    if (n > 0)
+    if (n > 0) {
+        TraceScope ts("route_scatter", s);
         route_scatter_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
             topk_expert, ranks, bases, T, E, k, dest_row, src_token);
+    }
     return hipGetLastError();
 }
 
@@ -199,10 +207,12 @@ hipError_t launch_route_bwd(const float* topk_prob, const float* dprob_perm,
                             const int32_t* dest_row, const int32_t* topk_expert,
                             const float* logits, int T, int E, int k, uint32_t flags,
                             float* dlogits, hipStream_t s) {
-    if (T > 0)
+    if (T > 0) {
+        TraceScope ts("route_bwd", s);
         route_bwd_kernel<<<(T + 255) / 256, 256, 0, s>>>(topk_prob, dprob_perm, dest_row,
                                                          topk_expert, logits, T, E, k, flags,
                                                          dlogits);
+    }
     return hipGetLastError();
 }
 
