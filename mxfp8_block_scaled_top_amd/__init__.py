@@ -18,7 +18,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "_lib", "libmoe_mi355x.so")
+LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(_PKG, "_lib", "libmoe_mi355x.so")
 
 MOE_BF16, MOE_MXFP8 = 0, 1
 MOE_ROUTE_RENORM, MOE_ROUTE_SOFTMAX_ALL = 0, 1

@@ -42,9 +42,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the ROCm toolchain is required to build the library")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, extra=(), odir: str = BUILD) -> str:
+    obj = os.path.join(odir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,28 +56,37 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
+def build(jobs: int = 8, verbose: bool = False, defines=(), out: str | None = None,
+          objdir: str | None = None) -> str:
+    """Compile every source and link the library (``out`` defaults to the
+    in-tree path; ``defines`` are extra -D flags)."""
+    lib_path = out or LIB
+    odir = objdir or BUILD
+    os.makedirs(odir, exist_ok=True)
+    os.makedirs(os.path.dirname(lib_path), exist_ok=True)
+    extra = [f"-D{d}" for d in defines]
     with ThreadPoolExecutor(max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, extra, odir), SOURCES))
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("-D", dest="defines", action="append", default=[])
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--objdir", default=None)
     a = ap.parse_args()
-    print(build(a.jobs, a.verbose))
+    print(build(a.jobs, a.verbose, a.defines, a.out, a.objdir))
 
 
 if __name__ == "__main__":

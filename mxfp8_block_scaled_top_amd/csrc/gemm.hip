@@ -8,20 +8,27 @@
 // next GEMM reads [same page, section on MXFP8 and the fused MLP].
 //
 // Work decomposition
-//   * 256 x 256 output tile per workgroup of 512 threads (8 waves, 2 x 4);
-//     every wave owns a 128 x 64 sub-tile = 4 x 2 MFMA 32x32 fragments.
+//   * 256 x 256 output tile per workgroup of 256 threads (4 waves, 2 x 2);
+//     every wave owns a 128 x 128 sub-tile = 4 x 4 MFMA 32x32 fragments whose
+//     256 fp32 accumulators live in the accumulation registers (one wave per
+//     SIMD, 512 registers per lane).
 //   * K steps of 128 bytes per operand row: 64 bf16 (4 x
 //     v_mfma_f32_32x32x16_bf16) or 128 E4M3 (2 x
 //     v_mfma_scale_f32_32x32x64_f8f6f4 with one E8M0 scale per 32 K-values
 //     and row, fed straight to the instruction).
-//   * Operand tiles are staged through LDS, double-buffered (2 x 64 KiB):
-//     the next K step is loaded to registers while the current one feeds the
-//     MFMAs.  16-byte chunks of a 128-byte LDS row are XOR-swizzled by
-//     (row ^ row >> 3) & 7 so the 16-byte fragment reads of 16 consecutive
-//     rows hit distinct banks.
-//   * Operands contiguous along M/N (the bf16 weight-gradient and dgrad
-//     operands) are loaded as 4 K-rows x 8 elements per thread and transposed
-//     in registers before the LDS store, so every LDS row is K-contiguous.
+//   * LDS holds two stages of both operand tiles (2 x 64 KiB).  K-contiguous
+//     operands go from memory to LDS without passing through registers
+//     (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at the wave's
+//     LDS base + 16 * lane, so the lane chooses which global chunk fills its
+//     slot); 16-byte chunks of a 128-byte tile row are XOR-swizzled by
+//     (row ^ row >> 3) & 7 so 16-byte fragment reads of 16 consecutive rows
+//     hit distinct banks.  Offsets past a row's valid K read zeros.
+//   * M/N-contiguous bf16 operands (the dgrad weights and both weight-gradient
+//     operands) are staged through registers into LDS in their natural
+//     [k][m] order (16-byte chunks of a 512-byte row XOR-ed with 4*(k&3)) and
+//     turned into K-packed MFMA fragments by ds_read_b64_tr_b16, which
+//     transposes 4 K-rows x 16 columns across each 16-lane group.
+//   * Stage k+1 is loaded while stage k feeds the MFMAs; one barrier per K step.
 //   * Grouping: the tile list is the concatenation over experts of their
 //     tiles (ragged M: ceil(M_e / 256) x N-tiles each; ragged K: a fixed
 //     M x N grid each, looping over the expert's rows).  The per-expert prefix
@@ -41,15 +48,25 @@ namespace moe {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-constexpr int kRowB = 128;                    // LDS bytes per tile row per K step
+constexpr int kRowB = 128;                    // K-contiguous LDS tile row (bytes / K step)
 constexpr int kTileB = kGemmBM * kRowB;       // 32 KiB per operand per stage
 constexpr int kStageB = 2 * kTileB;           // A + B
 constexpr int kLdsB = 2 * kStageB;            // double-buffered: 128 KiB
+constexpr int kMNRowB = kGemmBM * 2;          // M/N-contiguous LDS row: 256 bf16 = 512 B
+constexpr uint32_t kOob = 0x80000000u;        // buffer offset that reads zeros
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ int lds_off(int row, int chunk) {
     return row * kRowB + ((chunk ^ swz(row)) << 4);
+}
+// M/N-contiguous tile: row k (64 rows per stage), 16-byte chunk c (32 per row)
+__device__ __forceinline__ int mn_off(int k, int c) {
+    return k * kMNRowB + ((c ^ ((k & 3) << 2)) << 4);
 }
 
 // Per-workgroup tile descriptor.
@@ -62,6 +79,21 @@ struct Tile {
     int pad_e;       // padded size of this expert
     int n_tile;
 };
+
+// Order of the mt x nt tiles of one expert: bands of kGroupM row-tiles, and
+// inside a band the row-tiles vary fastest.  Consecutive workgroups (which
+// run together on one XCD) then share both operands: each weight tile is read
+// by up to kGroupM concurrent tiles and each activation tile by the band's
+// column-tiles in flight.
+constexpr int kGroupM = 8;
+__device__ __forceinline__ void grouped_order(int t, int mt, int nt, int& m, int& n) {
+    int band = t / (kGroupM * nt);
+    int m0 = band * kGroupM;
+    int gm = min(mt - m0, kGroupM);
+    int r = t - band * kGroupM * nt;
+    m = m0 + r % gm;
+    n = r / gm;
+}
 
 // Builds the per-expert prefix tables in LDS and decodes the tile.  Returns
 // false when this workgroup has no tile (uniform over the workgroup).
@@ -85,18 +117,20 @@ __device__ bool decode_tile(const GemmArgs& g, int ntn, int mtm, int t, int* sch
         if (e >= g.E) return false;
         tloc = t - (e ? sched[e - 1] : 0);
         int mt = (sched[128 + e] + kGemmBM - 1) / kGemmBM;
-        tl.n_tile = tloc / mt;
-        tl.m0 = (tloc - tl.n_tile * mt) * kGemmBM;
+        int m;
+        grouped_order(tloc, mt, ntn, m, tl.n_tile);
+        tl.m0 = m * kGemmBM;
     } else {
         int per = mtm * ntn;
         e = t / per;
         if (e >= g.E) return false;
         tloc = t - e * per;
-        tl.n_tile = tloc / mtm;
-        tl.m0 = (tloc - tl.n_tile * mtm) * kGemmBM;
+        int m;
+        grouped_order(tloc, mtm, ntn, m, tl.n_tile);
+        tl.m0 = m * kGemmBM;
     }
     tl.e = e;
-    tl.n0 = tl.n_tile * (kGemmBN);
+    tl.n0 = tl.n_tile * kGemmBN;
     tl.row0 = e ? sched[64 + e - 1] : 0;
     tl.rows_e = sched[128 + e];
     tl.pbase = (int64_t)(e ? sched[192 + e - 1] : 0) * 32;
@@ -105,45 +139,45 @@ __device__ bool decode_tile(const GemmArgs& g, int ntn, int mtm, int t, int* sch
 }
 
 // ---------------------------------------------------------------- operand loads
-// K-contiguous operand: rows of `stride` bytes; the tile row r maps to global
-// row grow(r) (clamped into [0, rows_valid)); K bytes beyond kbytes read zero.
+// K-contiguous operand: rows of `stride` bytes from `base`; tile row r maps to
+// operand row kop_row(r) (clamped into [0, rows_valid)); K bytes at or past
+// kbytes read zero.  Offsets from `base` stay below 2^31 (checked by the host).
 struct KOp {
     const uint8_t* base;
     int64_t stride;
-    int64_t row_first;  // global row of tile row 0 (linear map)
-    int rows_valid;     // global rows that exist (for clamping)
-    int64_t kbytes;
+    int row_first;      // operand row of tile row 0 (linear map)
+    int rows_valid;     // operand rows that exist (for clamping)
+    int kbytes;
     int pair_I;         // >0: SwiGLU pairing of gate/up rows (tile covers 128 j)
     int j0;
 };
 
-__device__ __forceinline__ int64_t kop_row(const KOp& op, int r) {
-    int64_t gr;
+__device__ __forceinline__ int kop_row(const KOp& op, int r) {
+    int gr;
     if (op.pair_I > 0)
-        gr = (int64_t)((r >> 5) & 1) * op.pair_I + op.j0 + (r >> 6) * 32 + (r & 31);
+        gr = ((r >> 5) & 1) * op.pair_I + op.j0 + (r >> 6) * 32 + (r & 31);
     else
         gr = op.row_first + r;
-    return gr < op.rows_valid ? gr : (int64_t)op.rows_valid - 1;
+    return gr < op.rows_valid ? gr : op.rows_valid - 1;
 }
 
-__device__ __forceinline__ void load_kop(const KOp& op, int64_t k0b, u32x4 (&r)[4]) {
-    const int tid = threadIdx.x;
+// LDS-DMA of one K step of a K-contiguous tile: the wave's 8 instructions
+// cover tile rows (wave*8 + j)*8 .. +7; slot i of instruction j is tile row
+// (wave*8 + j)*8 + i/8 and physical chunk i%8, whose logical chunk is
+// (i%8) ^ swz(row) = (i%8) ^ (i/8) ^ j.
+__device__ __forceinline__ void dma_kop(const KOp& op, int k0b, uint8_t* lds) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)op.base, 0, 0x7fffffff, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int id = tid + i * kGemmThreads;
-        int row = id >> 3, kc = id & 7;
-        int64_t kb = k0b + kc * 16;
-        r[i] = (u32x4){0u, 0u, 0u, 0u};
-        if (kb < op.kbytes) r[i] = *(const u32x4*)(op.base + kop_row(op, row) * op.stride + kb);
-    }
-}
-
-__device__ __forceinline__ void store_kop(uint8_t* lds, const u32x4 (&r)[4]) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int id = tid + i * kGemmThreads;
-        *(u32x4*)(lds + lds_off(id >> 3, id & 7)) = r[i];
+    for (int j = 0; j < 8; ++j) {
+        int r = (wave * 8 + j) * 8 + (lane >> 3);
+        int kc16 = (((lane & 7) ^ (lane >> 3) ^ j) & 7) * 16 + k0b;
+        uint32_t o = kc16 < op.kbytes
+                         ? (uint32_t)((int64_t)kop_row(op, r) * op.stride) + (uint32_t)kc16
+                         : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + (wave * 8 + j) * 1024),
+                                                 16, o, 0, 0, 0);
     }
 }
 
@@ -155,31 +189,44 @@ struct MNOp {
     int mn_valid;
 };
 
-__device__ __forceinline__ void load_mnop(const MNOp& op, int k0, u32x4 (&r)[4]) {
+// 64 K-rows x 256 columns: 2048 16-byte chunks, 8 per thread (chunk id =
+// tid + 256 i: row id >> 5, column chunk id & 31).
+__device__ __forceinline__ void load_mnop(const MNOp& op, int k0, u32x4* r) {
     const int tid = threadIdx.x;
-    const int mc = tid & 31, kg = tid >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int k = k0 + kg * 4 + i;
+    for (int i = 0; i < 8; ++i) {
+        int id = tid + i * 256;
+        int k = k0 + (id >> 5), c = id & 31;
         r[i] = (u32x4){0u, 0u, 0u, 0u};
-        if (k < op.k_valid && mc * 8 < op.mn_valid)
-            r[i] = *(const u32x4*)(op.base + (int64_t)k * op.stride + mc * 16);
+        if (k < op.k_valid && c * 8 < op.mn_valid)
+            r[i] = *(const u32x4*)(op.base + (int64_t)k * op.stride + c * 16);
     }
 }
 
-// 4 K-rows x 8 elements -> 8 LDS rows (one per element) of 4 K-values.
-__device__ __forceinline__ void store_mnop(uint8_t* lds, const u32x4 (&r)[4]) {
+__device__ __forceinline__ void store_mnop(uint8_t* lds, const u32x4* r) {
     const int tid = threadIdx.x;
-    const int mc = tid & 31, kg = tid >> 5;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-        const int w = n >> 1, sh = (n & 1) * 16;
-        uint32_t e0 = (r[0][w] >> sh) & 0xffffu, e1 = (r[1][w] >> sh) & 0xffffu;
-        uint32_t e2 = (r[2][w] >> sh) & 0xffffu, e3 = (r[3][w] >> sh) & 0xffffu;
-        int row = mc * 8 + n;
-        *(u32x2*)(lds + lds_off(row, kg >> 1) + ((kg & 1) << 3)) =
-            (u32x2){e0 | (e1 << 16), e2 | (e3 << 16)};
+    for (int i = 0; i < 8; ++i) {
+        int id = tid + i * 256;
+        *(u32x4*)(lds + mn_off(id >> 5, id & 31)) = r[i];
     }
+}
+
+// K-packed bf16 fragment (8 K-values, K sub-step s, columns colbase..+31) of
+// an M/N-contiguous LDS tile, via two transposing reads: in each 16-lane
+// group g, lane q supplies (K row kb + q/4, columns n..n+3) and receives
+// column n0 + q for 4 consecutive K rows.
+__device__ __forceinline__ bf16x8_t mn_frag(const uint8_t* lds, int s, int colbase) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, q = lane & 15;
+    const int kb = 16 * s + 8 * (g >> 1) + (q >> 2);
+    const int n = colbase + 16 * (g & 1) + 4 * (q & 3);       // element column
+    const int c = n >> 3, sub = (n & 7) * 2;                   // 16-byte chunk, byte in chunk
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds + mn_off(kb, c) + sub));
+    i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)(lds + mn_off(kb + 4, c) + sub));
+    i16x8 v = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
 }
 
 // MXFP8 scales of one K step (4 blocks of 32) for one tile row, as a dword
@@ -212,76 +259,260 @@ __device__ __forceinline__ float half_sum32(float v) {
     return v;
 }
 
-// Row (along the 32 columns of a fragment) + column (along its 32 rows)
-// MXFP8 quantization of one 32x32 fragment value set held in MFMA C layout.
-// vals[v] is the value at row (4*(lane>>5) + 8*(v>>2) + (v&3)), column lane&31.
-struct QOut {
-    uint8_t* row_codes;   // + grouped row * row_ld + column
-    int64_t row_ld;
-    uint8_t* row_scales;  // + grouped row * (row_ld/32) + column/32
-    uint8_t* col_codes;   // grouped columnwise layout base of this expert (+ pbase*C)
-    uint8_t* col_scales;
-    int64_t C;            // columns of the columnwise layout
-};
+// ---------------------------------------------------------------- epilogue staging
+// The SwiGLU epilogues stage each 32-row slice of a wave's 128x128 result
+// through a private 32 x 128 fp32 LDS region (16-byte chunks XOR-swizzled by
+// row & 7), so that global traffic is 16-byte row / column pieces and the
+// MXFP8 block maxima are per-lane reductions:
+//   phase 1  the wave writes its 4 fragments of row slice fi;
+//   phase 2  lane (row = lane/2, half = lane&1) handles 32-column blocks of
+//            one row: SwiGLU math, bf16 stores, rowwise MXFP8 (codes + scale);
+//   phase 3  lane = column: the 32 rows of one column -> columnwise MXFP8.
+__device__ __forceinline__ int st_idx(int row, int col) {
+    return row * 128 + ((((col >> 2) ^ (row & 7))) << 2) + (col & 3);
+}
 
-__device__ __forceinline__ void quant_fragment(const float (&vals)[16], int64_t grow0,
-                                               int frow0, int rows_e, int pad_e, int col,
-                                               int64_t pbase, const QOut& q) {
-    const int lane = threadIdx.x & 63;
-    const int hi = lane >> 5;
-    // rowwise: each row's 32 values sit in the 32 lanes of one half-wave
+__device__ __forceinline__ void stage_fragments(float* R, const f32x16& f0, const f32x16& f1,
+                                                const f32x16& f2, const f32x16& f3) {
+    const int lane = threadIdx.x & 63, fr = lane & 31, hi = lane >> 5;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-        int lr = 4 * hi + 8 * (v >> 2) + (v & 3);
-        float m = half_max32(__builtin_fabsf(vals[v]));
-        uint32_t S = mx_scale_byte(m);
-        if (frow0 + lr < rows_e) {
-            int64_t gr = grow0 + lr;
-            q.row_codes[gr * q.row_ld + col] = (uint8_t)mx_encode(vals[v], S);
-            if ((lane & 31) == 0) q.row_scales[gr * (q.row_ld / 32) + col / 32] = (uint8_t)S;
-        }
+        int row = 4 * hi + 8 * (v >> 2) + (v & 3);
+        R[st_idx(row, fr)] = f0[v];
+        R[st_idx(row, 32 + fr)] = f1[v];
+        R[st_idx(row, 64 + fr)] = f2[v];
+        R[st_idx(row, 96 + fr)] = f3[v];
     }
-    // columnwise: the fragment's 32 rows are one block (rows past the expert
-    // count as zero); lane and lane^32 hold the two halves
-    if (frow0 < rows_e) {
-        float m = 0.f;
+}
+
+__device__ __forceinline__ void load_row8(const float* R, int row, int col, float (&x)[8]) {
+    float4 a = *(const float4*)(R + st_idx(row, col));
+    float4 b = *(const float4*)(R + st_idx(row, col + 4));
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ void store_row8(float* R, int row, int col, const float* x) {
+    *(float4*)(R + st_idx(row, col)) = make_float4(x[0], x[1], x[2], x[3]);
+    *(float4*)(R + st_idx(row, col + 4)) = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+__device__ __forceinline__ u32x4 pack8_bf16(const float* x) {
+    return (u32x4){pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                   pack_bf16x2(x[6], x[7])};
+}
+
+__device__ __forceinline__ void unpack8_bf16(u32x4 w, float* x) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            int lr = 4 * hi + 8 * (v >> 2) + (v & 3);
-            if (frow0 + lr < rows_e) m = fmaxf(m, __builtin_fabsf(vals[v]));
-        }
-        m = fmaxf(m, __shfl_xor(m, 32));
-        uint32_t S = mx_scale_byte(m);
-        uint8_t* dst = q.col_codes + pbase * q.C + (int64_t)col * pad_e + frow0;
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = lo_bf16(w[i]);
+        x[2 * i + 1] = hi_bf16(w[i]);
+    }
+}
+
+// One block of 32 values -> E8M0 scale and 32 E4M3 codes as two 16-byte words.
+__device__ __forceinline__ uint32_t quant32(const float* x, u32x4& c0, u32x4& c1) {
+    float m = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t w = 0;
+    for (int i = 0; i < 32; ++i) m = fmaxf(m, __builtin_fabsf(x[i]));
+    uint32_t S = mx_scale_byte(m);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int v = 4 * j + i;
-                int lr = 4 * hi + 8 * j + i;
-                float x = frow0 + lr < rows_e ? vals[v] : 0.f;
-                w |= mx_encode(x, S) << (8 * i);
+    for (int w = 0; w < 8; ++w) {
+        uint32_t word = mx_encode(x[4 * w], S) | (mx_encode(x[4 * w + 1], S) << 8) |
+                        (mx_encode(x[4 * w + 2], S) << 16) | (mx_encode(x[4 * w + 3], S) << 24);
+        if (w < 4) c0[w] = word;
+        else c1[w - 4] = word;
+    }
+    return S;
+}
+
+// Columnwise MXFP8 of column `col` of the staged region (32 rows, rows at or
+// past `valid` count as zero) into the grouped columnwise layout.
+__device__ __forceinline__ void col_quant(const float* R, int col, int valid, uint8_t* codes,
+                                          uint8_t* scale) {
+    float x[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) x[r] = r < valid ? R[st_idx(r, col)] : 0.f;
+    u32x4 c0, c1;
+    uint32_t S = quant32(x, c0, c1);
+    ((u32x4*)codes)[0] = c0;
+    ((u32x4*)codes)[1] = c1;
+    *scale = (uint8_t)S;
+}
+
+struct EpiCtx {
+    const GemmArgs& g;
+    const Tile& tl;
+    int wm, wn, ntn;
+};
+
+// ScaledSwiGLU forward of row slice fi of the wave's tile.  Staged columns
+// [64q, 64q+32) are gate and [64q+32, 64q+64) up for j = tile j0 + (2wn+q)*32.
+template <int DT>
+__device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const f32x16& f0,
+                                                const f32x16& f1, const f32x16& f2,
+                                                const f32x16& f3, int fi) {
+    const GemmArgs& g = c.g;
+    const Tile& tl = c.tl;
+    const int lane = threadIdx.x & 63;
+    const int64_t I = g.I;
+    stage_fragments(R, f0, f1, f2, f3);
+    __syncthreads();
+    const int frow0 = tl.m0 + c.wm * 128 + fi * 32;      // row inside the expert
+    const int valid = min(32, tl.rows_e - frow0);          // rows of this slice that exist
+    {
+        const int row = lane >> 1, q = lane & 1;
+        const int j0 = tl.n_tile * (kGemmBN / 2) + (2 * c.wn + q) * 32;
+        float a2[32];
+        if (row < valid) {
+            const int64_t gr = tl.row0 + frow0 + row;
+            const float p = g.prob[gr];
+            u32x4* a1g = (u32x4*)(g.a1 + gr * 2 * I + j0);
+            u32x4* a1u = (u32x4*)(g.a1 + gr * 2 * I + I + j0);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                float gt[8], up[8];
+                load_row8(R, row, 64 * q + 8 * b, gt);
+                load_row8(R, row, 64 * q + 32 + 8 * b, up);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) a2[8 * b + i] = p * silu_f(gt[i]) * up[i];
+                a1g[b] = pack8_bf16(gt);
+                a1u[b] = pack8_bf16(up);
             }
-            *(uint32_t*)(dst + 4 * hi + 8 * j) = w;
+            if (DT == DT_BF16) {
+                u32x4* o = (u32x4*)(g.act + gr * I + j0);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) o[b] = pack8_bf16(a2 + 8 * b);
+            } else {
+                u32x4 c0, c1;
+                uint32_t S = quant32(a2, c0, c1);
+                u32x4* o = (u32x4*)(g.q_row + gr * I + j0);
+                o[0] = c0;
+                o[1] = c1;
+                g.q_row_s[gr * (I / 32) + j0 / 32] = (uint8_t)S;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) a2[i] = 0.f;
         }
-        if (hi == 0)
-            q.col_scales[pbase / 32 * q.C + (int64_t)col * (pad_e / 32) + frow0 / 32] = (uint8_t)S;
-    } else {
-        // keep the shuffle pattern uniform across the wave
-        (void)__shfl_xor(0.f, 32);
+        if (DT == DT_MX)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) store_row8(R, row, 64 * q + 8 * b, a2 + 8 * b);
     }
+    __syncthreads();
+    if (DT == DT_MX && valid > 0) {
+        const int q = lane >> 5, jj = lane & 31;
+        const int64_t j = tl.n_tile * (kGemmBN / 2) + (2 * c.wn + q) * 32 + jj;
+        col_quant(R, 64 * q + jj, valid, g.q_col + tl.pbase * I + j * tl.pad_e + frow0,
+                  g.q_col_s + tl.pbase / 32 * I + j * (tl.pad_e / 32) + frow0 / 32);
+    }
+    __syncthreads();
+}
+
+// SwiGLU backward of row slice fi: staged columns are dA2 for j = n0 + wn*128
+// + col.  Writes dA1 (bf16, or rowwise + columnwise MXFP8) and the row's
+// probability-gradient partial over these 128 columns into red.
+template <int DT>
+__device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float* R2,
+                                                float* red, const f32x16& f0, const f32x16& f1,
+                                                const f32x16& f2, const f32x16& f3, int fi) {
+    const GemmArgs& g = c.g;
+    const Tile& tl = c.tl;
+    const int lane = threadIdx.x & 63;
+    const int64_t I = g.I;
+    stage_fragments(R, f0, f1, f2, f3);
+    __syncthreads();
+    const int frow0 = tl.m0 + c.wm * 128 + fi * 32;
+    const int valid = min(32, tl.rows_e - frow0);
+    const int jw = tl.n0 + c.wn * 128;                      // first column of the wave
+    const bool slab = jw < I;                              // I % 128 == 0: all or nothing
+    const int row = lane >> 1, h = lane & 1;
+    float part = 0.f;
+#pragma unroll 1
+    for (int blk = 0; blk < 2; ++blk) {
+        const int cb = 64 * h + 32 * blk;                   // staged column of the block
+        float dg[32], du[32];
+        if (slab && row < valid) {
+            const int64_t gr = tl.row0 + frow0 + row;
+            const float p = g.prob[gr];
+            const u32x4* a1g = (const u32x4*)(g.a1 + gr * 2 * I + jw + cb);
+            const u32x4* a1u = (const u32x4*)(g.a1 + gr * 2 * I + I + jw + cb);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                float d[8], gt[8], up[8];
+                load_row8(R, row, cb + 8 * b, d);
+                unpack8_bf16(a1g[b], gt);
+                unpack8_bf16(a1u[b], up);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    float sg = sigmoid_f(gt[i]);
+                    float sl = gt[i] * sg;
+                    float dp = d[i] * p;
+                    dg[8 * b + i] = dp * up[i] * sg * (1.f + gt[i] * (1.f - sg));
+                    du[8 * b + i] = dp * sl;
+                    part += d[i] * sl * up[i];
+                }
+            }
+            if (DT == DT_BF16) {
+                u32x4* og = (u32x4*)(g.act + gr * 2 * I + jw + cb);
+                u32x4* ou = (u32x4*)(g.act + gr * 2 * I + I + jw + cb);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    og[b] = pack8_bf16(dg + 8 * b);
+                    ou[b] = pack8_bf16(du + 8 * b);
+                }
+            } else {
+                u32x4 c0, c1;
+                uint32_t S = quant32(dg, c0, c1);
+                u32x4* o = (u32x4*)(g.q_row + gr * 2 * I + jw + cb);
+                o[0] = c0;
+                o[1] = c1;
+                g.q_row_s[gr * (2 * I / 32) + (jw + cb) / 32] = (uint8_t)S;
+                S = quant32(du, c0, c1);
+                o = (u32x4*)(g.q_row + gr * 2 * I + I + jw + cb);
+                o[0] = c0;
+                o[1] = c1;
+                g.q_row_s[gr * (2 * I / 32) + (I + jw + cb) / 32] = (uint8_t)S;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) dg[i] = du[i] = 0.f;
+        }
+        if (DT == DT_MX) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                store_row8(R, row, cb + 8 * b, dg + 8 * b);
+                store_row8(R2, row, cb + 8 * b, du + 8 * b);
+            }
+        }
+    }
+    part += __shfl_xor(part, 1);
+    if (h == 0) red[c.wn * kGemmBM + c.wm * 128 + fi * 32 + row] = part;
+    __syncthreads();
+    if (DT == DT_MX && slab && valid > 0) {
+#pragma unroll 1
+        for (int t = 0; t < 4; ++t) {
+            const int col = lane + 64 * t;                  // 0..127 dg, 128..255 du
+            const int cc = col & 127;
+            const int64_t j = (col < 128 ? 0 : I) + jw + cc;
+            col_quant(col < 128 ? R : R2, cc, valid,
+                      g.q_col + tl.pbase * 2 * I + j * tl.pad_e + frow0,
+                      g.q_col_s + tl.pbase / 32 * 2 * I + j * (tl.pad_e / 32) + frow0 / 32);
+        }
+    }
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------- the kernel
 template <int DT, int LA, int LB, int GRP, int EPI>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int ntn, int mtm) {
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsB];
-    __shared__ uint32_t ssc[2][2][kGemmBM];    // MXFP8 scales [stage][A/B][row]
+    __shared__ uint32_t ssc[2][2][kGemmBM];    // MXFP8 scales [stage][A/B][tile row]
     __shared__ int sched[256];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave >> 1, wn = wave & 1;
 
     // XCD-aware remap: dispatch is round-robin over 8 XCDs; hand XCD x the
     // contiguous logical range [x*G/8, (x+1)*G/8).
@@ -295,24 +526,24 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int ntn,
     constexpr int kElemB = DT == DT_BF16 ? 2 : 1;
     KOp ka{}, kb{};
     MNOp ma{}, mb{};
-    int64_t kext;       // K extent in elements
-    const uint8_t* sa_row = nullptr;   // scale row of this thread's A/B row (MX)
+    int kext;                          // K extent in elements
+    const uint8_t* srow = nullptr;     // MXFP8 scale row of this thread's A row / B row
+    const uint8_t* srow_b = nullptr;
     int nblk = 0;
     bool sdw = false;
     if (GRP == G_M) {
         kext = g.K;
-        ka.base = (const uint8_t*)g.a;
+        ka.base = (const uint8_t*)g.a + (tl.row0 + tl.m0) * g.lda * kElemB;
         ka.stride = g.lda * kElemB;
-        ka.row_first = tl.row0 + tl.m0;
-        ka.rows_valid = (int)g.rows;
-        ka.kbytes = (int64_t)g.K * kElemB;
-        ka.pair_I = 0;
+        ka.row_first = 0;
+        ka.rows_valid = (int)(g.rows - (tl.row0 + tl.m0));
+        ka.kbytes = g.K * kElemB;
         if (LB == L_KMAJ) {
             kb.base = (const uint8_t*)g.b.p[tl.e];
             kb.stride = g.ldb * kElemB;
             kb.row_first = tl.n0;
             kb.rows_valid = EPI == EPI_SWIGLU_FWD ? 2 * g.I : g.N;
-            kb.kbytes = (int64_t)g.K * kElemB;
+            kb.kbytes = g.K * kElemB;
             kb.pair_I = EPI == EPI_SWIGLU_FWD ? g.I : 0;
             kb.j0 = tl.n_tile * (kGemmBN / 2);
         } else {
@@ -324,13 +555,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int ntn,
         if (DT == DT_MX) {
             nblk = g.K / 32;
             sdw = true;
-            if (tid < kGemmBM) {
-                int64_t r = kop_row(ka, tid);
-                sa_row = g.a_scale + r * g.lda_s;
-            } else {
-                int64_t r = kop_row(kb, tid - kGemmBM);
-                sa_row = (const uint8_t*)g.b_scale.p[tl.e] + r * g.ldb_s;
-            }
+            srow = g.a_scale + (tl.row0 + tl.m0 + kop_row(ka, tid)) * g.lda_s;
+            srow_b = (const uint8_t*)g.b_scale.p[tl.e] + (int64_t)kop_row(kb, tid) * g.ldb_s;
         }
     } else {
         kext = DT == DT_MX ? tl.pad_e : tl.rows_e;
@@ -349,101 +575,103 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int ntn,
             ka.row_first = tl.m0;
             ka.rows_valid = g.M;
             ka.kbytes = tl.pad_e;
-            ka.pair_I = 0;
             kb.base = (const uint8_t*)g.b.p[0] + tl.pbase * g.N;
             kb.stride = tl.pad_e;
             kb.row_first = tl.n0;
             kb.rows_valid = g.N;
             kb.kbytes = tl.pad_e;
-            kb.pair_I = 0;
             nblk = tl.pad_e / 32;
             sdw = (tl.pad_e % 128) == 0;
-            if (tid < kGemmBM)
-                sa_row = g.a_scale + tl.pbase / 32 * g.M + kop_row(ka, tid) * (tl.pad_e / 32);
-            else
-                sa_row = (const uint8_t*)g.b_scale.p[0] + tl.pbase / 32 * g.N +
-                         kop_row(kb, tid - kGemmBM) * (tl.pad_e / 32);
+            srow = g.a_scale + tl.pbase / 32 * g.M + (int64_t)kop_row(ka, tid) * (tl.pad_e / 32);
+            srow_b = (const uint8_t*)g.b_scale.p[0] + tl.pbase / 32 * g.N +
+                     (int64_t)kop_row(kb, tid) * (tl.pad_e / 32);
         }
     }
     constexpr int kStepElems = DT == DT_BF16 ? 64 : 128;
-    const int nk = (int)((kext + kStepElems - 1) / kStepElems);
+    const int nk = (kext + kStepElems - 1) / kStepElems;
 
-    f32x16 acc[4][2];
+    f32x16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    u32x4 ra[4], rb[4];
-    uint32_t rs = 0;
-    auto gload = [&](int kt) {
-        if (LA == L_KMAJ) load_kop(ka, (int64_t)kt * kRowB, ra);
+    u32x4 ra[LA == L_MNMAJ ? 8 : 1], rb[LB == L_MNMAJ ? 8 : 1];
+    uint32_t rsa = 0, rsb = 0;
+    // issue the loads of K step kt into stage st (DMA lands directly in LDS;
+    // register-staged parts are written by sstore)
+    auto gload = [&](int kt, int st) {
+        uint8_t* base = smem + st * kStageB;
+        if (LA == L_KMAJ) dma_kop(ka, kt * kRowB, base);
         else load_mnop(ma, kt * 64, ra);
-        if (LB == L_KMAJ) load_kop(kb, (int64_t)kt * kRowB, rb);
+        if (LB == L_KMAJ) dma_kop(kb, kt * kRowB, base + kTileB);
         else load_mnop(mb, kt * 64, rb);
-        if (DT == DT_MX) rs = load_scales(sa_row, kt, nblk, sdw);
+        if (DT == DT_MX) {
+            rsa = load_scales(srow, kt, nblk, sdw);
+            rsb = load_scales(srow_b, kt, nblk, sdw);
+        }
     };
     auto sstore = [&](int st) {
         uint8_t* base = smem + st * kStageB;
-        if (LA == L_KMAJ) store_kop(base, ra);
-        else store_mnop(base, ra);
-        if (LB == L_KMAJ) store_kop(base + kTileB, rb);
-        else store_mnop(base + kTileB, rb);
-        if (DT == DT_MX) ssc[st][tid >> 8][tid & 255] = rs;
+        if (LA == L_MNMAJ) store_mnop(base, ra);
+        if (LB == L_MNMAJ) store_mnop(base + kTileB, rb);
+        if (DT == DT_MX) {
+            ssc[st][0][tid] = rsa;
+            ssc[st][1][tid] = rsb;
+        }
     };
 
     if (nk > 0) {
-        gload(0);
+        gload(0, 0);
         sstore(0);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): LDS-DMA data has landed
     __syncthreads();
 
     const int fr = lane & 31, hi = lane >> 5;
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
+        if (kt + 1 < nk) gload(kt + 1, cur ^ 1);
         const uint8_t* A = smem + cur * kStageB;
         const uint8_t* B = A + kTileB;
         if (DT == DT_BF16) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                bf16x8_t af[4], bfr[2];
+                bf16x8_t bfr[4];
 #pragma unroll
-                for (int fi = 0; fi < 4; ++fi)
-                    af[fi] = *(const bf16x8_t*)(A + lds_off(wm * 128 + fi * 32 + fr, s * 2 + hi));
-#pragma unroll
-                for (int fj = 0; fj < 2; ++fj)
-                    bfr[fj] = *(const bf16x8_t*)(B + lds_off(wn * 64 + fj * 32 + fr, s * 2 + hi));
-#pragma unroll
-                for (int fi = 0; fi < 4; ++fi)
-#pragma unroll
-                    for (int fj = 0; fj < 2; ++fj)
-                        acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fi], bfr[fj],
-                                                                              acc[fi][fj], 0, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                // Operand layout of the scaled 32x32x64 MFMA: lane (row r, half h)
-                // holds K [16h, 16h+16) and [32+16h, 32+16h+16) of the 64-K step;
-                // the E8M0 scale of K-block 0 of row r is taken from lane r, that
-                // of block 1 from lane r+32; opsel picks the byte of the register.
-                i32x8 af[4], bfr[2];
-                uint32_t sa[4], sb[2];
-#pragma unroll
-                for (int fi = 0; fi < 4; ++fi) {
-                    int row = wm * 128 + fi * 32 + fr;
-                    u32x4 lo = *(const u32x4*)(A + lds_off(row, s * 4 + hi));
-                    u32x4 up = *(const u32x4*)(A + lds_off(row, s * 4 + 2 + hi));
-                    af[fi] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                     (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
-                    sa[fi] = ssc[cur][0][row] >> (8 * hi);
+                for (int fj = 0; fj < 4; ++fj) {
+                    if (LB == L_KMAJ)
+                        bfr[fj] = *(const bf16x8_t*)(B + lds_off(wn * 128 + fj * 32 + fr, s * 2 + hi));
+                    else
+                        bfr[fj] = mn_frag(B, s, wn * 128 + fj * 32);
                 }
 #pragma unroll
-                for (int fj = 0; fj < 2; ++fj) {
-                    int row = wn * 64 + fj * 32 + fr;
+                for (int fi = 0; fi < 4; ++fi) {
+                    bf16x8_t af;
+                    if (LA == L_KMAJ)
+                        af = *(const bf16x8_t*)(A + lds_off(wm * 128 + fi * 32 + fr, s * 2 + hi));
+                    else
+                        af = mn_frag(A, s, wm * 128 + fi * 32);
+#pragma unroll
+                    for (int fj = 0; fj < 4; ++fj)
+                        acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[fj],
+                                                                              acc[fi][fj], 0, 0, 0);
+                }
+            }
+        } else {
+            // Operand layout of the scaled 32x32x64 MFMA: lane (row r, half h)
+            // holds K [16h, 16h+16) and [32+16h, 32+16h+16) of the 64-K step;
+            // the E8M0 scale of K-block 0 of row r is taken from lane r, that
+            // of block 1 from lane r+32; opsel picks the byte of the register.
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                i32x8 bfr[4];
+                uint32_t sb[4];
+#pragma unroll
+                for (int fj = 0; fj < 4; ++fj) {
+                    int row = wn * 128 + fj * 32 + fr;
                     u32x4 lo = *(const u32x4*)(B + lds_off(row, s * 4 + hi));
                     u32x4 up = *(const u32x4*)(B + lds_off(row, s * 4 + 2 + hi));
                     bfr[fj] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
@@ -451,17 +679,25 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int ntn,
                     sb[fj] = ssc[cur][1][row] >> (8 * hi);
                 }
 #pragma unroll
-                for (int fi = 0; fi < 4; ++fi)
+                for (int fi = 0; fi < 4; ++fi) {
+                    int row = wm * 128 + fi * 32 + fr;
+                    u32x4 lo = *(const u32x4*)(A + lds_off(row, s * 4 + hi));
+                    u32x4 up = *(const u32x4*)(A + lds_off(row, s * 4 + 2 + hi));
+                    i32x8 af = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                       (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+                    uint32_t sa = ssc[cur][0][row] >> (8 * hi);
 #pragma unroll
-                    for (int fj = 0; fj < 2; ++fj)
+                    for (int fj = 0; fj < 4; ++fj)
                         acc[fi][fj] = s == 0
                             ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                  af[fi], bfr[fj], acc[fi][fj], 0, 0, 0, (int)sa[fi], 0, (int)sb[fj])
+                                  af, bfr[fj], acc[fi][fj], 0, 0, 0, (int)sa, 0, (int)sb[fj])
                             : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                  af[fi], bfr[fj], acc[fi][fj], 0, 0, 2, (int)sa[fi], 2, (int)sb[fj]);
+                                  af, bfr[fj], acc[fi][fj], 0, 0, 2, (int)sa, 2, (int)sb[fj]);
+                }
             }
         }
         if (kt + 1 < nk) sstore(cur ^ 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
     }
 
@@ -480,8 +716,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int ntn,
 #pragma unroll
         for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
-            for (int fj = 0; fj < 2; ++fj) {
-                int col = wn * 64 + fj * 32 + fr;
+            for (int fj = 0; fj < 4; ++fj) {
+                int col = wn * 128 + fj * 32 + fr;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     int row = wm * 128 + fi * 32 + 4 * hi + 8 * (v >> 2) + (v & 3);
@@ -493,100 +729,27 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g, int ntn,
     }
 
     if (EPI == EPI_SWIGLU_FWD) {
-        // fragment fj = 0 holds gate columns, fj = 1 the up columns of the same j
-        const int I = g.I;
-        const int j = tl.n_tile * (kGemmBN / 2) + wn * 32 + fr;
-        QOut q{g.q_row, I, g.q_row_s, g.q_col, g.q_col_s, I};
-#pragma unroll
-        for (int fi = 0; fi < 4; ++fi) {
-            const int frow0 = tl.m0 + wm * 128 + fi * 32;   // row inside the expert
-            const int64_t grow0 = tl.row0 + frow0;
-            float a2v[16];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                int lr = 4 * hi + 8 * (v >> 2) + (v & 3);
-                float gt = acc[fi][0][v], up = acc[fi][1][v];
-                bool ok = frow0 + lr < tl.rows_e;
-                float p = ok ? g.prob[grow0 + lr] : 0.f;
-                a2v[v] = p * silu_f(gt) * up;
-                if (ok) {
-                    bf16_t* a1r = g.a1 + (grow0 + lr) * (2 * (int64_t)I);
-                    a1r[j] = (bf16_t)f32_to_bf16(gt);
-                    a1r[I + j] = (bf16_t)f32_to_bf16(up);
-                    if (DT == DT_BF16) g.act[(grow0 + lr) * (int64_t)I + j] = (bf16_t)f32_to_bf16(a2v[v]);
-                }
-            }
-            if (DT == DT_MX) quant_fragment(a2v, grow0, frow0, tl.rows_e, tl.pad_e, j, tl.pbase, q);
-        }
+        EpiCtx c{g, tl, wm, wn, ntn};
+        float* R = (float*)smem + wave * (32 * 128);
+        swiglu_fwd_rows<DT>(c, R, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0);
+        swiglu_fwd_rows<DT>(c, R, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1);
+        swiglu_fwd_rows<DT>(c, R, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2);
+        swiglu_fwd_rows<DT>(c, R, acc[3][0], acc[3][1], acc[3][2], acc[3][3], 3);
         return;
     }
 
     if (EPI == EPI_SWIGLU_BWD) {
-        const int I = g.I;
-        float* red = (float*)smem;                     // [4 waves along N][256 rows]
-        float rowpart[4][16];
-        QOut q{g.q_row, 2 * (int64_t)I, g.q_row_s, g.q_col, g.q_col_s, 2 * (int64_t)I};
-#pragma unroll
-        for (int fi = 0; fi < 4; ++fi)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) rowpart[fi][v] = 0.f;
-#pragma unroll
-        for (int fj = 0; fj < 2; ++fj) {
-            const int j = tl.n0 + wn * 64 + fj * 32 + fr;
-            const bool jok = j < I;
-#pragma unroll
-            for (int fi = 0; fi < 4; ++fi) {
-                const int frow0 = tl.m0 + wm * 128 + fi * 32;
-                const int64_t grow0 = tl.row0 + frow0;
-                float dgv[16], duv[16];
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    int lr = 4 * hi + 8 * (v >> 2) + (v & 3);
-                    bool ok = jok && (frow0 + lr < tl.rows_e);
-                    float d = acc[fi][fj][v];
-                    float gt = 0.f, up = 0.f, p = 0.f;
-                    if (ok) {
-                        const bf16_t* a1r = g.a1 + (grow0 + lr) * (2 * (int64_t)I);
-                        gt = bf16_to_f32(a1r[j]);
-                        up = bf16_to_f32(a1r[I + j]);
-                        p = g.prob[grow0 + lr];
-                    }
-                    float sg = sigmoid_f(gt);
-                    float sl = gt * sg;
-                    float dp = d * p;
-                    dgv[v] = dp * up * sg * (1.f + gt * (1.f - sg));
-                    duv[v] = dp * sl;
-                    rowpart[fi][v] += ok ? d * sl * up : 0.f;
-                    if (DT == DT_BF16 && ok) {
-                        bf16_t* o = g.act + (grow0 + lr) * (2 * (int64_t)I);
-                        o[j] = (bf16_t)f32_to_bf16(dgv[v]);
-                        o[I + j] = (bf16_t)f32_to_bf16(duv[v]);
-                    }
-                }
-                if (DT == DT_MX && tl.n0 + wn * 64 + fj * 32 < I) {
-                    quant_fragment(dgv, grow0, frow0, tl.rows_e, tl.pad_e, j, tl.pbase, q);
-                    quant_fragment(duv, grow0, frow0, tl.rows_e, tl.pad_e, I + j, tl.pbase, q);
-                }
-            }
-        }
-        // probability gradient: sum over this tile's columns, per row
-#pragma unroll
-        for (int fi = 0; fi < 4; ++fi)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                float sm = half_sum32(rowpart[fi][v]);
-                int row = wm * 128 + fi * 32 + 4 * hi + 8 * (v >> 2) + (v & 3);
-                if (fr == 0) red[wn * kGemmBM + row] = sm;
-            }
-        __syncthreads();
-        if (tid < kGemmBM) {
-            int row = tid;
-            if (tl.m0 + row < tl.rows_e) {
-                float sm = red[row] + red[kGemmBM + row] + red[2 * kGemmBM + row] +
-                           red[3 * kGemmBM + row];
-                g.dprob_part[(tl.row0 + tl.m0 + row) * (int64_t)ntn + tl.n_tile] = sm;
-            }
-        }
+        EpiCtx c{g, tl, wm, wn, ntn};
+        float* R = (float*)smem + wave * (2 * 32 * 128);
+        float* R2 = R + 32 * 128;
+        float* red = (float*)&ssc[0][0][0];                 // [2 waves along N][256 rows]
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0);
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1);
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2);
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[3][0], acc[3][1], acc[3][2], acc[3][3], 3);
+        if (tl.m0 + tid < tl.rows_e)
+            g.dprob_part[(tl.row0 + tl.m0 + tid) * (int64_t)ntn + tl.n_tile] =
+                red[tid] + red[kGemmBM + tid];
         return;
     }
 }

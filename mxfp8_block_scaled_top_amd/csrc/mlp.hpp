@@ -10,7 +10,7 @@ enum GemmLayout { L_KMAJ = 0, L_MNMAJ = 1 };   // operand contiguous along K / a
 enum GemmGroup { G_M = 0, G_K = 1 };           // ragged rows (fwd, dgrad) / ragged K (wgrad)
 enum GemmEpi { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };
 
-constexpr int kGemmBM = 256, kGemmBN = 256, kGemmThreads = 512;
+constexpr int kGemmBM = 256, kGemmBN = 256, kGemmThreads = 256;
 
 // Arguments of one grouped GEMM C_e = A_e B_e^T over all experts e.
 //
