@@ -38,6 +38,8 @@
 //     share a weight tile run on the same XCD and share its L2.
 //   * No float atomics: the probability gradient is written as per-(row,
 //     N-tile) partial sums and reduced in a fixed order by a second kernel.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mlp.hpp"
@@ -53,18 +55,20 @@ typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-constexpr int kRowB = 128;                    // K-contiguous LDS tile row (bytes / K step)
-constexpr int kTileB = kGemmBM * kRowB;       // 32 KiB per operand per stage
+constexpr int kStages = 4;                    // LDS pipeline depth (loads run 3 steps ahead)
+constexpr int kRowB = 64;                     // K-contiguous LDS tile row (bytes per K step)
+constexpr int kTileB = kGemmBM * kRowB;       // 16 KiB per operand per stage
 constexpr int kStageB = 2 * kTileB;           // A + B
-constexpr int kLdsB = 2 * kStageB;            // double-buffered: 128 KiB
+constexpr int kLdsB = kStages * kStageB;      // 128 KiB
 constexpr int kMNRowB = kGemmBM * 2;          // M/N-contiguous LDS row: 256 bf16 = 512 B
 constexpr uint32_t kOob = 0x80000000u;        // buffer offset that reads zeros
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// K-contiguous tile: row r, 16-byte chunk c (4 per row); XOR with (r>>2)&3
+// makes the 16-byte reads of 16 consecutive rows hit 16 distinct bank groups.
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-    return row * kRowB + ((chunk ^ swz(row)) << 4);
+    return row * kRowB + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
-// M/N-contiguous tile: row k (64 rows per stage), 16-byte chunk c (32 per row)
+// M/N-contiguous tile: K row k (32 per stage), 16-byte chunk c (32 per row)
 __device__ __forceinline__ int mn_off(int k, int c) {
     return k * kMNRowB + ((c ^ ((k & 3) << 2)) << 4);
 }
@@ -161,23 +165,66 @@ __device__ __forceinline__ int kop_row(const KOp& op, int r) {
     return gr < op.rows_valid ? gr : op.rows_valid - 1;
 }
 
-// LDS-DMA of one K step of a K-contiguous tile: the wave's 8 instructions
-// cover tile rows (wave*8 + j)*8 .. +7; slot i of instruction j is tile row
-// (wave*8 + j)*8 + i/8 and physical chunk i%8, whose logical chunk is
-// (i%8) ^ swz(row) = (i%8) ^ (i/8) ^ j.
-__device__ __forceinline__ void dma_kop(const KOp& op, int k0b, uint8_t* lds) {
+// LDS-DMA issued through inline assembly.  The compiler does not see these
+// loads, so it inserts no waits for them (it cannot track many in-flight
+// LDS-DMA stores and would otherwise wait for all of them before every LDS
+// read); the pipeline waits for them explicitly with pipe_barrier.  The
+// buffer resource (base, stride 0, 2^31-1 records) makes offsets >= 2^31 read
+// zeros.  buffer_load_dwordx4 ... lds writes lane l's 16 bytes at M0 + 16 l;
+// buffer_load_ubyte ... lds writes lane l's byte, zero-extended, at M0 + 4 l.
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+__device__ __forceinline__ i32x4 make_rsrc(const void* p) {
+    uint64_t a = (uint64_t)p;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    r[2] = 0x7fffffff;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// LDS byte address of a shared-memory pointer (the low 32 bits of the
+// generic address; the LDS aperture is 4 GiB aligned), as a uniform value.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+__device__ __forceinline__ void dma16(const i32x4& rs, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 ::"s"(lds), "v"(voff), "s"(rs) : "memory");
+}
+
+__device__ __forceinline__ void dma1(const i32x4& rs, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ubyte %1, %2, 0 offen lds"
+                 ::"s"(lds), "v"(voff), "s"(rs) : "memory");
+}
+
+// Pipeline barrier: wait until at most N vector-memory loads (LDS-DMA batches
+// of later K steps) are outstanding and all LDS accesses are done, then
+// synchronize the workgroup.  __syncthreads() would also fence global memory,
+// which waits for every outstanding load and so drains the look-ahead.
+template <int N>
+__device__ __forceinline__ void pipe_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// LDS-DMA of one K step of a K-contiguous tile: the wave's 4 instructions
+// cover tile rows (wave*4 + j)*16 .. +15; slot i of instruction j is tile row
+// (wave*4 + j)*16 + i/4 and physical chunk i%4, whose logical chunk is
+// (i%4) ^ ((row>>2)&3) = (i%4) ^ ((i>>4)&3).
+__device__ __forceinline__ void dma_kop(const KOp& op, const i32x4& rs, int k0b, uint8_t* lds) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)op.base, 0, 0x7fffffff, 0x00020000);
+    const int kc16 = (((lane & 3) ^ ((lane >> 4) & 3)) << 4) + k0b;
+    const uint32_t l0 = lds_u32(lds + wave * 4 * 1024);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        int r = (wave * 8 + j) * 8 + (lane >> 3);
-        int kc16 = (((lane & 7) ^ (lane >> 3) ^ j) & 7) * 16 + k0b;
+    for (int j = 0; j < 4; ++j) {
+        int r = (wave * 4 + j) * 16 + (lane >> 2);
         uint32_t o = kc16 < op.kbytes
                          ? (uint32_t)((int64_t)kop_row(op, r) * op.stride) + (uint32_t)kc16
                          : kOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + (wave * 8 + j) * 1024),
-                                                 16, o, 0, 0, 0);
+        dma16(rs, o, l0 + j * 1024);
     }
 }
 
@@ -189,26 +236,21 @@ struct MNOp {
     int mn_valid;
 };
 
-// 64 K-rows x 256 columns: 2048 16-byte chunks, 8 per thread (chunk id =
-// tid + 256 i: row id >> 5, column chunk id & 31).
-__device__ __forceinline__ void load_mnop(const MNOp& op, int k0, u32x4* r) {
-    const int tid = threadIdx.x;
+// LDS-DMA of one K step (32 K rows x 256 columns) of an M/N-contiguous tile
+// into its natural order: instruction j of the wave covers K rows
+// (wave*4 + j)*2 .. +1; slot i is K row (wave*4+j)*2 + i/32, physical chunk
+// i%32, logical chunk (i%32) ^ ((k&3)<<2).  Rows past k_valid and columns
+// past mn_valid read zeros.
+__device__ __forceinline__ void dma_mnop(const MNOp& op, const i32x4& rs, int k0, uint8_t* lds) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t l0 = lds_u32(lds + wave * 4 * 1024);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        int id = tid + i * 256;
-        int k = k0 + (id >> 5), c = id & 31;
-        r[i] = (u32x4){0u, 0u, 0u, 0u};
-        if (k < op.k_valid && c * 8 < op.mn_valid)
-            r[i] = *(const u32x4*)(op.base + (int64_t)k * op.stride + c * 16);
-    }
-}
-
-__device__ __forceinline__ void store_mnop(uint8_t* lds, const u32x4* r) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        int id = tid + i * 256;
-        *(u32x4*)(lds + mn_off(id >> 5, id & 31)) = r[i];
+    for (int j = 0; j < 4; ++j) {
+        int k = (wave * 4 + j) * 2 + (lane >> 5);
+        int c = (lane & 31) ^ ((k & 3) << 2);
+        bool ok = k0 + k < op.k_valid && c * 8 < op.mn_valid;
+        uint32_t o = ok ? (uint32_t)((int64_t)(k0 + k) * op.stride) + (uint32_t)(c * 16) : kOob;
+        dma16(rs, o, l0 + j * 1024);
     }
 }
 
@@ -229,20 +271,17 @@ __device__ __forceinline__ bf16x8_t mn_frag(const uint8_t* lds, int s, int colba
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// MXFP8 scales of one K step (4 blocks of 32) for one tile row, as a dword
-// (byte b = block 4*kt + b).  Blocks past nblk read 127 (2^0; their codes
-// are zero anyway).
-__device__ __forceinline__ uint32_t load_scales(const uint8_t* srow, int kt, int nblk,
-                                                bool dword_ok) {
-    int b0 = kt * 4;
-    if (dword_ok && b0 + 4 <= nblk) return *(const uint32_t*)(srow + b0);
-    uint32_t v = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        uint32_t s = b0 + b < nblk ? srow[b0 + b] : 127u;
-        v |= s << (8 * b);
-    }
-    return v;
+// MXFP8 scales of one K step: blocks 2kt and 2kt+1 of the 64 tile rows of
+// this wave, one byte-DMA per block into dst[block][row] (one dword per row).
+// rs covers the scale array; row_off is this lane's row offset in it; blocks
+// at or past nblk read zero (a finite scale; their codes are zero too).
+__device__ __forceinline__ void dma_scales(const i32x4& rs, uint32_t row_off, int kt, int nblk,
+                                           uint32_t* dst_lo, uint32_t* dst_hi) {
+    const int wave = threadIdx.x >> 6;
+    uint32_t o0 = 2 * kt < nblk ? row_off + 2 * kt : kOob;
+    uint32_t o1 = 2 * kt + 1 < nblk ? row_off + 2 * kt + 1 : kOob;
+    dma1(rs, o0, lds_u32(dst_lo + wave * 64));
+    dma1(rs, o1, lds_u32(dst_hi + wave * 64));
 }
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.f + __expf(-x)); }
@@ -507,8 +546,15 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
 template <int DT, int LA, int LB, int GRP, int EPI>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs g, int ntn, int mtm) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsB];
-    __shared__ uint32_t ssc[2][2][kGemmBM];    // MXFP8 scales [stage][A/B][tile row]
+    // One LDS array per pipeline stage: with the K loop unrolled by the stage
+    // count every access names its stage statically, which lets the compiler
+    // see that the DMA into one stage does not alias the reads of another
+    // (otherwise it waits for all DMA before every LDS read).
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[kStageB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[kStageB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds2[kStageB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds3[kStageB];
+    __shared__ uint32_t ssc[kStages][2][2][kGemmBM];   // MXFP8 scales [stage][A/B][block][row]
     __shared__ int sched[256];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -527,10 +573,10 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     KOp ka{}, kb{};
     MNOp ma{}, mb{};
     int kext;                          // K extent in elements
-    const uint8_t* srow = nullptr;     // MXFP8 scale row of this thread's A row / B row
-    const uint8_t* srow_b = nullptr;
+    const uint8_t* sbase_a = nullptr;  // MXFP8 scale arrays and this thread's row offsets
+    const uint8_t* sbase_b = nullptr;
+    uint32_t soff_a = 0, soff_b = 0;
     int nblk = 0;
-    bool sdw = false;
     if (GRP == G_M) {
         kext = g.K;
         ka.base = (const uint8_t*)g.a + (tl.row0 + tl.m0) * g.lda * kElemB;
@@ -554,9 +600,10 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         }
         if (DT == DT_MX) {
             nblk = g.K / 32;
-            sdw = true;
-            srow = g.a_scale + (tl.row0 + tl.m0 + kop_row(ka, tid)) * g.lda_s;
-            srow_b = (const uint8_t*)g.b_scale.p[tl.e] + (int64_t)kop_row(kb, tid) * g.ldb_s;
+            sbase_a = g.a_scale;
+            soff_a = (uint32_t)((tl.row0 + tl.m0 + kop_row(ka, tid)) * g.lda_s);
+            sbase_b = (const uint8_t*)g.b_scale.p[tl.e];
+            soff_b = (uint32_t)((int64_t)kop_row(kb, tid) * g.ldb_s);
         }
     } else {
         kext = DT == DT_MX ? tl.pad_e : tl.rows_e;
@@ -581,13 +628,13 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
             kb.rows_valid = g.N;
             kb.kbytes = tl.pad_e;
             nblk = tl.pad_e / 32;
-            sdw = (tl.pad_e % 128) == 0;
-            srow = g.a_scale + tl.pbase / 32 * g.M + (int64_t)kop_row(ka, tid) * (tl.pad_e / 32);
-            srow_b = (const uint8_t*)g.b_scale.p[0] + tl.pbase / 32 * g.N +
-                     (int64_t)kop_row(kb, tid) * (tl.pad_e / 32);
+            sbase_a = g.a_scale + tl.pbase / 32 * g.M;
+            soff_a = (uint32_t)((int64_t)kop_row(ka, tid) * (tl.pad_e / 32));
+            sbase_b = (const uint8_t*)g.b_scale.p[0] + tl.pbase / 32 * g.N;
+            soff_b = (uint32_t)((int64_t)kop_row(kb, tid) * (tl.pad_e / 32));
         }
     }
-    constexpr int kStepElems = DT == DT_BF16 ? 64 : 128;
+    constexpr int kStepElems = DT == DT_BF16 ? 32 : 64;   // K per stage (64 bytes per row)
     const int nk = (kext + kStepElems - 1) / kStepElems;
 
     f32x16 acc[4][4];
@@ -598,47 +645,43 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    u32x4 ra[LA == L_MNMAJ ? 8 : 1], rb[LB == L_MNMAJ ? 8 : 1];
-    uint32_t rsa = 0, rsb = 0;
-    // issue the loads of K step kt into stage st (DMA lands directly in LDS;
-    // register-staged parts are written by sstore)
-    auto gload = [&](int kt, int st) {
-        uint8_t* base = smem + st * kStageB;
-        if (LA == L_KMAJ) dma_kop(ka, kt * kRowB, base);
-        else load_mnop(ma, kt * 64, ra);
-        if (LB == L_KMAJ) dma_kop(kb, kt * kRowB, base + kTileB);
-        else load_mnop(mb, kt * 64, rb);
-        if (DT == DT_MX) {
-            rsa = load_scales(srow, kt, nblk, sdw);
-            rsb = load_scales(srow_b, kt, nblk, sdw);
-        }
-    };
-    auto sstore = [&](int st) {
-        uint8_t* base = smem + st * kStageB;
-        if (LA == L_MNMAJ) store_mnop(base, ra);
-        if (LB == L_MNMAJ) store_mnop(base + kTileB, rb);
-        if (DT == DT_MX) {
-            ssc[st][0][tid] = rsa;
-            ssc[st][1][tid] = rsb;
-        }
-    };
+    // One batch of loads per K step, always issued in the same order and
+    // number (DMA A: 4, DMA B: 4, MXFP8 scales: 4) so that "wait until at
+    // most two batches are outstanding" is a fixed vmcnt.  Steps past the end
+    // read zeros into stages that are never consumed.
+    constexpr int kBatch = 8 + (DT == DT_MX ? 4 : 0);
+    constexpr int kWait2 = 2 * kBatch;                           // vmcnt(2 batches)
+    const i32x4 rs_a = make_rsrc(LA == L_KMAJ ? (const void*)ka.base : (const void*)ma.base);
+    const i32x4 rs_b = make_rsrc(LB == L_KMAJ ? (const void*)kb.base : (const void*)mb.base);
+    const i32x4 rs_sa = make_rsrc(sbase_a), rs_sb = make_rsrc(sbase_b);
 
-    if (nk > 0) {
-        gload(0, 0);
-        sstore(0);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): LDS-DMA data has landed
-    __syncthreads();
+    auto stage_ptr = [&](auto S) -> uint8_t* {
+        constexpr int st = decltype(S)::value % kStages;
+        return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3;
+    };
+    // issue the loads of K step kt into stage S
+    auto issue = [&](auto S, int kt) {
+        constexpr int st = decltype(S)::value % kStages;
+        uint8_t* base = stage_ptr(S);
+        if (LA == L_KMAJ) dma_kop(ka, rs_a, kt * kRowB, base);
+        else dma_mnop(ma, rs_a, kt * 32, base);
+        if (LB == L_KMAJ) dma_kop(kb, rs_b, kt * kRowB, base + kTileB);
+        else dma_mnop(mb, rs_b, kt * 32, base + kTileB);
+        if (DT == DT_MX) {
+            dma_scales(rs_sa, soff_a, kt, nblk, ssc[st][0][0], ssc[st][0][1]);
+            dma_scales(rs_sb, soff_b, kt, nblk, ssc[st][1][0], ssc[st][1][1]);
+        }
+    };
 
     const int fr = lane & 31, hi = lane >> 5;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1, cur ^ 1);
-        const uint8_t* A = smem + cur * kStageB;
+    // compute one K step from stage S
+    auto compute = [&](auto S) {
+        constexpr int st = decltype(S)::value % kStages;
+        const uint8_t* A = stage_ptr(S);
         const uint8_t* B = A + kTileB;
         if (DT == DT_BF16) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < 2; ++s) {
                 bf16x8_t bfr[4];
 #pragma unroll
                 for (int fj = 0; fj < 4; ++fj) {
@@ -664,42 +707,61 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
             // Operand layout of the scaled 32x32x64 MFMA: lane (row r, half h)
             // holds K [16h, 16h+16) and [32+16h, 32+16h+16) of the 64-K step;
             // the E8M0 scale of K-block 0 of row r is taken from lane r, that
-            // of block 1 from lane r+32; opsel picks the byte of the register.
+            // of block 1 from lane r+32 (byte h of the staged scale pair).
+            i32x8 bfr[4];
+            uint32_t sb[4];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                i32x8 bfr[4];
-                uint32_t sb[4];
+            for (int fj = 0; fj < 4; ++fj) {
+                int row = wn * 128 + fj * 32 + fr;
+                u32x4 lo = *(const u32x4*)(B + lds_off(row, hi));
+                u32x4 up = *(const u32x4*)(B + lds_off(row, 2 + hi));
+                bfr[fj] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                  (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+                sb[fj] = ssc[st][1][hi][row];
+            }
 #pragma unroll
-                for (int fj = 0; fj < 4; ++fj) {
-                    int row = wn * 128 + fj * 32 + fr;
-                    u32x4 lo = *(const u32x4*)(B + lds_off(row, s * 4 + hi));
-                    u32x4 up = *(const u32x4*)(B + lds_off(row, s * 4 + 2 + hi));
-                    bfr[fj] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                      (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
-                    sb[fj] = ssc[cur][1][row] >> (8 * hi);
-                }
+            for (int fi = 0; fi < 4; ++fi) {
+                int row = wm * 128 + fi * 32 + fr;
+                u32x4 lo = *(const u32x4*)(A + lds_off(row, hi));
+                u32x4 up = *(const u32x4*)(A + lds_off(row, 2 + hi));
+                i32x8 af = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                   (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+                uint32_t sa = ssc[st][0][hi][row];
 #pragma unroll
-                for (int fi = 0; fi < 4; ++fi) {
-                    int row = wm * 128 + fi * 32 + fr;
-                    u32x4 lo = *(const u32x4*)(A + lds_off(row, s * 4 + hi));
-                    u32x4 up = *(const u32x4*)(A + lds_off(row, s * 4 + 2 + hi));
-                    i32x8 af = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                       (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
-                    uint32_t sa = ssc[cur][0][row] >> (8 * hi);
-#pragma unroll
-                    for (int fj = 0; fj < 4; ++fj)
-                        acc[fi][fj] = s == 0
-                            ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                  af, bfr[fj], acc[fi][fj], 0, 0, 0, (int)sa, 0, (int)sb[fj])
-                            : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                  af, bfr[fj], acc[fi][fj], 0, 0, 2, (int)sa, 2, (int)sb[fj]);
-                }
+                for (int fj = 0; fj < 4; ++fj)
+                    acc[fi][fj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        af, bfr[fj], acc[fi][fj], 0, 0, 0, (int)sa, 0, (int)sb[fj]);
             }
         }
-        if (kt + 1 < nk) sstore(cur ^ 1);
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    // one K step kt held in stage S: prefetch step kt+3 into stage S+3, compute,
+    // wait for step kt+1's batch, publish its scales
+    auto step = [&](auto S, int kt) {
+        constexpr int st = decltype(S)::value;
+        issue(std::integral_constant<int, (st + 3) % kStages>{}, kt + 3);
+        compute(S);
+        pipe_barrier<kWait2>();                                  // batch kt+1 has landed
+    };
+
+    if (nk > 0) {
+        issue(I0{}, 0);
+        issue(I1{}, 1);
+        issue(I2{}, 2);
     }
+    pipe_barrier<kWait2>();                                      // batch 0 has landed
+    for (int kt = 0; kt < nk; kt += kStages) {
+        step(I0{}, kt);
+        if (kt + 1 < nk) step(I1{}, kt + 1);
+        if (kt + 2 < nk) step(I2{}, kt + 2);
+        if (kt + 3 < nk) step(I3{}, kt + 3);
+    }
+    // the look-ahead batches past the end still write LDS: drain them before
+    // the epilogue reuses it
+    pipe_barrier<0>();
 
     // ---------------------------------------------------------------- epilogues
     if (EPI == EPI_STORE) {
@@ -730,7 +792,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
 
     if (EPI == EPI_SWIGLU_FWD) {
         EpiCtx c{g, tl, wm, wn, ntn};
-        float* R = (float*)smem + wave * (32 * 128);
+        float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         swiglu_fwd_rows<DT>(c, R, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0);
         swiglu_fwd_rows<DT>(c, R, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1);
         swiglu_fwd_rows<DT>(c, R, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2);
@@ -740,9 +802,9 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
 
     if (EPI == EPI_SWIGLU_BWD) {
         EpiCtx c{g, tl, wm, wn, ntn};
-        float* R = (float*)smem + wave * (2 * 32 * 128);
+        float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         float* R2 = R + 32 * 128;
-        float* red = (float*)&ssc[0][0][0];                 // [2 waves along N][256 rows]
+        float* red = (float*)&ssc[0][0][0][0];              // [2 waves along N][256 rows]
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0);
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1);
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2);
