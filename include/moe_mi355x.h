@@ -210,6 +210,9 @@ void mxfp8_colwise_bytes(int64_t rows, int64_t cols, int ngroups, size_t* code_b
  *   a2_col_*    MXFP8 mode: grouped columnwise MXFP8 of the ScaledSwiGLU
  *               output (groups = experts), mxfp8_colwise_bytes(rows, I, E).
  *   xp_col_*    MXFP8 mode: grouped columnwise MXFP8 of xp, (rows, H, E).
+ * The *_col_codes follow the grouped columnwise layout of mxfp8_quantize; the
+ * *_col_scales hold the same bytes block-major per group ([P_g/32][cols]
+ * at offset cols*sum(P_j/32, j<g)), the order the backward GEMMs read.
  * Members that the mode does not use may be NULL.
  */
 typedef struct moe_saved {

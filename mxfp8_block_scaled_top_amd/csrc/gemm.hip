@@ -171,7 +171,7 @@ __device__ __forceinline__ int kop_row(const KOp& op, int r) {
 // read); the pipeline waits for them explicitly with pipe_barrier.  The
 // buffer resource (base, stride 0, 2^31-1 records) makes offsets >= 2^31 read
 // zeros.  buffer_load_dwordx4 ... lds writes lane l's 16 bytes at M0 + 16 l;
-// buffer_load_ubyte ... lds writes lane l's byte, zero-extended, at M0 + 4 l.
+// buffer_load_dword ... lds writes lane l's 4 bytes at M0 + 4 l.
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 __device__ __forceinline__ i32x4 make_rsrc(const void* p) {
@@ -195,8 +195,8 @@ __device__ __forceinline__ void dma16(const i32x4& rs, uint32_t voff, uint32_t l
                  ::"s"(lds), "v"(voff), "s"(rs) : "memory");
 }
 
-__device__ __forceinline__ void dma1(const i32x4& rs, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ubyte %1, %2, 0 offen lds"
+__device__ __forceinline__ void dma4(const i32x4& rs, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                  ::"s"(lds), "v"(voff), "s"(rs) : "memory");
 }
 
@@ -271,17 +271,22 @@ __device__ __forceinline__ bf16x8_t mn_frag(const uint8_t* lds, int s, int colba
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// MXFP8 scales of one K step: blocks 2kt and 2kt+1 of the 64 tile rows of
-// this wave, one byte-DMA per block into dst[block][row] (one dword per row).
-// rs covers the scale array; row_off is this lane's row offset in it; blocks
-// at or past nblk read zero (a finite scale; their codes are zero too).
-__device__ __forceinline__ void dma_scales(const i32x4& rs, uint32_t row_off, int kt, int nblk,
-                                           uint32_t* dst_lo, uint32_t* dst_hi) {
-    const int wave = threadIdx.x >> 6;
-    uint32_t o0 = 2 * kt < nblk ? row_off + 2 * kt : kOob;
-    uint32_t o1 = 2 * kt + 1 < nblk ? row_off + 2 * kt + 1 : kOob;
-    dma1(rs, o0, lds_u32(dst_lo + wave * 64));
-    dma1(rs, o1, lds_u32(dst_hi + wave * 64));
+// MXFP8 scales of one K step.  GEMM operands keep their E8M0 scales
+// block-major ([block][row]), so the scales of one K block for the 256 tile
+// rows are 256 bytes: one dword per lane covers 4 consecutive tile rows.
+// Wave w loads operand w/2, block 2kt + (w&1), into dst[w/2][w&1][256 rows].
+// off_a/off_b: offset of this lane's 4-row group inside a block row, or kOob
+// when the whole group lies past the operand's rows; blocks at or past nblk
+// read zero (a finite scale; their codes are zero too).
+__device__ __forceinline__ void dma_scales(const i32x4& rs_a, const i32x4& rs_b,
+                                           uint32_t off_a, uint32_t off_b, uint32_t ld_a,
+                                           uint32_t ld_b, int kt, int nblk,
+                                           uint8_t (*dst)[2][kGemmBM]) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
+    const int op = wave >> 1, blk = 2 * kt + (wave & 1);
+    const uint32_t off = op ? off_b : off_a, ld = op ? ld_b : ld_a;
+    const uint32_t o = (blk < nblk && off != kOob) ? (uint32_t)blk * ld + off : kOob;
+    dma4(op ? rs_b : rs_a, o, lds_u32(&dst[op][wave & 1][0]));
 }
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.f + __expf(-x)); }
@@ -428,7 +433,7 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
                 u32x4* o = (u32x4*)(g.q_row + gr * I + j0);
                 o[0] = c0;
                 o[1] = c1;
-                g.q_row_s[gr * (I / 32) + j0 / 32] = (uint8_t)S;
+                g.q_row_s[(j0 / 32) * g.rows + gr] = (uint8_t)S;
             }
         } else {
 #pragma unroll
@@ -443,7 +448,7 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
         const int q = lane >> 5, jj = lane & 31;
         const int64_t j = tl.n_tile * (kGemmBN / 2) + (2 * c.wn + q) * 32 + jj;
         col_quant(R, 64 * q + jj, valid, g.q_col + tl.pbase * I + j * tl.pad_e + frow0,
-                  g.q_col_s + tl.pbase / 32 * I + j * (tl.pad_e / 32) + frow0 / 32);
+                  g.q_col_s + tl.pbase / 32 * I + (frow0 / 32) * I + j);
     }
     __syncthreads();
 }
@@ -506,12 +511,12 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
                 u32x4* o = (u32x4*)(g.q_row + gr * 2 * I + jw + cb);
                 o[0] = c0;
                 o[1] = c1;
-                g.q_row_s[gr * (2 * I / 32) + (jw + cb) / 32] = (uint8_t)S;
+                g.q_row_s[((jw + cb) / 32) * g.rows + gr] = (uint8_t)S;
                 S = quant32(du, c0, c1);
                 o = (u32x4*)(g.q_row + gr * 2 * I + I + jw + cb);
                 o[0] = c0;
                 o[1] = c1;
-                g.q_row_s[gr * (2 * I / 32) + (I + jw + cb) / 32] = (uint8_t)S;
+                g.q_row_s[((I + jw + cb) / 32) * g.rows + gr] = (uint8_t)S;
             }
         } else {
 #pragma unroll
@@ -536,7 +541,7 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
             const int64_t j = (col < 128 ? 0 : I) + jw + cc;
             col_quant(col < 128 ? R : R2, cc, valid,
                       g.q_col + tl.pbase * 2 * I + j * tl.pad_e + frow0,
-                      g.q_col_s + tl.pbase / 32 * 2 * I + j * (tl.pad_e / 32) + frow0 / 32);
+                      g.q_col_s + tl.pbase / 32 * 2 * I + (frow0 / 32) * 2 * I + j);
         }
     }
     __syncthreads();
@@ -554,7 +559,8 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     __shared__ __attribute__((aligned(16))) uint8_t lds1[kStageB];
     __shared__ __attribute__((aligned(16))) uint8_t lds2[kStageB];
     __shared__ __attribute__((aligned(16))) uint8_t lds3[kStageB];
-    __shared__ uint32_t ssc[kStages][2][2][kGemmBM];   // MXFP8 scales [stage][A/B][block][row]
+    __shared__ __attribute__((aligned(16))) uint8_t ssc[kStages][2][2][kGemmBM];   // MXFP8 scales
+    __shared__ float red[2 * kGemmBM];                  // probability-gradient row partials
     __shared__ int sched[256];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -573,9 +579,10 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     KOp ka{}, kb{};
     MNOp ma{}, mb{};
     int kext;                          // K extent in elements
-    const uint8_t* sbase_a = nullptr;  // MXFP8 scale arrays and this thread's row offsets
-    const uint8_t* sbase_b = nullptr;
-    uint32_t soff_a = 0, soff_b = 0;
+    const uint8_t* sbase_a = nullptr;  // MXFP8 scale arrays (block-major), the offsets of
+    const uint8_t* sbase_b = nullptr;  // this lane's 4-row group and the block-row lengths
+    uint32_t soff_a = 0, soff_b = 0, sld_a = 0, sld_b = 0;
+    const int r4 = (lane & 63) * 4;    // first of the 4 tile rows whose scales this lane loads
     int nblk = 0;
     if (GRP == G_M) {
         kext = g.K;
@@ -601,9 +608,12 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         if (DT == DT_MX) {
             nblk = g.K / 32;
             sbase_a = g.a_scale;
-            soff_a = (uint32_t)((tl.row0 + tl.m0 + kop_row(ka, tid)) * g.lda_s);
+            soff_a = r4 < ka.rows_valid ? (uint32_t)(tl.row0 + tl.m0 + r4) : kOob;
+            sld_a = (uint32_t)g.rows;
             sbase_b = (const uint8_t*)g.b_scale.p[tl.e];
-            soff_b = (uint32_t)((int64_t)kop_row(kb, tid) * g.ldb_s);
+            soff_b = (kb.pair_I > 0 || kb.row_first + r4 < kb.rows_valid)
+                         ? (uint32_t)kop_row(kb, r4) : kOob;
+            sld_b = (uint32_t)kb.rows_valid;
         }
     } else {
         kext = DT == DT_MX ? tl.pad_e : tl.rows_e;
@@ -629,9 +639,11 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
             kb.kbytes = tl.pad_e;
             nblk = tl.pad_e / 32;
             sbase_a = g.a_scale + tl.pbase / 32 * g.M;
-            soff_a = (uint32_t)((int64_t)kop_row(ka, tid) * (tl.pad_e / 32));
+            soff_a = tl.m0 + r4 < g.M ? (uint32_t)(tl.m0 + r4) : kOob;
+            sld_a = (uint32_t)g.M;
             sbase_b = (const uint8_t*)g.b_scale.p[0] + tl.pbase / 32 * g.N;
-            soff_b = (uint32_t)((int64_t)kop_row(kb, tid) * (tl.pad_e / 32));
+            soff_b = tl.n0 + r4 < g.N ? (uint32_t)(tl.n0 + r4) : kOob;
+            sld_b = (uint32_t)g.N;
         }
     }
     constexpr int kStepElems = DT == DT_BF16 ? 32 : 64;   // K per stage (64 bytes per row)
@@ -646,10 +658,10 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     // One batch of loads per K step, always issued in the same order and
-    // number (DMA A: 4, DMA B: 4, MXFP8 scales: 4) so that "wait until at
+    // number (DMA A: 4, DMA B: 4, MXFP8 scales: 1) so that "wait until at
     // most two batches are outstanding" is a fixed vmcnt.  Steps past the end
     // read zeros into stages that are never consumed.
-    constexpr int kBatch = 8 + (DT == DT_MX ? 4 : 0);
+    constexpr int kBatch = 8 + (DT == DT_MX ? 1 : 0);
     constexpr int kWait2 = 2 * kBatch;                           // vmcnt(2 batches)
     const i32x4 rs_a = make_rsrc(LA == L_KMAJ ? (const void*)ka.base : (const void*)ma.base);
     const i32x4 rs_b = make_rsrc(LB == L_KMAJ ? (const void*)kb.base : (const void*)mb.base);
@@ -667,10 +679,8 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         else dma_mnop(ma, rs_a, kt * 32, base);
         if (LB == L_KMAJ) dma_kop(kb, rs_b, kt * kRowB, base + kTileB);
         else dma_mnop(mb, rs_b, kt * 32, base + kTileB);
-        if (DT == DT_MX) {
-            dma_scales(rs_sa, soff_a, kt, nblk, ssc[st][0][0], ssc[st][0][1]);
-            dma_scales(rs_sb, soff_b, kt, nblk, ssc[st][1][0], ssc[st][1][1]);
-        }
+        if (DT == DT_MX)
+            dma_scales(rs_sa, rs_sb, soff_a, soff_b, sld_a, sld_b, kt, nblk, ssc[st]);
     };
 
     const int fr = lane & 31, hi = lane >> 5;
@@ -717,7 +727,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
                 u32x4 up = *(const u32x4*)(B + lds_off(row, 2 + hi));
                 bfr[fj] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                   (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
-                sb[fj] = ssc[st][1][hi][row];
+                sb[fj] = ssc[st][1][hi][row];           // byte -> low 8 bits
             }
 #pragma unroll
             for (int fi = 0; fi < 4; ++fi) {
@@ -804,7 +814,6 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         EpiCtx c{g, tl, wm, wn, ntn};
         float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         float* R2 = R + 32 * 128;
-        float* red = (float*)&ssc[0][0][0][0];              // [2 waves along N][256 rows]
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0);
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1);
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2);

@@ -34,12 +34,16 @@ hipError_t launch_unpermute(const bf16_t* yp, int T, int H, int k, const int32_t
 
 // ---- MXFP8
 int64_t colwise_block_bound(int64_t rows, int ngroups);
+// scales_t: store the E8M0 scales block-major ([K/32][rows] for rowwise,
+// [P_g/32][cols] per group for grouped columnwise), the layout the grouped
+// GEMM reads with one coalesced load per K step; false = the public layout.
 hipError_t launch_quant_rows(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, int64_t rows, int64_t cols, hipStream_t s,
-                             const char* name = "mx_quant_rows");
+                             const char* name = "mx_quant_rows", bool scales_t = false);
 hipError_t launch_quant_cols(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, const int32_t* sizes, int ngroups, int64_t rows,
-                             int64_t cols, hipStream_t s, const char* name = "mx_quant_cols");
+                             int64_t cols, hipStream_t s, const char* name = "mx_quant_cols",
+                             bool scales_t = false);
 hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                int64_t cols, bf16_t* out, hipStream_t s);
 hipError_t launch_dequant_cols(const uint8_t* codes, const uint8_t* scales, const int32_t* sizes,

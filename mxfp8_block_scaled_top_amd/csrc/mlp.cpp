@@ -201,10 +201,10 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     src.p[0] = xp;
     cd.p[0] = w.xq;
     sc.p[0] = w.xq_s;
-    MOE_TRY(launch_quant_rows(src, cd, sc, 1, rows, H, stream, "mx_quant_rows_xp"));
+    MOE_TRY(launch_quant_rows(src, cd, sc, 1, rows, H, stream, "mx_quant_rows_xp", true));
     cd.p[0] = saved->xp_col_codes;
     sc.p[0] = saved->xp_col_scales;
-    MOE_TRY(launch_quant_cols(src, cd, sc, 1, split_sizes, E, rows, H, stream, "mx_quant_cols_xp"));
+    MOE_TRY(launch_quant_cols(src, cd, sc, 1, split_sizes, E, rows, H, stream, "mx_quant_cols_xp", true));
     MatTable w1t{}, w1c{}, w1s{}, w2t{}, w2c{}, w2s{};
     for (int e = 0; e < E; ++e) {
         w1t.p[e] = w_gate_up[e];
@@ -214,8 +214,8 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
         w2c.p[e] = w.w2q + (size_t)e * H * I;
         w2s.p[e] = w.w2q_s + (size_t)e * H * I / 32;
     }
-    MOE_TRY(launch_quant_rows(w1t, w1c, w1s, E, 2 * (int64_t)I, H, stream, "mx_quant_rows_w1"));
-    MOE_TRY(launch_quant_rows(w2t, w2c, w2s, E, H, I, stream, "mx_quant_rows_w2"));
+    MOE_TRY(launch_quant_rows(w1t, w1c, w1s, E, 2 * (int64_t)I, H, stream, "mx_quant_rows_w1", true));
+    MOE_TRY(launch_quant_rows(w2t, w2c, w2s, E, H, I, stream, "mx_quant_rows_w2", true));
 
     g.a = w.xq;
     g.lda = H;
@@ -374,11 +374,11 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         src.p[0] = dyp;
         cd.p[0] = w.dyq;
         sc.p[0] = w.dyq_s;
-        MOE_TRY(launch_quant_rows(src, cd, sc, 1, rows, H, stream, "mx_quant_rows_dyp"));
+        MOE_TRY(launch_quant_rows(src, cd, sc, 1, rows, H, stream, "mx_quant_rows_dyp", true));
         cd.p[0] = w.dyc;
         sc.p[0] = w.dyc_s;
         MOE_TRY(launch_quant_cols(src, cd, sc, 1, split_sizes, E, rows, H, stream,
-                                  "mx_quant_cols_dyp"));
+                                  "mx_quant_cols_dyp", true));
     }
     MatTable w1t{}, w1c{}, w1s{}, w2t{}, w2c{}, w2s{};
     for (int e = 0; e < E; ++e) {
@@ -391,9 +391,9 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     }
     if (rows > 0) {
         // W2 [H, I] along H -> [I, H];  W1 [2I, H] along 2I -> [H, 2I]
-        MOE_TRY(launch_quant_cols(w2t, w2c, w2s, E, nullptr, 1, H, I, stream, "mx_quant_cols_w2"));
+        MOE_TRY(launch_quant_cols(w2t, w2c, w2s, E, nullptr, 1, H, I, stream, "mx_quant_cols_w2", true));
         MOE_TRY(launch_quant_cols(w1t, w1c, w1s, E, nullptr, 1, 2 * (int64_t)I, H, stream,
-                                  "mx_quant_cols_w1"));
+                                  "mx_quant_cols_w1", true));
         GemmArgs g{};
         g.split = split_sizes;
         g.E = E;

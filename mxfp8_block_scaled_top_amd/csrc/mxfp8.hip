@@ -23,7 +23,7 @@ namespace moe {
 // ---------------------------------------------------------------- rowwise
 __global__ __launch_bounds__(256) void quant_rows_kernel(MatTable src, MatTable codes,
                                                          MatTable scales, int nmat, int64_t rows,
-                                                         int64_t cols) {
+                                                         int64_t cols, int scales_t) {
     const int64_t bpr = cols / kMxBlock;
     const int64_t per_mat = rows * bpr;
     const int64_t total = per_mat * nmat;
@@ -56,7 +56,12 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(MatTable src, MatTable 
         u32x4* out = (u32x4*)codes.p[m] + b * 2;
         out[0] = o[0];
         out[1] = o[1];
-        ((uint8_t*)scales.p[m])[b] = (uint8_t)S;
+        int64_t si = b;
+        if (scales_t) {                               // block-major: [cols/32][rows]
+            int64_t r = b / bpr, kb = b - r * bpr;
+            si = kb * rows + r;
+        }
+        ((uint8_t*)scales.p[m])[si] = (uint8_t)S;
     }
 }
 
@@ -130,7 +135,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(MatTable src, MatTable 
                                                          MatTable scales,
                                                          const int32_t* __restrict__ sizes,
                                                          int ngroups, int64_t rows,
-                                                         int64_t cols) {
+                                                         int64_t cols, int scales_t) {
     __shared__ int lds[192];
     const int m = blockIdx.z;
     ColBlock cb = locate_col_block(sizes, ngroups, rows, blockIdx.y, lds);
@@ -145,8 +150,10 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(MatTable src, MatTable 
         if (i < cb.valid) v[i] = *(const u32x2*)(in + (cb.r0 + i) * cols + c0);
     }
     uint8_t* cout = (uint8_t*)codes.p[m] + cb.pbase * cols + cb.i0;
-    uint8_t* sout = (uint8_t*)scales.p[m] + cb.pbase / kMxBlock * cols + cb.i0 / kMxBlock;
-    const int64_t sstride = cb.pad_rows / kMxBlock;
+    // scale of (column c, block i0/32): [c][P/32] (public) or [P/32][c] (block-major)
+    uint8_t* sout = (uint8_t*)scales.p[m] + cb.pbase / kMxBlock * cols +
+                    (scales_t ? cb.i0 / kMxBlock * cols : cb.i0 / kMxBlock);
+    const int64_t sstride = scales_t ? 1 : cb.pad_rows / kMxBlock;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         float amax = 0.f;
@@ -227,22 +234,24 @@ int64_t colwise_block_bound(int64_t rows, int ngroups) {
 
 hipError_t launch_quant_rows(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, int64_t rows, int64_t cols, hipStream_t s,
-                             const char* name) {
+                             const char* name, bool scales_t) {
     int64_t n = (int64_t)nmat * rows * (cols / kMxBlock);
     if (n == 0) return hipSuccess;
     TraceScope ts(name, s);
-    quant_rows_kernel<<<grid_1d(n, 256), 256, 0, s>>>(src, codes, scales, nmat, rows, cols);
+    quant_rows_kernel<<<grid_1d(n, 256), 256, 0, s>>>(src, codes, scales, nmat, rows, cols,
+                                                      scales_t ? 1 : 0);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_cols(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, const int32_t* sizes, int ngroups, int64_t rows,
-                             int64_t cols, hipStream_t s, const char* name) {
+                             int64_t cols, hipStream_t s, const char* name, bool scales_t) {
     if (rows == 0 || cols == 0 || nmat == 0) return hipSuccess;
     dim3 grid((unsigned)((cols + 1023) / 1024), (unsigned)colwise_block_bound(rows, ngroups),
               (unsigned)nmat);
     TraceScope ts(name, s);
-    quant_cols_kernel<<<grid, 256, 0, s>>>(src, codes, scales, sizes, ngroups, rows, cols);
+    quant_cols_kernel<<<grid, 256, 0, s>>>(src, codes, scales, sizes, ngroups, rows, cols,
+                                           scales_t ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -39,6 +39,17 @@ def _inputs(T, H, I, E, seed, wstd=0.05, dead=()):
             "dy": bf(rng.standard_normal((T, H)))}
 
 
+def _block_major_to_public(scales, sizes, C):
+    """The saved columnwise scales are stored block-major per group
+    ([P_g/32][C]); return them in the public [C][P_g/32] order."""
+    out, base = [], 0
+    for m in sizes:
+        nb = (int(m) + 31) // 32
+        out.append(scales[base: base + nb * C].reshape(nb, C).T.reshape(-1))
+        base += nb * C
+    return np.concatenate(out) if out else scales[:0]
+
+
 def _layer_compare(inp, k, precision, tag):
     say(f"layer {tag} prec={PREC[precision]} T={inp['x'].shape[0]} H={inp['x'].shape[1]} "
         f"I={inp['w2'][0].shape[1]} E={len(inp['w1'])} k={k}")
@@ -70,7 +81,8 @@ def _layer_compare(inp, k, precision, tag):
         H = inp["x"].shape[1]
         xc, xs = omx.quantize_cols_grouped(ref["xp"], r["split_sizes"])
         assert np.array_equal(np_(got["saved"]["xp_col_codes"])[: xc.size], xc)
-        assert np.array_equal(np_(got["saved"]["xp_col_scales"])[: xs.size], xs)
+        got_s = np_(got["saved"]["xp_col_scales"])
+        assert np.array_equal(_block_major_to_public(got_s, r["split_sizes"], H)[: xs.size], xs)
     return got, ref
 
 
