@@ -241,8 +241,10 @@ typedef struct moe_saved {
  *
  * precision    MOE_BF16 or MOE_MXFP8.
  * E            experts, 1..64.   H, I: hidden and intermediate sizes,
- *              multiples of 128 (bf16) / 128 (mxfp8).
- * rows         T*k, 0 <= rows <= INT32_MAX.
+ *              multiples of 128.
+ * rows         T*k, 0 <= rows <= INT32_MAX, with rows * max(H, 2I) * 2 and
+ *              2I * H * 2 below 2^31 (the kernels address each operand with
+ *              31-bit byte offsets); otherwise MOE_ERR_SHAPE.
  * xp           bf16 [rows, H], expert-grouped (moe_permute).
  * split_sizes  int32 [E] device, sum = rows.
  * w_gate_up    HOST array of E device pointers, each bf16 [2I, H] (rows

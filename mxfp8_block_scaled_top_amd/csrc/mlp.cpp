@@ -116,6 +116,12 @@ int check_common(int precision, int E, int H, int I, int64_t rows) {
     if (E < 1 || E > kMaxExperts) return MOE_ERR_SHAPE;
     if (H < 128 || I < 128 || (H % 128) || (I % 128)) return MOE_ERR_SHAPE;
     if (rows < 0 || rows > INT32_MAX) return MOE_ERR_SHAPE;
+    // the GEMM kernels address every operand with 32-bit byte offsets below
+    // 2^31 from its base: bf16 activations [rows, max(H, 2I)] and one expert's
+    // bf16 weight [2I, H]
+    const int64_t kMaxSpan = (int64_t)1 << 31;
+    const int64_t widest = H > 2 * (int64_t)I ? H : 2 * (int64_t)I;
+    if (rows * widest * 2 >= kMaxSpan || 2 * (int64_t)I * H * 2 >= kMaxSpan) return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 
