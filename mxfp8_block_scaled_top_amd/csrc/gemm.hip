@@ -12,33 +12,32 @@
 //     every wave owns a 128 x 128 sub-tile = 4 x 4 MFMA 32x32 fragments whose
 //     256 fp32 accumulators live in the accumulation registers (one wave per
 //     SIMD, 512 registers per lane).
-//   * K steps of 128 bytes per operand row: 64 bf16 (4 x
-//     v_mfma_f32_32x32x16_bf16) or 128 E4M3 (2 x
+//   * K steps of 64 bytes per operand row: 32 bf16 (2 x
+//     v_mfma_f32_32x32x16_bf16) or 64 E4M3 (one
 //     v_mfma_scale_f32_32x32x64_f8f6f4, the E8M0 scale of every 32 K-values
 //     and row fed straight to the instruction, so nothing is dequantized).
-//     A 128-byte step reads whole cache lines: half-line (64-byte) rows cost
-//     the load path twice the requests per byte.
-//   * LDS holds two stages of both operand tiles (2 x 64 KiB); the loads of
-//     step k+1 run while step k feeds the MFMAs, one barrier per step.
-//     Operands go from memory to LDS without passing through registers
-//     (buffer_load_dwordx4 ... lds: lane l's 16 bytes land at the wave's LDS
-//     base + 16 l, so the lane picks the global chunk that fills its slot).
-//     K-contiguous tiles are stored one 128-byte row per tile row with the
-//     16-byte chunks XOR-swizzled (conflict-free fragment reads).
+//   * LDS holds four stages of both operand tiles (4 x 32 KiB); the loads of
+//     steps k+1..k+3 are in flight while step k feeds the MFMAs, one barrier
+//     per step.  Operands go from memory to LDS without passing through
+//     registers (buffer_load_dwordx4 ... lds: lane l's 16 bytes land at the
+//     wave's LDS base + 16 l, so the lane picks the global chunk that fills
+//     its slot); 16-byte chunks of a 64-byte tile row are XOR-swizzled by
+//     (row >> 2) & 3 so fragment reads of 16 consecutive rows hit distinct
+//     banks.  Offsets past a row's valid K read zeros.
 //   * M/N-contiguous bf16 operands (the dgrad weights and both weight-gradient
-//     operands) are staged in their natural [k][m] order (16-byte chunks of a
-//     512-byte row XOR-ed with 4*(k&3)) and turned into K-packed MFMA
-//     fragments by ds_read_b64_tr_b16, which transposes 4 K-rows x 16 columns
-//     across each 16-lane group, so no transposed copy is ever written.
+//     operands) are staged in LDS in their natural [k][m] order (16-byte
+//     chunks of a 512-byte row XOR-ed with 4*(k&3)) and turned into K-packed
+//     MFMA fragments by ds_read_b64_tr_b16, which transposes 4 K-rows x 16
+//     columns across each 16-lane group, so no transposed copy is written.
 //   * MXFP8 operands carry block-major scales ([K/32][rows]); one dword per
 //     lane of one wave moves the 256 scale bytes of a block.
 //   * Grouping: the tile list is the concatenation over experts of their
 //     tiles (ragged M: ceil(M_e / 256) x N-tiles each; ragged K: a fixed
 //     M x N grid each, looping over the expert's rows).  The per-expert prefix
 //     sums are rebuilt on the device from split_sizes by the first wave of
-//     every workgroup.  Workgroup ids are remapped so that each of the 8 XCDs
-//     (round-robin dispatch) gets a contiguous run of tiles, ordered in bands
-//     of 8 row-tiles, so tiles that share operand tiles share an L2.
+//     every workgroup.  Tiles are spread over the 8 XCDs (round-robin
+//     dispatch) so that all XCDs work on the same expert at the same time,
+//     each on its own N-tiles, in bands of row-tiles that share an L2.
 //   * No float atomics: the probability gradient is written as per-(row,
 //     N-tile) partial sums and reduced in a fixed order by a second kernel.
 #include <type_traits>
@@ -58,24 +57,20 @@ typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-constexpr int kStages = 2;                    // LDS double buffer (loads run one K step ahead)
-constexpr int kRowB = 128;                    // K-contiguous LDS tile row: one 128-byte line per step
-constexpr int kTileB = kGemmBM * kRowB;       // 32 KiB per operand per stage
+constexpr int kStages = 4;                    // LDS pipeline depth (loads run 3 steps ahead)
+constexpr int kRowB = 64;                     // K-contiguous LDS tile row (bytes per K step)
+constexpr int kTileB = kGemmBM * kRowB;       // 16 KiB per operand per stage
 constexpr int kStageB = 2 * kTileB;           // A + B
 constexpr int kLdsB = kStages * kStageB;      // 128 KiB
 constexpr int kMNRowB = kGemmBM * 2;          // M/N-contiguous LDS row: 256 bf16 = 512 B
-constexpr int kMNRows = kStageB / 2 / kMNRowB;   // K rows of an M/N-contiguous stage (64)
-constexpr int kSscB = kStages * 2 * 4 * kGemmBM;  // MXFP8 scale staging (4 KiB)
 constexpr uint32_t kOob = 0x80000000u;        // buffer offset that reads zeros
 
-// K-contiguous tile: row r, 16-byte chunk c (8 per row), XOR-ed with
-// (r ^ r>>3) & 7, so that the 16-byte reads of 8 (and of 16) consecutive rows
-// land in distinct bank groups.
-__device__ __forceinline__ int kswz(int row) { return (row ^ (row >> 3)) & 7; }
+// K-contiguous tile: row r, 16-byte chunk c (4 per row); XOR with (r>>2)&3
+// makes the 16-byte reads of 16 consecutive rows hit 16 distinct bank groups.
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-    return row * kRowB + ((chunk ^ kswz(row)) << 4);
+    return row * kRowB + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
-// M/N-contiguous tile: K row k (64 per stage), 16-byte chunk c (32 per row)
+// M/N-contiguous tile: K row k (32 per stage), 16-byte chunk c (32 per row)
 __device__ __forceinline__ int mn_off(int k, int c) {
     return k * kMNRowB + ((c ^ ((k & 3) << 2)) << 4);
 }
@@ -122,7 +117,33 @@ __device__ bool decode_tile(const GemmArgs& g, int ntn, int mtm, int t, int* sch
     __syncthreads();
     int e;
     int tloc;
-    if (GRP == G_M) {
+    if ((ntn & 7) == 0) {
+        // Expert-synchronous split over the 8 XCDs: XCD x takes the N-tiles
+        // n = 8n' + x of every expert, experts in order, so that all XCDs
+        // stream the same expert at the same time: the activation rows they
+        // all read are fetched from HBM once and served to the other XCDs by
+        // the last-level cache, and every weight byte comes from HBM once.
+        // Inside the XCD's share: bands of row-tiles (grouped_order).
+        const int x = blockIdx.x & 7, i = blockIdx.x >> 3, nt8 = ntn >> 3;
+        int mt;
+        if (GRP == G_M) {
+            e = 0;
+            while (e < g.E && (sched[e] >> 3) <= i) ++e;
+            if (e >= g.E) return false;
+            tloc = i - (e ? (sched[e - 1] >> 3) : 0);
+            mt = (sched[128 + e] + kGemmBM - 1) / kGemmBM;
+        } else {
+            const int per = mtm * nt8;
+            e = i / per;
+            if (e >= g.E) return false;
+            tloc = i - e * per;
+            mt = mtm;
+        }
+        int m, n8;
+        grouped_order(tloc, mt, nt8, m, n8);
+        tl.n_tile = n8 * 8 + x;
+        tl.m0 = m * kGemmBM;
+    } else if (GRP == G_M) {
         e = 0;
         while (e < g.E && sched[e] <= t) ++e;
         if (e >= g.E) return false;
@@ -201,67 +222,41 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
-// voff: per-lane offset; soff: uniform offset added to it (the K advance).
-__device__ __forceinline__ void dma16(const i32x4& rs, uint32_t voff, uint32_t soff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 ::"s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory");
+__device__ __forceinline__ void dma16(const i32x4& rs, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 ::"s"(lds), "v"(voff), "s"(rs) : "memory");
 }
 
-__device__ __forceinline__ void dma4(const i32x4& rs, uint32_t voff, uint32_t soff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 ::"s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory");
+__device__ __forceinline__ void dma4(const i32x4& rs, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 ::"s"(lds), "v"(voff), "s"(rs) : "memory");
 }
 
-// Pipeline barrier: wait until at most N vector-memory loads are outstanding
-// and all LDS accesses are done, then synchronize the workgroup.
-// __syncthreads() would also fence global memory, which waits for every
-// outstanding load, including the look-ahead.
+// Pipeline barrier: wait until at most N vector-memory loads (LDS-DMA batches
+// of later K steps) are outstanding and all LDS accesses are done, then
+// synchronize the workgroup.  __syncthreads() would also fence global memory,
+// which waits for every outstanding load and so drains the look-ahead.
 template <int N>
 __device__ __forceinline__ void pipe_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// LDS-DMA of one K step of a K-contiguous tile (256 rows x 128 bytes): the
-// wave's 8 instructions cover tile rows (wave*8 + j)*8 .. +7, one full
-// 128-byte line per row.  Slot i of instruction j is tile row
-// r = (wave*8 + j)*8 + i/8 and physical chunk i%8, which holds logical chunk
-// (i%8) ^ kswz(r) = (i%8) ^ (i/8) ^ j.
-// The per-lane offsets (row offset + chunk) are computed once per tile; a
-// step adds its K offset as the uniform soffset.
-struct KDma {
-    uint32_t o[8];
-};
-
-__device__ __forceinline__ int kdma_chunk(int j) {
-    const int lane = threadIdx.x & 63;
-    return ((lane & 7) ^ (lane >> 3) ^ j) << 4;
-}
-
-__device__ __forceinline__ KDma kdma_offsets(const KOp& op) {
+// LDS-DMA of one K step of a K-contiguous tile: the wave's 4 instructions
+// cover tile rows (wave*4 + j)*16 .. +15; slot i of instruction j is tile row
+// (wave*4 + j)*16 + i/4 and physical chunk i%4, whose logical chunk is
+// (i%4) ^ ((row>>2)&3) = (i%4) ^ ((i>>4)&3).
+__device__ __forceinline__ void dma_kop(const KOp& op, const i32x4& rs, int k0b, uint8_t* lds) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    KDma d;
+    const int kc16 = (((lane & 3) ^ ((lane >> 4) & 3)) << 4) + k0b;
+    const uint32_t l0 = lds_u32(lds + wave * 4 * 1024);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = (wave * 8 + j) * 8 + (lane >> 3);
-        d.o[j] = (uint32_t)((int64_t)kop_row(op, r) * op.stride) + (uint32_t)kdma_chunk(j);
-    }
-    return d;
-}
-
-// Steps that lie wholly inside K need no per-lane test; the last step of a
-// ragged K extent sends the chunks at or past kbytes to the zero range.
-__device__ __forceinline__ void dma_kop(const KDma& d, const i32x4& rs, int k0b, int kbytes,
-                                        uint8_t* lds, int wv) {
-    const uint32_t l0 = lds_u32(lds) + wv * 8 * 1024;
-    const uint32_t soff = __builtin_amdgcn_readfirstlane(k0b);
-    if (k0b + kRowB <= kbytes) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dma16(rs, d.o[j], soff, l0 + j * 1024);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            dma16(rs, kdma_chunk(j) + k0b < kbytes ? d.o[j] : kOob, soff, l0 + j * 1024);
+    for (int j = 0; j < 4; ++j) {
+        int r = (wave * 4 + j) * 16 + (lane >> 2);
+        uint32_t o = kc16 < op.kbytes
+                         ? (uint32_t)((int64_t)kop_row(op, r) * op.stride) + (uint32_t)kc16
+                         : kOob;
+        dma16(rs, o, l0 + j * 1024);
     }
 }
 
@@ -273,115 +268,57 @@ struct MNOp {
     int mn_valid;
 };
 
-// LDS-DMA of one K step (64 K rows x 256 columns) of an M/N-contiguous tile
+// LDS-DMA of one K step (32 K rows x 256 columns) of an M/N-contiguous tile
 // into its natural order: instruction j of the wave covers K rows
-// (wave*8 + j)*2 .. +1; slot i is K row (wave*8+j)*2 + i/32, physical chunk
-// i%32, logical chunk (i%32) ^ ((k&3)<<2).  Columns past mn_valid read zeros
-// (folded into the per-tile offsets), rows past k_valid too (last step only).
-__device__ __forceinline__ int mndma_k(int j) {
-    return ((threadIdx.x >> 6) * 8 + j) * 2 + ((threadIdx.x & 63) >> 5);
-}
-
-__device__ __forceinline__ KDma mndma_offsets(const MNOp& op) {
-    const int lane = threadIdx.x & 63;
-    KDma d;
+// (wave*4 + j)*2 .. +1; slot i is K row (wave*4+j)*2 + i/32, physical chunk
+// i%32, logical chunk (i%32) ^ ((k&3)<<2).  Rows past k_valid and columns
+// past mn_valid read zeros.
+__device__ __forceinline__ void dma_mnop(const MNOp& op, const i32x4& rs, int k0, uint8_t* lds) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t l0 = lds_u32(lds + wave * 4 * 1024);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int k = mndma_k(j);
-        const int c = (lane & 31) ^ ((k & 3) << 2);
-        d.o[j] = c * 8 < op.mn_valid ? (uint32_t)((int64_t)k * op.stride) + (uint32_t)(c * 16)
-                                     : kOob;
-    }
-    return d;
-}
-
-__device__ __forceinline__ void dma_mnop(const KDma& d, const MNOp& op, const i32x4& rs, int k0,
-                                         uint8_t* lds, int wv) {
-    const uint32_t l0 = lds_u32(lds) + wv * 8 * 1024;
-    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)k0 * op.stride));
-    if (k0 + kMNRows <= op.k_valid) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dma16(rs, d.o[j], soff, l0 + j * 1024);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            dma16(rs, k0 + mndma_k(j) < op.k_valid ? d.o[j] : kOob, soff, l0 + j * 1024);
+    for (int j = 0; j < 4; ++j) {
+        int k = (wave * 4 + j) * 2 + (lane >> 5);
+        int c = (lane & 31) ^ ((k & 3) << 2);
+        bool ok = k0 + k < op.k_valid && c * 8 < op.mn_valid;
+        uint32_t o = ok ? (uint32_t)((int64_t)(k0 + k) * op.stride) + (uint32_t)(c * 16) : kOob;
+        dma16(rs, o, l0 + j * 1024);
     }
 }
 
-// LDS loads from 32-bit LDS byte addresses.
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
-typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
-__device__ __forceinline__ u32x4 lds_ld16(uint32_t a) { return *(const lds_u32x4_t*)(size_t)a; }
-__device__ __forceinline__ uint32_t lds_ld8(uint32_t a) { return *(const lds_u8_t*)(size_t)a; }
-
-// A uniform value the compiler cannot fold into the addresses built on it.
-__device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
-    asm volatile("" : "+s"(x));
-    return x;
-}
-
-// M/N-contiguous tile, K-packed bf16 fragment of columns colbase..+31 via two
-// transposing reads: in each 16-lane group g, lane q supplies (K row kb + q/4,
-// columns n..n+3) and receives column n0 + q for 4 consecutive K rows.
-// mn_lane: the lane's byte offset for K sub-step 0 (kb = 8(g>>1) + q/4); sub-step
-// s adds 16 K rows (8192 bytes, the XOR term depends on kb & 3 only), the
-// second read 4 K rows (2048 bytes).
-__device__ __forceinline__ uint32_t mn_lane(int colbase) {
+// K-packed bf16 fragment (8 K-values, K sub-step s, columns colbase..+31) of
+// an M/N-contiguous LDS tile, via two transposing reads: in each 16-lane
+// group g, lane q supplies (K row kb + q/4, columns n..n+3) and receives
+// column n0 + q for 4 consecutive K rows.
+__device__ __forceinline__ bf16x8_t mn_frag(const uint8_t* lds, int s, int colbase) {
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, q = lane & 15;
-    const int kb = 8 * (g >> 1) + (q >> 2);
+    const int kb = 16 * s + 8 * (g >> 1) + (q >> 2);
     const int n = colbase + 16 * (g & 1) + 4 * (q & 3);       // element column
-    return (uint32_t)(mn_off(kb, n >> 3) + (n & 7) * 2);
-}
-
-__device__ __forceinline__ bf16x8_t mn_frag(uint32_t base, int s) {
-    const uint32_t a = base + s * 16 * kMNRowB;
-    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(size_t)a);
-    i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(size_t)(a + 4 * kMNRowB));
+    const int c = n >> 3, sub = (n & 7) * 2;                   // 16-byte chunk, byte in chunk
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds + mn_off(kb, c) + sub));
+    i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)(lds + mn_off(kb + 4, c) + sub));
     i16x8 v = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// Per-lane LDS byte offsets of the K-contiguous fragments of a wave's 128
-// tile rows wx*128 + f*32 + (lane & 31): with w = kswz of the lane's row
-// (without the f term) ^ (lane >> 5), b[q] = row offset + ((2q ^ w) << 4), and
-// fragment f reads at f*4096 + b[q'] for a q' fixed at compile time:
-//   bf16 sub-step s (chunk 2s + hi):            q' = s ^ 2(f&1)
-//   MXFP8 sub-step s (chunks 4s + hi, 4s+2+hi): q' = 2(s ^ (f&1)) + {0, 1}
-struct KFrag {
-    uint32_t b[4];
-};
-
-__device__ __forceinline__ KFrag kfrag_bases(int wx) {
-    const int lane = threadIdx.x & 63, fr = lane & 31, hi = lane >> 5;
-    const int w = (fr & 7) ^ (fr >> 3) ^ hi;
-    KFrag k;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) k.b[q] = wx * 16384 + fr * kRowB + (((2 * q) ^ w) << 4);
-    return k;
-}
-
-// MXFP8 scales of one K step (4 blocks of 32).  GEMM operands keep their
-// E8M0 scales block-major ([block][row]), so the scales of one K block for
-// the 256 tile rows are 256 bytes: one dword per lane covers 4 consecutive
-// tile rows.  Wave w loads operand w/2, blocks 4kt + 2(w&1) + {0, 1}, into
-// dst[w/2][block % 4][256 rows].  off: offset of this lane's 4-row group
-// inside a block row of the wave's operand, or kOob when the whole group lies
-// past the operand's rows; blocks at or past nblk read zero (a finite scale;
-// their codes are zero too).
-__device__ __forceinline__ void dma_scales(const i32x4& rs, uint32_t off, uint32_t ld, int kt,
-                                           int nblk, uint8_t (*dst)[4][kGemmBM], int wv) {
-    const int wave = wv, op = wave >> 1;
-    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(4 * kt) * ld);
-    const bool full = 4 * kt + 4 <= nblk;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int b4 = 2 * (wave & 1) + i;
-        uint32_t o = off == kOob ? kOob : (uint32_t)b4 * ld + off;
-        if (!full && 4 * kt + b4 >= nblk) o = kOob;
-        dma4(rs, o, soff, lds_u32(&dst[op][b4][0]));
-    }
+// MXFP8 scales of one K step.  GEMM operands keep their E8M0 scales
+// block-major ([block][row]), so the scales of one K block for the 256 tile
+// rows are 256 bytes: one dword per lane covers 4 consecutive tile rows.
+// Wave w loads operand w/2, block 2kt + (w&1), into dst[w/2][w&1][256 rows].
+// off_a/off_b: offset of this lane's 4-row group inside a block row, or kOob
+// when the whole group lies past the operand's rows; blocks at or past nblk
+// read zero (a finite scale; their codes are zero too).
+__device__ __forceinline__ void dma_scales(const i32x4& rs_a, const i32x4& rs_b,
+                                           uint32_t off_a, uint32_t off_b, uint32_t ld_a,
+                                           uint32_t ld_b, int kt, int nblk,
+                                           uint8_t (*dst)[2][kGemmBM]) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
+    const int op = wave >> 1, blk = 2 * kt + (wave & 1);
+    const uint32_t off = op ? off_b : off_a, ld = op ? ld_b : ld_a;
+    const uint32_t o = (blk < nblk && off != kOob) ? (uint32_t)blk * ld + off : kOob;
+    dma4(op ? rs_b : rs_a, o, lds_u32(&dst[op][wave & 1][0]));
 }
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.f + __expf(-x)); }
@@ -447,22 +384,6 @@ __device__ __forceinline__ void unpack8_bf16(u32x4 w, float* x) {
         x[2 * i] = lo_bf16(w[i]);
         x[2 * i + 1] = hi_bf16(w[i]);
     }
-}
-
-// Plain epilogue: rows r0 .. r0+31 of the wave's staged slice to bf16 C.
-__device__ __forceinline__ void store_slice(const float* R, bf16_t* C, int64_t ldc, int r0,
-                                            int row, int h, int wn, bool cols_ok, int row_lim) {
-    __syncthreads();
-    if (cols_ok && r0 + row < row_lim) {
-        u32x4* o = (u32x4*)(C + (int64_t)(r0 + row) * ldc + wn * 128 + h * 64);
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            float x[8];
-            load_row8(R, row, h * 64 + 8 * b, x);
-            o[b] = pack8_bf16(x);
-        }
-    }
-    __syncthreads();
 }
 
 // One block of 32 values -> E8M0 scale and 32 E4M3 codes as two 16-byte words.
@@ -662,9 +583,15 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
 template <int DT, int LA, int LB, int GRP, int EPI>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs g, int ntn, int mtm) {
-    // Main-loop LDS, carved by hand: stage s at s*64 KiB (A tile, then B
-    // tile), then the MXFP8 scales [stage][operand][block of 4][256 rows].
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsB + kSscB];
+    // One LDS array per pipeline stage: with the K loop unrolled by the stage
+    // count every access names its stage statically, which lets the compiler
+    // see that the DMA into one stage does not alias the reads of another
+    // (otherwise it waits for all DMA before every LDS read).
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[kStageB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[kStageB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds2[kStageB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds3[kStageB];
+    __shared__ __attribute__((aligned(16))) uint8_t ssc[kStages][2][2][kGemmBM];   // MXFP8 scales
     __shared__ float red[2 * kGemmBM];                  // probability-gradient row partials
     __shared__ int sched[256];
 
@@ -751,7 +678,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
             sld_b = (uint32_t)g.N;
         }
     }
-    constexpr int kStepElems = DT == DT_BF16 ? 64 : 128;  // K per stage (128 bytes per row)
+    constexpr int kStepElems = DT == DT_BF16 ? 32 : 64;   // K per stage (64 bytes per row)
     const int nk = (kext + kStepElems - 1) / kStepElems;
 
     f32x16 acc[4][4];
@@ -762,163 +689,130 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // One batch of loads per K step (DMA A: 8, DMA B: 8, MXFP8 scales: 2 per
-    // wave), issued one step ahead; the step past the end reads zeros into a
-    // stage that is never consumed.
+    // One batch of loads per K step, always issued in the same order and
+    // number (DMA A: 4, DMA B: 4, MXFP8 scales: 1) so that "wait until at
+    // most two batches are outstanding" is a fixed vmcnt.  Steps past the end
+    // read zeros into stages that are never consumed.
+    constexpr int kBatch = 8 + (DT == DT_MX ? 1 : 0);
+    constexpr int kWait2 = 2 * kBatch;                           // vmcnt(2 batches)
     const i32x4 rs_a = make_rsrc(LA == L_KMAJ ? (const void*)ka.base : (const void*)ma.base);
     const i32x4 rs_b = make_rsrc(LB == L_KMAJ ? (const void*)kb.base : (const void*)mb.base);
-    KDma dA, dB;
-    if (LA == L_KMAJ) dA = kdma_offsets(ka);
-    else dA = mndma_offsets(ma);
-    if (LB == L_KMAJ) dB = kdma_offsets(kb);
-    else dB = mndma_offsets(mb);
-    // scales: waves 0-1 load operand A's, waves 2-3 operand B's
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const i32x4 rs_s = make_rsrc(wv < 2 ? sbase_a : sbase_b);
-    const uint32_t s_off = wv < 2 ? soff_a : soff_b;
-    const uint32_t s_ld = wv < 2 ? sld_a : sld_b;
-    const KFrag fa = kfrag_bases(wm), fb = kfrag_bases(wn);
+    const i32x4 rs_sa = make_rsrc(sbase_a), rs_sb = make_rsrc(sbase_b);
 
     auto stage_ptr = [&](auto S) -> uint8_t* {
         constexpr int st = decltype(S)::value % kStages;
-        return smem + st * kStageB;
-    };
-    auto ssc_ptr = [&](auto S) {
-        constexpr int st = decltype(S)::value % kStages;
-        return (uint8_t(*)[4][kGemmBM])(smem + kLdsB + st * 2 * 4 * kGemmBM);
+        return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3;
     };
     // issue the loads of K step kt into stage S
     auto issue = [&](auto S, int kt) {
         constexpr int st = decltype(S)::value % kStages;
-        if (kt >= nk) return;
         uint8_t* base = stage_ptr(S);
-        if (LA == L_KMAJ) dma_kop(dA, rs_a, kt * kRowB, ka.kbytes, base, wv);
-        else dma_mnop(dA, ma, rs_a, kt * kMNRows, base, wv);
-        if (LB == L_KMAJ) dma_kop(dB, rs_b, kt * kRowB, kb.kbytes, base + kTileB, wv);
-        else dma_mnop(dB, mb, rs_b, kt * kMNRows, base + kTileB, wv);
-        if (DT == DT_MX) dma_scales(rs_s, s_off, s_ld, kt, nblk, ssc_ptr(S), wv);
+        if (LA == L_KMAJ) dma_kop(ka, rs_a, kt * kRowB, base);
+        else dma_mnop(ma, rs_a, kt * 32, base);
+        if (LB == L_KMAJ) dma_kop(kb, rs_b, kt * kRowB, base + kTileB);
+        else dma_mnop(mb, rs_b, kt * 32, base + kTileB);
+        if (DT == DT_MX)
+            dma_scales(rs_sa, rs_sb, soff_a, soff_b, sld_a, sld_b, kt, nblk, ssc[st]);
     };
 
     const int fr = lane & 31, hi = lane >> 5;
-    // Per-lane LDS read addresses.  The LDS base goes through an opaque
-    // register so that every read is "lane base + small constant" (ds_read
-    // offsets hold 16 bits): one base per (operand, stage, q) for K-contiguous
-    // tiles, per (operand, stage, fragment) for M/N-contiguous ones, one per
-    // operand for the scales.
-    const uint32_t sm = opaque_u32(lds_u32(smem));
-    uint32_t abase[kStages][4], bbase[kStages][4];
-#pragma unroll
-    for (int st = 0; st < kStages; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            abase[st][i] = sm + st * kStageB +
-                           (LA == L_KMAJ ? fa.b[i] : mn_lane(wm * 128 + i * 32));
-            bbase[st][i] = sm + st * kStageB + kTileB +
-                           (LB == L_KMAJ ? fb.b[i] : mn_lane(wn * 128 + i * 32));
-        }
-    const uint32_t sa_base = sm + kLdsB + 0 * 4 * kGemmBM + hi * kGemmBM + wm * 128 + fr;
-    const uint32_t sb_base = sm + kLdsB + 1 * 4 * kGemmBM + hi * kGemmBM + wn * 128 + fr;
-    constexpr int kSscStage = 2 * 4 * kGemmBM;
-
     // compute one K step from stage S
     auto compute = [&](auto S) {
         constexpr int st = decltype(S)::value % kStages;
+        const uint8_t* A = stage_ptr(S);
+        const uint8_t* B = A + kTileB;
         if (DT == DT_BF16) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < 2; ++s) {
                 bf16x8_t bfr[4];
 #pragma unroll
                 for (int fj = 0; fj < 4; ++fj) {
                     if (LB == L_KMAJ)
-                        bfr[fj] = __builtin_bit_cast(
-                            bf16x8_t, lds_ld16(bbase[st][s ^ (2 * (fj & 1))] + fj * 4096));
+                        bfr[fj] = *(const bf16x8_t*)(B + lds_off(wn * 128 + fj * 32 + fr, s * 2 + hi));
                     else
-                        bfr[fj] = mn_frag(bbase[st][fj], s);
+                        bfr[fj] = mn_frag(B, s, wn * 128 + fj * 32);
                 }
 #pragma unroll
                 for (int fi = 0; fi < 4; ++fi) {
                     bf16x8_t af;
                     if (LA == L_KMAJ)
-                        af = __builtin_bit_cast(
-                            bf16x8_t, lds_ld16(abase[st][s ^ (2 * (fi & 1))] + fi * 4096));
+                        af = *(const bf16x8_t*)(A + lds_off(wm * 128 + fi * 32 + fr, s * 2 + hi));
                     else
-                        af = mn_frag(abase[st][fi], s);
+                        af = mn_frag(A, s, wm * 128 + fi * 32);
 #pragma unroll
                     for (int fj = 0; fj < 4; ++fj)
                         acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[fj],
                                                                               acc[fi][fj], 0, 0, 0);
                 }
-                // keep the next sub-step's fragment reads behind these MFMAs
-                // (hoisting them all would need 4x the fragment registers)
-                __builtin_amdgcn_sched_barrier(0);
             }
         } else {
             // Operand layout of the scaled 32x32x64 MFMA: lane (row r, half h)
-            // holds K [16h, 16h+16) and [32+16h, 32+16h+16) of the 64-K
-            // sub-step; the E8M0 scale of K-block 0 of row r is taken from
-            // lane r, that of block 1 from lane r+32 (staged block 2s + h).
+            // holds K [16h, 16h+16) and [32+16h, 32+16h+16) of the 64-K step;
+            // the E8M0 scale of K-block 0 of row r is taken from lane r, that
+            // of block 1 from lane r+32 (byte h of the staged scale pair).
+            i32x8 bfr[4];
+            uint32_t sb[4];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                i32x8 bfr[4];
-                uint32_t sb[4];
+            for (int fj = 0; fj < 4; ++fj) {
+                int row = wn * 128 + fj * 32 + fr;
+                u32x4 lo = *(const u32x4*)(B + lds_off(row, hi));
+                u32x4 up = *(const u32x4*)(B + lds_off(row, 2 + hi));
+                bfr[fj] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                  (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+                sb[fj] = ssc[st][1][hi][row];           // byte -> low 8 bits
+            }
 #pragma unroll
-                for (int fj = 0; fj < 4; ++fj) {
-                    const int q = 2 * (s ^ (fj & 1));
-                    u32x4 lo = lds_ld16(bbase[st][q] + fj * 4096);
-                    u32x4 up = lds_ld16(bbase[st][q + 1] + fj * 4096);
-                    bfr[fj] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                      (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
-                    sb[fj] = lds_ld8(sb_base + st * kSscStage + 2 * s * kGemmBM + fj * 32);
-                }
+            for (int fi = 0; fi < 4; ++fi) {
+                int row = wm * 128 + fi * 32 + fr;
+                u32x4 lo = *(const u32x4*)(A + lds_off(row, hi));
+                u32x4 up = *(const u32x4*)(A + lds_off(row, 2 + hi));
+                i32x8 af = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                   (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+                uint32_t sa = ssc[st][0][hi][row];
 #pragma unroll
-                for (int fi = 0; fi < 4; ++fi) {
-                    const int q = 2 * (s ^ (fi & 1));
-                    u32x4 lo = lds_ld16(abase[st][q] + fi * 4096);
-                    u32x4 up = lds_ld16(abase[st][q + 1] + fi * 4096);
-                    i32x8 af = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                       (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
-                    uint32_t sa = lds_ld8(sa_base + st * kSscStage + 2 * s * kGemmBM + fi * 32);
-#pragma unroll
-                    for (int fj = 0; fj < 4; ++fj)
-                        acc[fi][fj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            af, bfr[fj], acc[fi][fj], 0, 0, 0, (int)sa, 0, (int)sb[fj]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                for (int fj = 0; fj < 4; ++fj)
+                    acc[fi][fj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        af, bfr[fj], acc[fi][fj], 0, 0, 0, (int)sa, 0, (int)sb[fj]);
             }
         }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    // one K step kt held in stage S: load step kt+1 into the other stage,
-    // compute, then wait for that batch (and for every wave to be done with
-    // stage S before the next step refills it)
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    // one K step kt held in stage S: prefetch step kt+3 into stage S+3, compute,
+    // wait for step kt+1's batch, publish its scales
     auto step = [&](auto S, int kt) {
         constexpr int st = decltype(S)::value;
-        issue(std::integral_constant<int, (st + 1) % kStages>{}, kt + 1);
+        issue(std::integral_constant<int, (st + 3) % kStages>{}, kt + 3);
         compute(S);
-        pipe_barrier<0>();
+        pipe_barrier<kWait2>();                                  // batch kt+1 has landed
     };
 
-    if (nk > 0) issue(I0{}, 0);
-    pipe_barrier<0>();                                           // batch 0 has landed
-    // whole pairs of steps, then the odd last one: a conditional second step
-    // inside the loop body makes the register allocator shuttle the 256
-    // accumulators between register files on every iteration
+    if (nk > 0) {
+        issue(I0{}, 0);
+        issue(I1{}, 1);
+        issue(I2{}, 2);
+    }
+    pipe_barrier<kWait2>();                                      // batch 0 has landed
+    // whole groups of four steps, then the rest: a conditional step inside
+    // the loop body makes the register allocator shuttle accumulators
+    // between register files on every iteration
     int kt = 0;
-    for (; kt + 2 <= nk; kt += 2) {
+    for (; kt + kStages <= nk; kt += kStages) {
         step(I0{}, kt);
         step(I1{}, kt + 1);
+        step(I2{}, kt + 2);
+        step(I3{}, kt + 3);
     }
     if (kt < nk) step(I0{}, kt);
+    if (kt + 1 < nk) step(I1{}, kt + 1);
+    if (kt + 2 < nk) step(I2{}, kt + 2);
     // the look-ahead batches past the end still write LDS: drain them before
     // the epilogue reuses it
     pipe_barrier<0>();
 
     // ---------------------------------------------------------------- epilogues
-    // Every epilogue stages the wave's result through its own 32 KiB of the
-    // (now idle) operand stages: wave w uses bytes [32K w, 32K (w+1)).
-    float* R = (float*)(smem + wave * kTileB);
-
     if (EPI == EPI_STORE) {
         bf16_t* C;
         int64_t ldc = g.ldc;
@@ -930,24 +824,24 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
             C = (bf16_t*)g.c_tab.p[tl.e] + (int64_t)tl.m0 * ldc + tl.n0;
             row_lim = g.M - tl.m0;
         }
-        // 32-row slices: lane (row = lane/2, half h = lane&1) writes 64
-        // consecutive bf16 of one row as 8 x 16 bytes (N is a multiple of
-        // 128, so a wave's 128 columns are all inside or all outside)
-        const int row = lane >> 1, h = lane & 1;
-        const bool cols_ok = wn * 128 < col_lim;
-        stage_fragments(R, acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
-        store_slice(R, C, ldc, wm * 128 + 0 * 32, row, h, wn, cols_ok, row_lim);
-        stage_fragments(R, acc[1][0], acc[1][1], acc[1][2], acc[1][3]);
-        store_slice(R, C, ldc, wm * 128 + 1 * 32, row, h, wn, cols_ok, row_lim);
-        stage_fragments(R, acc[2][0], acc[2][1], acc[2][2], acc[2][3]);
-        store_slice(R, C, ldc, wm * 128 + 2 * 32, row, h, wn, cols_ok, row_lim);
-        stage_fragments(R, acc[3][0], acc[3][1], acc[3][2], acc[3][3]);
-        store_slice(R, C, ldc, wm * 128 + 3 * 32, row, h, wn, cols_ok, row_lim);
+#pragma unroll
+        for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+            for (int fj = 0; fj < 4; ++fj) {
+                int col = wn * 128 + fj * 32 + fr;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    int row = wm * 128 + fi * 32 + 4 * hi + 8 * (v >> 2) + (v & 3);
+                    if (row < row_lim && col < col_lim)
+                        C[(int64_t)row * ldc + col] = (bf16_t)f32_to_bf16(acc[fi][fj][v]);
+                }
+            }
         return;
     }
 
     if (EPI == EPI_SWIGLU_FWD) {
         EpiCtx c{g, tl, wm, wn, ntn};
+        float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         swiglu_fwd_rows<DT>(c, R, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0);
         swiglu_fwd_rows<DT>(c, R, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1);
         swiglu_fwd_rows<DT>(c, R, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2);
@@ -957,6 +851,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
 
     if (EPI == EPI_SWIGLU_BWD) {
         EpiCtx c{g, tl, wm, wn, ntn};
+        float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         float* R2 = R + 32 * 128;
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0);
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1);
