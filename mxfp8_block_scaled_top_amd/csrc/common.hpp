@@ -81,6 +81,20 @@ __device__ __forceinline__ uint32_t mx_encode(float v, uint32_t S) {
     return sign | mag;
 }
 
+// Four E4M3 codes of v0..v3 / 2^(S-127), packed little-endian in a word.
+// The power-of-two unscale is exact; the hardware fp32 -> E4M3 conversion
+// then rounds to nearest even and keeps the sign, which gives the same bytes
+// as mx_encode for every value a block's scale admits (checked exhaustively
+// over all bf16 inputs and scales, rounding ties and subnormal midpoints).
+__device__ __forceinline__ uint32_t mx_encode4(float v0, float v1, float v2, float v3,
+                                               uint32_t S) {
+    const int sh = 127 - (int)S;
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(v0, sh),
+                                                 __builtin_ldexpf(v1, sh), 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(v2, sh), __builtin_ldexpf(v3, sh),
+                                           w, true);
+}
+
 // Value of an E4M3 code times 2^(S-127), exact in fp32.
 __device__ __forceinline__ float mx_decode(uint32_t code, uint32_t S) {
     uint32_t e = (code >> 3) & 15u, m = code & 7u;

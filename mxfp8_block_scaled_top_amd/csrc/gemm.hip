@@ -394,8 +394,7 @@ __device__ __forceinline__ uint32_t quant32(const float* x, u32x4& c0, u32x4& c1
     uint32_t S = mx_scale_byte(m);
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-        uint32_t word = mx_encode(x[4 * w], S) | (mx_encode(x[4 * w + 1], S) << 8) |
-                        (mx_encode(x[4 * w + 2], S) << 16) | (mx_encode(x[4 * w + 3], S) << 24);
+        uint32_t word = mx_encode4(x[4 * w], x[4 * w + 1], x[4 * w + 2], x[4 * w + 3], S);
         if (w < 4) c0[w] = word;
         else c1[w - 4] = word;
     }
@@ -504,61 +503,110 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
     const bool slab = jw < I;                              // I % 128 == 0: all or nothing
     const int row = lane >> 1, h = lane & 1;
     float part = 0.f;
+    if (DT == DT_BF16) {
 #pragma unroll 1
-    for (int blk = 0; blk < 2; ++blk) {
-        const int cb = 64 * h + 32 * blk;                   // staged column of the block
-        float dg[32], du[32];
-        if (slab && row < valid) {
+        for (int blk = 0; blk < 2; ++blk) {
+            const int cb = 64 * h + 32 * blk;               // staged column of the block
+            if (!(slab && row < valid)) continue;
             const int64_t gr = tl.row0 + frow0 + row;
             const float p = g.prob[gr];
             const u32x4* a1g = (const u32x4*)(g.a1 + gr * 2 * I + jw + cb);
             const u32x4* a1u = (const u32x4*)(g.a1 + gr * 2 * I + I + jw + cb);
+            u32x4* og = (u32x4*)(g.act + gr * 2 * I + jw + cb);
+            u32x4* ou = (u32x4*)(g.act + gr * 2 * I + I + jw + cb);
+            // all of the block's loads before its stores (which may alias them
+            // for the compiler): one round trip
+            u32x4 wg[4], wu[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                float d[8], gt[8], up[8];
+                wg[b] = a1g[b];
+                wu[b] = a1u[b];
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                float d[8], gt[8], up[8], dg[8], du[8];
                 load_row8(R, row, cb + 8 * b, d);
-                unpack8_bf16(a1g[b], gt);
-                unpack8_bf16(a1u[b], up);
+                unpack8_bf16(wg[b], gt);
+                unpack8_bf16(wu[b], up);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     float sg = sigmoid_f(gt[i]);
                     float sl = gt[i] * sg;
                     float dp = d[i] * p;
-                    dg[8 * b + i] = dp * up[i] * sg * (1.f + gt[i] * (1.f - sg));
-                    du[8 * b + i] = dp * sl;
+                    dg[i] = dp * up[i] * sg * (1.f + gt[i] * (1.f - sg));
+                    du[i] = dp * sl;
                     part += d[i] * sl * up[i];
                 }
+                og[b] = pack8_bf16(dg);
+                ou[b] = pack8_bf16(du);
             }
-            if (DT == DT_BF16) {
-                u32x4* og = (u32x4*)(g.act + gr * 2 * I + jw + cb);
-                u32x4* ou = (u32x4*)(g.act + gr * 2 * I + I + jw + cb);
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    og[b] = pack8_bf16(dg + 8 * b);
-                    ou[b] = pack8_bf16(du + 8 * b);
-                }
-            } else {
-                u32x4 c0, c1;
-                uint32_t S = quant32(dg, c0, c1);
-                u32x4* o = (u32x4*)(g.q_row + gr * 2 * I + jw + cb);
-                o[0] = c0;
-                o[1] = c1;
-                g.q_row_s[((jw + cb) / 32) * g.rows + gr] = (uint8_t)S;
-                S = quant32(du, c0, c1);
-                o = (u32x4*)(g.q_row + gr * 2 * I + I + jw + cb);
-                o[0] = c0;
-                o[1] = c1;
-                g.q_row_s[((I + jw + cb) / 32) * g.rows + gr] = (uint8_t)S;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) dg[i] = du[i] = 0.f;
         }
-        if (DT == DT_MX) {
+    } else {
+        // phase 1, 8 values at a time: dg replaces the staged dA2 in R, du
+        // goes to R2 (rows past the expert stay zero for the column blocks)
+        const bool live = slab && row < valid;
+        const int64_t gr = tl.row0 + frow0 + row;
+        const float p = live ? g.prob[gr] : 0.f;
+#pragma unroll 1
+        for (int blk = 0; blk < 2; ++blk) {
+            const int cb = 64 * h + 32 * blk;
+            const u32x4* a1g = (const u32x4*)(g.a1 + gr * 2 * I + jw + cb);
+            const u32x4* a1u = (const u32x4*)(g.a1 + gr * 2 * I + I + jw + cb);
+            // the block's saved gate/up values in one round trip
+            u32x4 wg[4], wu[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                store_row8(R, row, cb + 8 * b, dg + 8 * b);
-                store_row8(R2, row, cb + 8 * b, du + 8 * b);
+                wg[b] = live ? a1g[b] : (u32x4){0, 0, 0, 0};
+                wu[b] = live ? a1u[b] : (u32x4){0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                float d[8], dg[8], du[8];
+                load_row8(R, row, cb + 8 * b, d);
+                if (live) {
+                    float gt[8], up[8];
+                    unpack8_bf16(wg[b], gt);
+                    unpack8_bf16(wu[b], up);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        float sg = sigmoid_f(gt[i]);
+                        float sl = gt[i] * sg;
+                        float dp = d[i] * p;
+                        dg[i] = dp * up[i] * sg * (1.f + gt[i] * (1.f - sg));
+                        du[i] = dp * sl;
+                        part += d[i] * sl * up[i];
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) dg[i] = du[i] = 0.f;
+                }
+                store_row8(R, row, cb + 8 * b, dg);
+                store_row8(R2, row, cb + 8 * b, du);
+            }
+        }
+        // phase 2: rowwise MXFP8 of the lane's own 32-column blocks (the same
+        // lane wrote them, so no barrier is needed)
+        if (slab && row < valid) {
+            const int64_t gr = tl.row0 + frow0 + row;
+#pragma unroll 1
+            for (int q = 0; q < 4; ++q) {
+                const int cb = 64 * h + 32 * (q & 1);
+                const float* src = q < 2 ? R : R2;
+                float x[32];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    float y[8];
+                    load_row8(src, row, cb + 8 * b, y);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) x[8 * b + i] = y[i];
+                }
+                u32x4 c0, c1;
+                uint32_t S = quant32(x, c0, c1);
+                const int64_t j = (q < 2 ? 0 : I) + jw + cb;
+                u32x4* o = (u32x4*)(g.q_row + gr * 2 * I + j);
+                o[0] = c0;
+                o[1] = c1;
+                g.q_row_s[(j / 32) * g.rows + gr] = (uint8_t)S;
             }
         }
     }

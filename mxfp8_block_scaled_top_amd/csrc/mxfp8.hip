@@ -46,12 +46,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(MatTable src, MatTable 
         u32x4 o[2];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            uint32_t c0 = mx_encode(lo_bf16(v[q][0]), S), c1 = mx_encode(hi_bf16(v[q][0]), S);
-            uint32_t c2 = mx_encode(lo_bf16(v[q][1]), S), c3 = mx_encode(hi_bf16(v[q][1]), S);
-            uint32_t c4 = mx_encode(lo_bf16(v[q][2]), S), c5 = mx_encode(hi_bf16(v[q][2]), S);
-            uint32_t c6 = mx_encode(lo_bf16(v[q][3]), S), c7 = mx_encode(hi_bf16(v[q][3]), S);
-            o[q >> 1][(q & 1) * 2] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-            o[q >> 1][(q & 1) * 2 + 1] = c4 | (c5 << 8) | (c6 << 16) | (c7 << 24);
+            o[q >> 1][(q & 1) * 2] = mx_encode4(lo_bf16(v[q][0]), hi_bf16(v[q][0]),
+                                                lo_bf16(v[q][1]), hi_bf16(v[q][1]), S);
+            o[q >> 1][(q & 1) * 2 + 1] = mx_encode4(lo_bf16(v[q][2]), hi_bf16(v[q][2]),
+                                                    lo_bf16(v[q][3]), hi_bf16(v[q][3]), S);
         }
         u32x4* out = (u32x4*)codes.p[m] + b * 2;
         out[0] = o[0];
@@ -167,14 +165,13 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(MatTable src, MatTable 
         u32x4 o[2];
 #pragma unroll
         for (int i = 0; i < kMxBlock; i += 4) {
-            uint32_t word = 0;
+            float f[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 uint32_t w = v[i + r][j >> 1];
-                float f = (j & 1) ? hi_bf16(w) : lo_bf16(w);
-                word |= mx_encode(f, S) << (8 * r);
+                f[r] = (j & 1) ? hi_bf16(w) : lo_bf16(w);
             }
-            o[i >> 4][(i >> 2) & 3] = word;
+            o[i >> 4][(i >> 2) & 3] = mx_encode4(f[0], f[1], f[2], f[3], S);
         }
         u32x4* dst = (u32x4*)(cout + (c0 + j) * cb.pad_rows);
         dst[0] = o[0];
