@@ -42,8 +42,8 @@ def parse():
     ap.add_argument("--precision", default="both", choices=["mxfp8", "bf16", "both"])
     ap.add_argument("--workload", default="mixtral", choices=["mixtral", "skewed", "tiny"])
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=512)
-    ap.add_argument("--cpu-inter", type=int, default=128)
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-inter", type=int, default=512)
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -87,6 +87,24 @@ def kernel_work(name: str, T: int, H: int, I: int, E: int, k: int):
         "dprob_reduce": (0, A * ((I + 255) // 256) * 4 + A * 4),
     }
     return table.get(name, (0, 0))
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on copies of known size), or None when
+    there is none or the library sources changed since it was taken."""
+    from mxfp8_block_scaled_top_amd import profsum
+    path = os.path.join(ROOT, "profiles", f"gemm_traffic_{workload}_layer.md")
+    blob = profsum.load_traffic(path)
+    if blob is None or kernel not in blob["kernels"]:
+        return None, None
+    if blob["sources"] != profsum.source_hash():
+        return None, {"note": "counters were taken on other library sources",
+                      "source": os.path.relpath(path, ROOT)}
+    k = blob["kernels"][kernel]
+    return k["traffic_bytes"], {"read_bytes": k["fetch_bytes"], "written_bytes": k["write_bytes"],
+                                "algorithmic_bytes": k["algorithmic_bytes"],
+                                "source": os.path.relpath(path, ROOT)}
 
 
 def run_gpu(args, prec_name, inp_dev, shape):
@@ -140,7 +158,7 @@ def run_gpu(args, prec_name, inp_dev, shape):
         roof = {"bound": "hbm", "achieved": round(by / (dom_mean * 1e-3) / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"], roof["traffic_detail"] = measured_traffic(dom, args.workload)
     roof["kernel"] = dom
     roof["mean_ms"] = round(dom_mean, 4)
     flops = 18.0 * H * I * T * k

@@ -628,7 +628,7 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
 }
 
 // ---------------------------------------------------------------- the kernel
-template <int DT, int LA, int LB, int GRP, int EPI>
+template <int DT, int LA, int LB, int GRP, int EPI, int USE>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     // One LDS array per pipeline stage: with the K loop unrolled by the stage
@@ -928,7 +928,7 @@ int gemm_n_tiles(int epi, int N, int I) {
     return (N + kGemmBN - 1) / kGemmBN;
 }
 
-template <int DT, int LA, int LB, int GRP, int EPI>
+template <int DT, int LA, int LB, int GRP, int EPI, int USE>
 static hipError_t run(const GemmArgs& g, hipStream_t s) {
     const int ntn = gemm_n_tiles(EPI, g.N, g.I);
     int mtm = 0;
@@ -944,26 +944,28 @@ static hipError_t run(const GemmArgs& g, hipStream_t s) {
     if (tiles == 0) return hipSuccess;
     int64_t grid = (tiles + 7) / 8 * 8;
     TraceScope ts(g.name ? g.name : "gemm", s);
-    gemm_kernel<DT, LA, LB, GRP, EPI><<<(unsigned)grid, kGemmThreads, 0, s>>>(g, ntn, mtm);
+    gemm_kernel<DT, LA, LB, GRP, EPI, USE><<<(unsigned)grid, kGemmThreads, 0, s>>>(g, ntn, mtm);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(int dtype, int la, int lb, int grp, int epi, const GemmArgs& g,
-                       hipStream_t s) {
-#define MOE_GEMM_CASE(DT, LA, LB, GRP, EPI)                                        \
-    if (dtype == DT && la == LA && lb == LB && grp == GRP && epi == EPI)           \
-        return run<DT, LA, LB, GRP, EPI>(g, s);
-    // bf16
-    MOE_GEMM_CASE(DT_BF16, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_FWD)
-    MOE_GEMM_CASE(DT_BF16, L_KMAJ, L_KMAJ, G_M, EPI_STORE)
-    MOE_GEMM_CASE(DT_BF16, L_KMAJ, L_MNMAJ, G_M, EPI_SWIGLU_BWD)
-    MOE_GEMM_CASE(DT_BF16, L_KMAJ, L_MNMAJ, G_M, EPI_STORE)
-    MOE_GEMM_CASE(DT_BF16, L_MNMAJ, L_MNMAJ, G_K, EPI_STORE)
-    // mxfp8
-    MOE_GEMM_CASE(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_FWD)
-    MOE_GEMM_CASE(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_STORE)
-    MOE_GEMM_CASE(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_BWD)
-    MOE_GEMM_CASE(DT_MX, L_KMAJ, L_KMAJ, G_K, EPI_STORE)
+hipError_t launch_gemm(int dtype, int use, const GemmArgs& g, hipStream_t s) {
+#define MOE_GEMM_CASE(DT, USE, LA, LB, GRP, EPI) \
+    if (dtype == DT && use == USE) return run<DT, LA, LB, GRP, EPI, USE>(g, s);
+    // bf16: the backward reads W1, W2 and both weight-gradient operands in
+    // their natural (M/N-contiguous) layout
+    MOE_GEMM_CASE(DT_BF16, U_GATEUP_FWD, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_FWD)
+    MOE_GEMM_CASE(DT_BF16, U_DOWN_FWD, L_KMAJ, L_KMAJ, G_M, EPI_STORE)
+    MOE_GEMM_CASE(DT_BF16, U_DOWN_DGRAD, L_KMAJ, L_MNMAJ, G_M, EPI_SWIGLU_BWD)
+    MOE_GEMM_CASE(DT_BF16, U_DOWN_WGRAD, L_MNMAJ, L_MNMAJ, G_K, EPI_STORE)
+    MOE_GEMM_CASE(DT_BF16, U_GATEUP_DGRAD, L_KMAJ, L_MNMAJ, G_M, EPI_STORE)
+    MOE_GEMM_CASE(DT_BF16, U_GATEUP_WGRAD, L_MNMAJ, L_MNMAJ, G_K, EPI_STORE)
+    // mxfp8: every operand is quantized along its GEMM's K, K-contiguous
+    MOE_GEMM_CASE(DT_MX, U_GATEUP_FWD, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_FWD)
+    MOE_GEMM_CASE(DT_MX, U_DOWN_FWD, L_KMAJ, L_KMAJ, G_M, EPI_STORE)
+    MOE_GEMM_CASE(DT_MX, U_DOWN_DGRAD, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_BWD)
+    MOE_GEMM_CASE(DT_MX, U_DOWN_WGRAD, L_KMAJ, L_KMAJ, G_K, EPI_STORE)
+    MOE_GEMM_CASE(DT_MX, U_GATEUP_DGRAD, L_KMAJ, L_KMAJ, G_M, EPI_STORE)
+    MOE_GEMM_CASE(DT_MX, U_GATEUP_WGRAD, L_KMAJ, L_KMAJ, G_K, EPI_STORE)
 #undef MOE_GEMM_CASE
     return hipErrorInvalidValue;
 }

@@ -188,7 +188,7 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
         g.a1 = saved->a1;
         g.act = saved->a2;
         g.name = "gemm_bf16_gateup_fwd_swiglu";
-        MOE_TRY(launch_gemm(DT_BF16, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_FWD, g, stream));
+        MOE_TRY(launch_gemm(DT_BF16, U_GATEUP_FWD, g, stream));
         GemmArgs d = g;
         d.a = saved->a2;
         d.lda = I;
@@ -199,7 +199,7 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
         d.c = yp;
         d.ldc = H;
         d.name = "gemm_bf16_down_fwd";
-        MOE_TRY(launch_gemm(DT_BF16, L_KMAJ, L_KMAJ, G_M, EPI_STORE, d, stream));
+        MOE_TRY(launch_gemm(DT_BF16, U_DOWN_FWD, d, stream));
         return MOE_OK;
     }
     // MXFP8: quantize operands along their contraction axis
@@ -239,7 +239,7 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     g.q_col = saved->a2_col_codes;
     g.q_col_s = saved->a2_col_scales;
     g.name = "gemm_mx_gateup_fwd_swiglu";
-    MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_FWD, g, stream));
+    MOE_TRY(launch_gemm(DT_MX, U_GATEUP_FWD, g, stream));
     GemmArgs d{};
     d.split = split_sizes;
     d.E = E;
@@ -258,7 +258,7 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     d.c = yp;
     d.ldc = H;
     d.name = "gemm_mx_down_fwd";
-    MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_STORE, d, stream));
+    MOE_TRY(launch_gemm(DT_MX, U_DOWN_FWD, d, stream));
     return MOE_OK;
 }
 
@@ -321,7 +321,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
             g.act = (bf16_t*)w.da1;
             g.dprob_part = w.part;
             g.name = "gemm_bf16_down_dgrad_swiglu_bwd";
-            MOE_TRY(launch_gemm(DT_BF16, L_KMAJ, L_MNMAJ, G_M, EPI_SWIGLU_BWD, g, stream));
+            MOE_TRY(launch_gemm(DT_BF16, U_DOWN_DGRAD, g, stream));
             MOE_TRY(launch_dprob_reduce(w.part, rows, ntn, dprob_perm, stream));
         }
         // down wgrad: dW2 [H, I] = dYp^T A2
@@ -338,7 +338,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         wg.c_tab = dw2;
         wg.ldc = I;
         wg.name = "gemm_bf16_down_wgrad";
-        MOE_TRY(launch_gemm(DT_BF16, L_MNMAJ, L_MNMAJ, G_K, EPI_STORE, wg, stream));
+        MOE_TRY(launch_gemm(DT_BF16, U_DOWN_WGRAD, wg, stream));
         if (rows > 0) {
             // gate_up dgrad: dXp = dA1 W1
             GemmArgs dg{};
@@ -354,7 +354,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
             dg.c = dxp;
             dg.ldc = H;
             dg.name = "gemm_bf16_gateup_dgrad";
-            MOE_TRY(launch_gemm(DT_BF16, L_KMAJ, L_MNMAJ, G_M, EPI_STORE, dg, stream));
+            MOE_TRY(launch_gemm(DT_BF16, U_GATEUP_DGRAD, dg, stream));
         }
         // gate_up wgrad: dW1 [2I, H] = dA1^T Xp
         GemmArgs wg1{};
@@ -370,7 +370,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         wg1.c_tab = dw1;
         wg1.ldc = H;
         wg1.name = "gemm_bf16_gateup_wgrad";
-        MOE_TRY(launch_gemm(DT_BF16, L_MNMAJ, L_MNMAJ, G_K, EPI_STORE, wg1, stream));
+        MOE_TRY(launch_gemm(DT_BF16, U_GATEUP_WGRAD, wg1, stream));
         return MOE_OK;
     }
 
@@ -423,7 +423,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         g.q_col_s = w.da1c_s;
         g.dprob_part = w.part;
         g.name = "gemm_mx_down_dgrad_swiglu_bwd";
-        MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_BWD, g, stream));
+        MOE_TRY(launch_gemm(DT_MX, U_DOWN_DGRAD, g, stream));
         MOE_TRY(launch_dprob_reduce(w.part, rows, ntn, dprob_perm, stream));
     }
     // down wgrad: dW2 [H, I] = dYp^T A2 over grouped columnwise operands
@@ -440,7 +440,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     wg.c_tab = dw2;
     wg.ldc = I;
     wg.name = "gemm_mx_down_wgrad";
-    MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_K, EPI_STORE, wg, stream));
+    MOE_TRY(launch_gemm(DT_MX, U_DOWN_WGRAD, wg, stream));
     if (rows > 0) {
         GemmArgs dg{};
         dg.split = split_sizes;
@@ -459,7 +459,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         dg.c = dxp;
         dg.ldc = H;
         dg.name = "gemm_mx_gateup_dgrad";
-        MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_M, EPI_STORE, dg, stream));
+        MOE_TRY(launch_gemm(DT_MX, U_GATEUP_DGRAD, dg, stream));
     }
     GemmArgs wg1{};
     wg1.split = split_sizes;
@@ -474,7 +474,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     wg1.c_tab = dw1;
     wg1.ldc = H;
     wg1.name = "gemm_mx_gateup_wgrad";
-    MOE_TRY(launch_gemm(DT_MX, L_KMAJ, L_KMAJ, G_K, EPI_STORE, wg1, stream));
+    MOE_TRY(launch_gemm(DT_MX, U_GATEUP_WGRAD, wg1, stream));
     return MOE_OK;
 }
 

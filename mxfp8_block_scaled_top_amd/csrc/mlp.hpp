@@ -9,6 +9,16 @@ enum GemmDType { DT_BF16 = 0, DT_MX = 1 };
 enum GemmLayout { L_KMAJ = 0, L_MNMAJ = 1 };   // operand contiguous along K / along M or N
 enum GemmGroup { G_M = 0, G_K = 1 };           // ragged rows (fwd, dgrad) / ragged K (wgrad)
 enum GemmEpi { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };
+// The six grouped GEMMs of the layer; each gets a kernel symbol of its own so
+// that profiles attribute time per GEMM.
+enum GemmUse {
+    U_GATEUP_FWD = 0,    // xp W1^T, ScaledSwiGLU epilogue
+    U_DOWN_FWD = 1,      // A2 W2^T
+    U_DOWN_DGRAD = 2,    // dyp W2, SwiGLU-backward epilogue
+    U_DOWN_WGRAD = 3,    // dyp^T A2 per expert
+    U_GATEUP_DGRAD = 4,  // dA1 W1
+    U_GATEUP_WGRAD = 5,  // dA1^T xp per expert
+};
 
 constexpr int kGemmBM = 256, kGemmBN = 256, kGemmThreads = 256;
 
@@ -50,8 +60,7 @@ struct GemmArgs {
     const char* name;   // kernel name in launch traces
 };
 
-hipError_t launch_gemm(int dtype, int la, int lb, int grp, int epi, const GemmArgs& g,
-                       hipStream_t s);
+hipError_t launch_gemm(int dtype, int use, const GemmArgs& g, hipStream_t s);
 hipError_t launch_dprob_reduce(const float* part, int64_t rows, int ntiles, float* dprob,
                                hipStream_t s);
 int gemm_n_tiles(int epi, int N, int I);
