@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--workload", default="mixtral", choices=["mixtral", "skewed", "tiny"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
-    ap.add_argument("--cpu-inter", type=int, default=512)
+    ap.add_argument("--cpu-inter", type=int, default=768)
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 

@@ -228,3 +228,41 @@ def test_qdq_cols_matches_transposed_rows(shape):
     a = mx.qdq_cols(x).numpy()
     b = mx.dequantize_cols_grouped(*mx.quantize_cols_grouped(x, [shape[0]]), [shape[0]], shape[1])
     assert np.array_equal(a, b.astype(np.float32))
+
+
+# ---------------------------------------------------------------- fast path
+# qdq_rows_fast / qdq_cols_fast must give exactly the reference values: they
+# serve the full-size GPU parity tests, which quantize whole expert weights.
+
+def _bf16_all_finite_blocks(seed):
+    """Every finite bf16 pattern once, shuffled into rows of 32-value blocks."""
+    bits = np.arange(65536, dtype=np.uint32) << 16
+    finite = ((bits >> 23) & 0xFF) != 0xFF
+    vals = bits[finite].view(np.float32)
+    rng = np.random.default_rng(seed)
+    vals = rng.permutation(vals)
+    n = len(vals) // 512 * 512
+    return torch.from_numpy(vals[:n].reshape(-1, 512).copy()).to(torch.bfloat16)
+
+
+def test_fast_rows_equals_reference_all_bf16_patterns():
+    x = _bf16_all_finite_blocks(0)
+    assert torch.equal(mx.qdq_rows_fast(x), mx.qdq_rows(x))
+
+
+def test_fast_rows_equals_reference_scaled_zero_and_tiny_blocks():
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((96, 256)).astype(np.float32)
+    v *= np.exp2(rng.integers(-140, 120, size=(96, 1))).astype(np.float32)   # deep under/over
+    v[5] = 0.0                                   # all-zero blocks
+    v[7, :32] = -0.0
+    v[9, 3] = 65504.0                             # an outlier inside a small block
+    x = torch.from_numpy(v).to(torch.bfloat16)
+    assert torch.equal(mx.qdq_rows_fast(x), mx.qdq_rows(x))
+
+
+def test_fast_cols_equals_reference():
+    rng = np.random.default_rng(4)
+    v = (rng.standard_normal((320, 96)) * np.exp2(rng.integers(-8, 8, size=(1, 96)))).astype(np.float32)
+    x = torch.from_numpy(v).to(torch.bfloat16)
+    assert torch.equal(mx.qdq_cols_fast(x), mx.qdq_cols(x))
