@@ -62,12 +62,17 @@ def _sigmoid(g: torch.Tensor) -> torch.Tensor:
 
 
 class _Mode:
-    def __init__(self, precision: str, exact: bool):
+    def __init__(self, precision: str, exact: bool, fast_quant: bool = False):
         assert precision in ("bf16", "mxfp8")
         assert not (exact and precision != "bf16")
         self.mx = precision == "mxfp8"
         self.exact = exact
         self.acc = torch.float64 if exact else torch.float32
+        # the vectorized quantizers give the reference values bit for bit
+        # (pinned in the oracle tests); they make whole expert weights cheap
+        self.q_rows = _mx.qdq_rows_fast if fast_quant else _mx.qdq_rows
+        self.q_cols = _mx.qdq_cols_fast if fast_quant else _mx.qdq_cols
+        self.q_cols_grouped = _mx.qdq_cols_grouped_fast if fast_quant else _mx.qdq_cols_grouped
 
     def store(self, t: torch.Tensor) -> torch.Tensor:
         """Round a materialized tensor (bf16 storage unless exact)."""
@@ -78,18 +83,19 @@ class _Mode:
 
     # operand preparation for each GEMM (along its contraction axis)
     def rows_op(self, t):           # contraction axis = last dim
-        return _mx.qdq_rows(t).to(self.acc) if self.mx else self.val(t)
+        return self.q_rows(t).to(self.acc) if self.mx else self.val(t)
 
     def cols_op(self, t):           # contraction axis = first dim (weights)
-        return _mx.qdq_cols(t).to(self.acc) if self.mx else self.val(t)
+        return self.q_cols(t).to(self.acc) if self.mx else self.val(t)
 
     def group_cols_op(self, t):     # contraction over the rows of one expert
         if not self.mx:
             return self.val(t)
-        return _mx.qdq_cols_grouped(t, [t.shape[0]]).to(self.acc)
+        return self.q_cols_grouped(t, [t.shape[0]]).to(self.acc)
 
 
-def grouped_mlp_fwd(xp, split, w1, w2, pp, precision="bf16", exact=False) -> dict:
+def grouped_mlp_fwd(xp, split, w1, w2, pp, precision="bf16", exact=False,
+                    fast_quant=False, experts=None) -> dict:
     """Forward of all experts.  xp bf16 [A, H]; split int [E]; w1[e] bf16
     [2I, H]; w2[e] bf16 [H, I]; pp fp32 [A].
 
@@ -97,7 +103,7 @@ def grouped_mlp_fwd(xp, split, w1, w2, pp, precision="bf16", exact=False) -> dic
     the down GEMM as used), a2_w and xp_w (operands of the weight-gradient
     GEMMs as used; dequantized values in MXFP8 mode).
     """
-    m = _Mode(precision, exact)
+    m = _Mode(precision, exact, fast_quant)
     split = np.asarray(split, dtype=np.int64)
     A, H = xp.shape
     I = w2[0].shape[1]
@@ -111,6 +117,9 @@ def grouped_mlp_fwd(xp, split, w1, w2, pp, precision="bf16", exact=False) -> dic
     r0 = 0
     for e, n in enumerate(split):
         if n == 0:
+            continue
+        if experts is not None and e not in experts:   # rows left at zero
+            r0 += n
             continue
         rs = slice(r0, r0 + n)
         X = m.rows_op(xp[rs])
@@ -133,10 +142,11 @@ def grouped_mlp_fwd(xp, split, w1, w2, pp, precision="bf16", exact=False) -> dic
     return {"yp": yp, "a1": a1s, "a2": a2s, "a2_w": a2w, "xp_w": xpw}
 
 
-def grouped_mlp_bwd(dyp, xp, split, w1, w2, pp, saved, precision="bf16", exact=False) -> dict:
+def grouped_mlp_bwd(dyp, xp, split, w1, w2, pp, saved, precision="bf16", exact=False,
+                    fast_quant=False, experts=None) -> dict:
     """Backward of all experts.  Returns dxp [A, H], dw1[e] [2I, H],
     dw2[e] [H, I] (bf16 unless exact), dpp fp32 [A] and the dA1 operands."""
-    m = _Mode(precision, exact)
+    m = _Mode(precision, exact, fast_quant)
     split = np.asarray(split, dtype=np.int64)
     A, H = dyp.shape
     I = w2[0].shape[1]
@@ -150,6 +160,9 @@ def grouped_mlp_bwd(dyp, xp, split, w1, w2, pp, saved, precision="bf16", exact=F
     r0 = 0
     for e, n in enumerate(split):
         if n == 0:
+            continue
+        if experts is not None and e not in experts:   # rows left at zero
+            r0 += n
             continue
         rs = slice(r0, r0 + n)
         dY = m.rows_op(dyp[rs])
@@ -176,14 +189,19 @@ def grouped_mlp_bwd(dyp, xp, split, w1, w2, pp, saved, precision="bf16", exact=F
 
 
 def layer_step(logits, x, w1, w2, dy, k, precision="bf16", exact=False,
-               softmax_all=False, with_backward=True) -> dict:
+               softmax_all=False, with_backward=True, experts=None, fast_quant=False) -> dict:
     """One MoE layer step: route, permute, grouped MLP, unpermute; then the
     backward: permute dY, grouped MLP backward, unpermute dXp, routing
-    backward."""
+    backward.
+
+    experts: compute the expert MLPs of these experts only (the rows of the
+    others stay zero; every value of the chosen experts' rows and weights, and
+    of the tokens routed only to them, is the full step's).  fast_quant: the
+    vectorized quantizers (same values)."""
     r = _route.route(logits, k, softmax_all, np.float64 if exact else np.float32)
     xp = _route.permute(x, r["src_token"])
     pp = _route.permute_probs(r["topk_prob"], r["dest_row"])
-    fwd = grouped_mlp_fwd(xp, r["split_sizes"], w1, w2, pp, precision, exact)
+    fwd = grouped_mlp_fwd(xp, r["split_sizes"], w1, w2, pp, precision, exact, fast_quant, experts)
     acc = torch.float64 if exact else torch.float32
     out_dt = torch.float64 if exact else torch.bfloat16
     y = _route.unpermute(fwd["yp"], r["dest_row"], out_dt, acc)
@@ -191,7 +209,8 @@ def layer_step(logits, x, w1, w2, dy, k, precision="bf16", exact=False,
     if not with_backward:
         return res
     dyp = _route.permute(dy, r["src_token"])
-    bwd = grouped_mlp_bwd(dyp, xp, r["split_sizes"], w1, w2, pp, fwd, precision, exact)
+    bwd = grouped_mlp_bwd(dyp, xp, r["split_sizes"], w1, w2, pp, fwd, precision, exact, fast_quant,
+                          experts)
     dx = _route.unpermute(bwd["dxp"], r["dest_row"], out_dt, acc)
     dprob = bwd["dpp"].numpy()[r["dest_row"].astype(np.int64)]
     dlogits = _route.route_bwd(logits, r["topk_expert"], dprob, softmax_all)

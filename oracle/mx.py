@@ -32,7 +32,8 @@ Parity: pinned by brute force (nearest of all finite codes), by torch's own
 float8_e4m3fn conversion over every bf16 bit pattern, by the closed-form scale
 values, and by the round-trip and power-of-two-shift invariants (tests).
 
-qdq_rows_fast / qdq_cols_fast compute the same values as qdq_rows / qdq_cols
+qdq_rows_fast / qdq_cols_fast / qdq_cols_grouped_fast compute the same values
+as qdq_rows / qdq_cols / qdq_cols_grouped
 for whole expert weights in seconds instead of minutes: the same scale rule
 (block_scale_exponent), the exact power-of-two unscale in fp32, and torch's
 CPU float8_e4m3fn cast as the rounding step (the library routine the element
@@ -231,6 +232,23 @@ def qdq_rows_fast(x) -> torch.Tensor:
 def qdq_cols_fast(x) -> torch.Tensor:
     """Same values as qdq_cols(x): blocks of 32 consecutive rows."""
     return qdq_rows_fast(x.detach().to(torch.float32).T.contiguous()).T.contiguous()
+
+
+def qdq_cols_grouped_fast(x, sizes) -> torch.Tensor:
+    """Same values as qdq_cols_grouped(x, sizes): inside each group, blocks of
+    32 consecutive rows from the group's first row; the missing rows of the
+    last block count as zeros (they neither raise amax nor give codes)."""
+    v = x.detach().to(torch.float32)
+    out = torch.empty_like(v)
+    r0 = 0
+    for n in np.asarray(sizes, dtype=np.int64):
+        n = int(n)
+        if n:
+            pad = (-n) % BLOCK
+            g = torch.cat([v[r0:r0 + n], v.new_zeros((pad, v.shape[1]))]) if pad else v[r0:r0 + n]
+            out[r0:r0 + n] = qdq_cols_fast(g)[:n]
+        r0 += n
+    return out
 
 
 def dequantize_rows_bf16(codes, scales) -> torch.Tensor:

@@ -179,3 +179,30 @@ def test_mx_close_to_bf16():
     for key in ("y", "dx"):
         rel = (rm[key].float() - rb[key].float()).norm() / rb[key].float().norm()
         assert 0 < rel < 0.15, (key, rel)
+
+
+def test_fast_quant_and_expert_subset_give_the_same_values():
+    """The vectorized quantizers and the per-expert restriction used by the
+    full-size GPU tests change no value of the rows and weights they keep."""
+    c = _case(T=96, H=64, I=96, E=4, seed=81)
+    ref = mlp.layer_step(c["logits"], c["x"], c["w1"], c["w2"], c["dy"], 2, "mxfp8")
+    fast = mlp.layer_step(c["logits"], c["x"], c["w1"], c["w2"], c["dy"], 2, "mxfp8",
+                          fast_quant=True)
+    for key in ("y", "dx"):
+        assert torch.equal(ref[key], fast[key]), key
+    assert np.array_equal(ref["dlogits"], fast["dlogits"])
+    for e in range(4):
+        assert torch.equal(ref["bwd"]["dw1"][e], fast["bwd"]["dw1"][e])
+        assert torch.equal(ref["bwd"]["dw2"][e], fast["bwd"]["dw2"][e])
+    sub = mlp.layer_step(c["logits"], c["x"], c["w1"], c["w2"], c["dy"], 2, "mxfp8",
+                         fast_quant=True, experts={1, 2})
+    r = ref["route"]
+    rows = np.concatenate([np.arange(r["offsets"][e], r["offsets"][e + 1]) for e in (1, 2)])
+    assert torch.equal(sub["fwd"]["yp"][rows], ref["fwd"]["yp"][rows])
+    assert torch.equal(sub["bwd"]["dxp"][rows], ref["bwd"]["dxp"][rows])
+    for e in (1, 2):
+        assert torch.equal(sub["bwd"]["dw1"][e], ref["bwd"]["dw1"][e])
+    both = np.all(np.isin(r["topk_expert"], [1, 2]), axis=1)
+    assert both.any()
+    assert torch.equal(sub["y"][both], ref["y"][both])
+    assert np.array_equal(np.asarray(sub["dlogits"])[both], np.asarray(ref["dlogits"])[both])

@@ -266,3 +266,11 @@ def test_fast_cols_equals_reference():
     v = (rng.standard_normal((320, 96)) * np.exp2(rng.integers(-8, 8, size=(1, 96)))).astype(np.float32)
     x = torch.from_numpy(v).to(torch.bfloat16)
     assert torch.equal(mx.qdq_cols_fast(x), mx.qdq_cols(x))
+
+
+def test_fast_cols_grouped_equals_reference():
+    rng = np.random.default_rng(5)
+    sizes = [0, 1, 31, 32, 33, 70, 0, 5]
+    v = (rng.standard_normal((sum(sizes), 64)) * np.exp2(rng.integers(-6, 6, size=(1, 64)))).astype(np.float32)
+    x = torch.from_numpy(v).to(torch.bfloat16)
+    assert torch.equal(mx.qdq_cols_grouped_fast(x, sizes), mx.qdq_cols_grouped(x, sizes))
