@@ -76,6 +76,11 @@ def kernel_work(name: str, T: int, H: int, I: int, E: int, k: int):
         "route_bwd": (0, A * 16 + T * E * 4),
         "permute": (0, T * H * 2 + A * H * 2 + A * 8),
         "unpermute": (0, A * H * 2 + T * H * 2),
+        # both orientations from one read: 2 B in, twice 1 + 1/32 B out
+        "mx_quant_xp": (0, A * H * (2 + 2 * mx)),
+        "mx_quant_dyp": (0, A * H * (2 + 2 * mx)),
+        "mx_quant_w1": (0, E * 2 * I * H * (2 + 2 * mx)),
+        "mx_quant_w2": (0, E * H * I * (2 + 2 * mx)),
         "mx_quant_rows_xp": (0, A * H * (2 + mx)),
         "mx_quant_cols_xp": (0, A * H * (2 + mx)),
         "mx_quant_rows_dyp": (0, A * H * (2 + mx)),

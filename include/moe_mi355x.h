@@ -193,6 +193,19 @@ int mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, int axis,
                    const int32_t* group_sizes, int ngroups, uint8_t* codes, uint8_t* scales,
                    hipStream_t stream);
 
+/*
+ * mxfp8_quantize_both -- both orientations of mxfp8_quantize from one read of
+ * x: the rowwise codes and scales of axis=1 and the grouped columnwise codes
+ * and scales of axis=0, byte for byte the same as the two separate calls.
+ * [BioNeMo, "MXFP8与融合MLP": a tensor that enters GEMMs contracting along
+ *  either axis needs both copies.]
+ * cols: multiple of 32.  Buffers, groups and errors as for mxfp8_quantize.
+ */
+int mxfp8_quantize_both(const uint16_t* x, int64_t rows, int64_t cols,
+                        const int32_t* group_sizes, int ngroups, uint8_t* row_codes,
+                        uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
+                        hipStream_t stream);
+
 /* Inverse of mxfp8_quantize: out bf16 [rows, cols] = RNE_bf16(decode(code) * 2^(S-127)). */
 int mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                      int axis, const int32_t* group_sizes, int ngroups, uint16_t* out,
@@ -213,6 +226,19 @@ void mxfp8_colwise_bytes(int64_t rows, int64_t cols, int ngroups, size_t* code_b
  * The *_col_codes follow the grouped columnwise layout of mxfp8_quantize; the
  * *_col_scales hold the same bytes block-major per group ([P_g/32][cols]
  * at offset cols*sum(P_j/32, j<g)), the order the backward GEMMs read.
+ *
+ * Optional, MXFP8 mode (all four or none; otherwise MOE_ERR_ARG): the
+ * columnwise MXFP8 of the weights, which the backward's data-gradient GEMMs
+ * contract along the other axis than the forward's.
+ *   w_gate_up_col_*  E*2I*H code bytes: expert e's W1 quantized along 2I,
+ *                    codes [H, 2I] at e*2I*H, scales block-major [2I/32][H]
+ *                    (E*2I*H/32 bytes, expert e at e*2I*H/32).
+ *   w_down_col_*     E*H*I code bytes: W2_e quantized along H, codes [I, H] at
+ *                    e*H*I, scales [H/32][I] at e*H*I/32.
+ * When given, grouped_mlp_fwd writes them in the same pass that quantizes the
+ * weights rowwise (each weight is read once), and grouped_mlp_bwd uses them
+ * instead of quantizing w_gate_up and w_down again; the weights must then be
+ * the same in both calls.  When NULL, the backward quantizes the weights.
  * Members that the mode does not use may be NULL.
  */
 typedef struct moe_saved {
@@ -222,6 +248,10 @@ typedef struct moe_saved {
     uint8_t* a2_col_scales;
     uint8_t* xp_col_codes;
     uint8_t* xp_col_scales;
+    uint8_t* w_gate_up_col_codes;
+    uint8_t* w_gate_up_col_scales;
+    uint8_t* w_down_col_codes;
+    uint8_t* w_down_col_scales;
 } moe_saved;
 
 /*
@@ -235,9 +265,10 @@ typedef struct moe_saved {
  * Per expert e with its M_e = split_sizes[e] consecutive rows of xp:
  *   A1 = xp_e W1_e^T (fp32 accumulation); g = A1[:, :I], u = A1[:, I:]
  *   A2 = prob * silu(g) * u;  yp_e = A2 W2_e^T (rounded to bf16).
- * MXFP8 mode quantizes xp and W1 along H, A2 and W2 along I (rowwise, in the
- * GEMM prologue/epilogue), and also saves the columnwise MXFP8 of xp and A2
- * for the weight gradients.
+ * MXFP8 mode quantizes xp and W1 along H, A2 and W2 along I (rowwise; A2 in
+ * the gate_up GEMM's epilogue), and also saves the columnwise MXFP8 of xp and
+ * A2 for the weight gradients (and of W1 and W2 for the data gradients, when
+ * moe_saved holds their buffers).
  *
  * precision    MOE_BF16 or MOE_MXFP8.
  * E            experts, 1..64.   H, I: hidden and intermediate sizes,

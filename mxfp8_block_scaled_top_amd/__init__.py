@@ -8,7 +8,7 @@ device is not a gfx950.
 
 The functions carry the names of the C entry points (include/moe_mi355x.h):
 moe_route, moe_route_bwd, moe_permute, moe_unpermute, mxfp8_quantize,
-mxfp8_dequantize, grouped_mlp_fwd, grouped_mlp_bwd, moe_workspace_bytes.
+mxfp8_quantize_both, mxfp8_dequantize, grouped_mlp_fwd, grouped_mlp_bwd, moe_workspace_bytes.
 """
 from __future__ import annotations
 
@@ -35,7 +35,9 @@ class MoEError(RuntimeError):
 class _Saved(ctypes.Structure):
     _fields_ = [("a1", ctypes.c_void_p), ("a2", ctypes.c_void_p),
                 ("a2_col_codes", ctypes.c_void_p), ("a2_col_scales", ctypes.c_void_p),
-                ("xp_col_codes", ctypes.c_void_p), ("xp_col_scales", ctypes.c_void_p)]
+                ("xp_col_codes", ctypes.c_void_p), ("xp_col_scales", ctypes.c_void_p),
+                ("w_gate_up_col_codes", ctypes.c_void_p), ("w_gate_up_col_scales", ctypes.c_void_p),
+                ("w_down_col_codes", ctypes.c_void_p), ("w_down_col_scales", ctypes.c_void_p)]
 
 
 def lib() -> ctypes.CDLL:
@@ -55,6 +57,7 @@ def lib() -> ctypes.CDLL:
             "moe_permute": (I32, [P, I64, I32, I32, P, P, P, P, P]),
             "moe_unpermute": (I32, [P, I64, I32, I32, P, P, P, P]),
             "mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, P, P, P]),
+            "mxfp8_quantize_both": (I32, [P, I64, I64, P, I32, P, P, P, P, P]),
             "mxfp8_dequantize": (I32, [P, P, I64, I64, I32, P, I32, P, P]),
             "mxfp8_colwise_bytes": (None, [I64, I64, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
             "grouped_mlp_fwd": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P,
@@ -189,6 +192,23 @@ def mxfp8_quantize(x: torch.Tensor, axis: int = 1, group_sizes=None):
     return codes, scales
 
 
+def mxfp8_quantize_both(x: torch.Tensor, group_sizes=None):
+    """Both orientations from one read: (row codes [R, C], row scales
+    [R, C/32], grouped columnwise codes, their scales), as mxfp8_quantize with
+    axis=1 and axis=0."""
+    _dev(x, torch.bfloat16, "x")
+    R, C = x.shape
+    G = 0 if group_sizes is None else group_sizes.numel()
+    rc = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    rs = torch.empty((R, C // 32), dtype=torch.uint8, device=x.device)
+    cb, sb = colwise_bytes(R, C, max(G, 1))
+    cc = torch.zeros(cb, dtype=torch.uint8, device=x.device)
+    cs = torch.zeros(sb, dtype=torch.uint8, device=x.device)
+    _check(lib().mxfp8_quantize_both(_ptr(x), R, C, _ptr(group_sizes), G, _ptr(rc), _ptr(rs),
+                                     _ptr(cc), _ptr(cs), _stream(x.device)), "mxfp8_quantize_both")
+    return rc, rs, cc, cs
+
+
 def mxfp8_dequantize(codes, scales, rows: int, cols: int, axis: int = 1, group_sizes=None):
     G = 0 if group_sizes is None else group_sizes.numel()
     out = torch.empty((rows, cols), dtype=torch.bfloat16, device=codes.device)
@@ -204,8 +224,11 @@ def _ptr_array(ts):
     return arr
 
 
-def alloc_saved(rows: int, H: int, I: int, E: int, precision: int, device) -> dict:
-    """Caller-owned tensors the forward saves for the backward."""
+def alloc_saved(rows: int, H: int, I: int, E: int, precision: int, device,
+                weight_cols: bool = True) -> dict:
+    """Caller-owned tensors the forward saves for the backward.  weight_cols
+    (MXFP8): also the buffers for the weights' columnwise MXFP8, so that the
+    forward quantizes each weight once for both passes."""
     s = {"a1": torch.empty((rows, 2 * I), dtype=torch.bfloat16, device=device)}
     if precision == MOE_BF16:
         s["a2"] = torch.empty((rows, I), dtype=torch.bfloat16, device=device)
@@ -216,6 +239,12 @@ def alloc_saved(rows: int, H: int, I: int, E: int, precision: int, device) -> di
         cb, sb = colwise_bytes(rows, H, E)
         s["xp_col_codes"] = torch.empty(cb, dtype=torch.uint8, device=device)
         s["xp_col_scales"] = torch.empty(sb, dtype=torch.uint8, device=device)
+        if weight_cols:
+            n1, n2 = E * 2 * I * H, E * H * I
+            s["w_gate_up_col_codes"] = torch.empty(n1, dtype=torch.uint8, device=device)
+            s["w_gate_up_col_scales"] = torch.empty(n1 // 32, dtype=torch.uint8, device=device)
+            s["w_down_col_codes"] = torch.empty(n2, dtype=torch.uint8, device=device)
+            s["w_down_col_scales"] = torch.empty(n2 // 32, dtype=torch.uint8, device=device)
     return s
 
 

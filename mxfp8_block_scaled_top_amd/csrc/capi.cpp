@@ -152,6 +152,26 @@ int mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, int axis,
                                         rows, cols, stream));
 }
 
+int mxfp8_quantize_both(const uint16_t* x, int64_t rows, int64_t cols,
+                        const int32_t* group_sizes, int ngroups, uint8_t* row_codes,
+                        uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
+                        hipStream_t stream) {
+    int st = check_quant_args(x, row_codes, row_scales, rows, cols, 1, nullptr, 0);
+    if (st != MOE_OK) return st;
+    if ((st = check_quant_args(x, col_codes, col_scales, rows, cols, 0, group_sizes, ngroups)) !=
+        MOE_OK)
+        return st;
+    if (!device_ok()) return MOE_ERR_UNSUPPORTED;
+    MatTable src{}, rc{}, rs{}, cc{}, cs{};
+    src.p[0] = x;
+    rc.p[0] = row_codes;
+    rs.p[0] = row_scales;
+    cc.p[0] = col_codes;
+    cs.p[0] = col_scales;
+    return hip_status(launch_quant(src, 1, group_sizes, group_sizes ? ngroups : 1, rows, cols, &rc,
+                                   &rs, false, &cc, &cs, false, stream, "mx_quant_both"));
+}
+
 int mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                      int axis, const int32_t* group_sizes, int ngroups, uint16_t* out,
                      hipStream_t stream) {

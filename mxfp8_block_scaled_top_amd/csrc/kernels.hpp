@@ -37,6 +37,13 @@ int64_t colwise_block_bound(int64_t rows, int ngroups);
 // scales_t: store the E8M0 scales block-major ([K/32][rows] for rowwise,
 // [P_g/32][cols] per group for grouped columnwise), the layout the grouped
 // GEMM reads with one coalesced load per K step; false = the public layout.
+// Rowwise (rcodes given), grouped columnwise (ccodes given) or both, from one
+// read of each matrix.
+hipError_t launch_quant(const MatTable& src, int nmat, const int32_t* sizes, int ngroups,
+                        int64_t rows, int64_t cols, const MatTable* rcodes,
+                        const MatTable* rscales, bool rscales_t, const MatTable* ccodes,
+                        const MatTable* cscales, bool cscales_t, hipStream_t s,
+                        const char* name);
 hipError_t launch_quant_rows(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, int64_t rows, int64_t cols, hipStream_t s,
                              const char* name = "mx_quant_rows", bool scales_t = false);

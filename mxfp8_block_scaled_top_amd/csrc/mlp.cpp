@@ -111,6 +111,36 @@ BwdWs carve_bwd(void* base, int64_t rows, int H, int I, int E, int precision) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The optional columnwise MXFP8 copies of the weights in moe_saved: all four
+// buffers or none, 16-byte aligned.
+int check_weight_cols(const moe_saved* s) {
+    const void* p[4] = {s->w_gate_up_col_codes, s->w_gate_up_col_scales, s->w_down_col_codes,
+                        s->w_down_col_scales};
+    int n = 0;
+    for (const void* q : p) {
+        n += q != nullptr;
+        if (!aligned16(q)) return MOE_ERR_ALIGN;
+    }
+    return (n == 0 || n == 4) ? MOE_OK : MOE_ERR_ARG;
+}
+
+struct WeightCols {
+    MatTable w1c, w1s, w2c, w2s;
+};
+
+// Per-expert slices: W1_e along 2I as [H, 2I] with block-major scales
+// [2I/32][H]; W2_e along H as [I, H] with scales [H/32][I].
+WeightCols weight_cols(const moe_saved* s, int E, int H, int I) {
+    WeightCols w{};
+    for (int e = 0; e < E; ++e) {
+        w.w1c.p[e] = s->w_gate_up_col_codes + (size_t)e * 2 * I * H;
+        w.w1s.p[e] = s->w_gate_up_col_scales + (size_t)e * 2 * I * H / 32;
+        w.w2c.p[e] = s->w_down_col_codes + (size_t)e * H * I;
+        w.w2s.p[e] = s->w_down_col_scales + (size_t)e * H * I / 32;
+    }
+    return w;
+}
+
 int check_common(int precision, int E, int H, int I, int64_t rows) {
     if (precision != MOE_BF16 && precision != MOE_MXFP8) return MOE_ERR_ARG;
     if (E < 1 || E > kMaxExperts) return MOE_ERR_SHAPE;
@@ -162,6 +192,7 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
                                        !saved->xp_col_codes || !saved->xp_col_scales))
             return MOE_ERR_NULL;
     }
+    if ((st = check_weight_cols(saved)) != MOE_OK) return st;
     if (!aligned16(xp) || !aligned16(yp) || !aligned16(saved->a1) || !aligned16(saved->a2))
         return MOE_ERR_ALIGN;
     for (int e = 0; e < E; ++e)
@@ -202,15 +233,19 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
         MOE_TRY(launch_gemm(DT_BF16, U_DOWN_FWD, d, stream));
         return MOE_OK;
     }
-    // MXFP8: quantize operands along their contraction axis
-    MatTable src{}, cd{}, sc{};
+    // MXFP8: quantize operands along their contraction axis.  xp: rowwise for
+    // gate_up, grouped columnwise (saved) for the gate_up weight gradient, from
+    // one read.
+    MatTable src{}, cd{}, sc{}, ccd{}, csc{};
     src.p[0] = xp;
     cd.p[0] = w.xq;
     sc.p[0] = w.xq_s;
-    MOE_TRY(launch_quant_rows(src, cd, sc, 1, rows, H, stream, "mx_quant_rows_xp", true));
-    cd.p[0] = saved->xp_col_codes;
-    sc.p[0] = saved->xp_col_scales;
-    MOE_TRY(launch_quant_cols(src, cd, sc, 1, split_sizes, E, rows, H, stream, "mx_quant_cols_xp", true));
+    ccd.p[0] = saved->xp_col_codes;
+    csc.p[0] = saved->xp_col_scales;
+    MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, H, &cd, &sc, true, &ccd, &csc, true, stream,
+                         "mx_quant_xp"));
+    // weights: rowwise (along H for W1, along I for W2) for these GEMMs; with
+    // the saved columnwise buffers, also the backward's copies from the same read
     MatTable w1t{}, w1c{}, w1s{}, w2t{}, w2c{}, w2s{};
     for (int e = 0; e < E; ++e) {
         w1t.p[e] = w_gate_up[e];
@@ -220,8 +255,17 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
         w2c.p[e] = w.w2q + (size_t)e * H * I;
         w2s.p[e] = w.w2q_s + (size_t)e * H * I / 32;
     }
-    MOE_TRY(launch_quant_rows(w1t, w1c, w1s, E, 2 * (int64_t)I, H, stream, "mx_quant_rows_w1", true));
-    MOE_TRY(launch_quant_rows(w2t, w2c, w2s, E, H, I, stream, "mx_quant_rows_w2", true));
+    if (saved->w_gate_up_col_codes) {
+        WeightCols wc = weight_cols(saved, E, H, I);
+        MOE_TRY(launch_quant(w1t, E, nullptr, 1, 2 * (int64_t)I, H, &w1c, &w1s, true, &wc.w1c,
+                             &wc.w1s, true, stream, "mx_quant_w1"));
+        MOE_TRY(launch_quant(w2t, E, nullptr, 1, H, I, &w2c, &w2s, true, &wc.w2c, &wc.w2s, true,
+                             stream, "mx_quant_w2"));
+    } else {
+        MOE_TRY(launch_quant_rows(w1t, w1c, w1s, E, 2 * (int64_t)I, H, stream, "mx_quant_rows_w1",
+                                  true));
+        MOE_TRY(launch_quant_rows(w2t, w2c, w2s, E, H, I, stream, "mx_quant_rows_w2", true));
+    }
 
     g.a = w.xq;
     g.lda = H;
@@ -282,6 +326,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
                                        !saved->xp_col_codes || !saved->xp_col_scales))
             return MOE_ERR_NULL;
     }
+    if ((st = check_weight_cols(saved)) != MOE_OK) return st;
     if (!aligned16(dyp) || !aligned16(xp) || !aligned16(dxp) || !aligned16(saved->a1) ||
         !aligned16(saved->a2))
         return MOE_ERR_ALIGN;
@@ -377,14 +422,15 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     // ---- MXFP8
     MatTable src{}, cd{}, sc{};
     if (rows > 0) {
+        // rowwise for the down dgrad, grouped columnwise for the down wgrad
+        MatTable ccd{}, csc{};
         src.p[0] = dyp;
         cd.p[0] = w.dyq;
         sc.p[0] = w.dyq_s;
-        MOE_TRY(launch_quant_rows(src, cd, sc, 1, rows, H, stream, "mx_quant_rows_dyp", true));
-        cd.p[0] = w.dyc;
-        sc.p[0] = w.dyc_s;
-        MOE_TRY(launch_quant_cols(src, cd, sc, 1, split_sizes, E, rows, H, stream,
-                                  "mx_quant_cols_dyp", true));
+        ccd.p[0] = w.dyc;
+        csc.p[0] = w.dyc_s;
+        MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, H, &cd, &sc, true, &ccd, &csc, true,
+                             stream, "mx_quant_dyp"));
     }
     MatTable w1t{}, w1c{}, w1s{}, w2t{}, w2c{}, w2s{};
     for (int e = 0; e < E; ++e) {
@@ -395,11 +441,21 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         w1c.p[e] = w.w1c + (size_t)e * 2 * I * H;
         w1s.p[e] = w.w1c_s + (size_t)e * 2 * I * H / 32;
     }
+    if (saved->w_gate_up_col_codes) {   // made by the forward from the same weights
+        WeightCols wc = weight_cols(saved, E, H, I);
+        w1c = wc.w1c;
+        w1s = wc.w1s;
+        w2c = wc.w2c;
+        w2s = wc.w2s;
+    }
     if (rows > 0) {
-        // W2 [H, I] along H -> [I, H];  W1 [2I, H] along 2I -> [H, 2I]
-        MOE_TRY(launch_quant_cols(w2t, w2c, w2s, E, nullptr, 1, H, I, stream, "mx_quant_cols_w2", true));
-        MOE_TRY(launch_quant_cols(w1t, w1c, w1s, E, nullptr, 1, 2 * (int64_t)I, H, stream,
-                                  "mx_quant_cols_w1", true));
+        if (!saved->w_gate_up_col_codes) {
+            // W2 [H, I] along H -> [I, H];  W1 [2I, H] along 2I -> [H, 2I]
+            MOE_TRY(launch_quant_cols(w2t, w2c, w2s, E, nullptr, 1, H, I, stream,
+                                      "mx_quant_cols_w2", true));
+            MOE_TRY(launch_quant_cols(w1t, w1c, w1s, E, nullptr, 1, 2 * (int64_t)I, H, stream,
+                                      "mx_quant_cols_w1", true));
+        }
         GemmArgs g{};
         g.split = split_sizes;
         g.E = E;

@@ -5,12 +5,12 @@
 // MoE recipe page, bottleneck section and the section on MXFP8 and the fused
 // MLP].  Encoding rules in common.hpp.
 //
-// Rowwise (blocks along the last dim): one thread per block of 32 values, 64 B
-// read and 33 B written per thread.  Grouped columnwise (blocks of 32 rows
-// inside each group, stored transposed so the rows become the contiguous
-// axis): one thread per 4 columns of one 32-row block, so the block maximum
-// is a per-thread reduction and each column's 32 codes leave as two 16 B
-// stores.  Both are HBM-bound.
+// Quantization reads each value once and can write both orientations from
+// that read: rowwise (blocks along the last dim) and grouped columnwise
+// (blocks of 32 rows inside each group, stored transposed so the rows become
+// the contiguous axis).  A weight needs both (forward and backward GEMMs
+// contract it along different axes), and so do the activations that enter a
+// data-gradient GEMM and a weight-gradient GEMM.  HBM-bound.
 //
 // The kernels take tables of matrices so that all experts' weights are
 // quantized by one launch.
@@ -20,49 +20,7 @@
 
 namespace moe {
 
-// ---------------------------------------------------------------- rowwise
-__global__ __launch_bounds__(256) void quant_rows_kernel(MatTable src, MatTable codes,
-                                                         MatTable scales, int nmat, int64_t rows,
-                                                         int64_t cols, int scales_t) {
-    const int64_t bpr = cols / kMxBlock;
-    const int64_t per_mat = rows * bpr;
-    const int64_t total = per_mat * nmat;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        int m = (int)(i / per_mat);
-        int64_t b = i - (int64_t)m * per_mat;          // block index inside the matrix
-        const u32x4* in = (const u32x4*)src.p[m] + b * 4;
-        u32x4 v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = __builtin_nontemporal_load(in + q);
-        float amax = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-                amax = fmaxf(amax, fmaxf(__builtin_fabsf(lo_bf16(v[q][w])),
-                                         __builtin_fabsf(hi_bf16(v[q][w]))));
-        uint32_t S = mx_scale_byte(amax);
-        u32x4 o[2];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            o[q >> 1][(q & 1) * 2] = mx_encode4(lo_bf16(v[q][0]), hi_bf16(v[q][0]),
-                                                lo_bf16(v[q][1]), hi_bf16(v[q][1]), S);
-            o[q >> 1][(q & 1) * 2 + 1] = mx_encode4(lo_bf16(v[q][2]), hi_bf16(v[q][2]),
-                                                    lo_bf16(v[q][3]), hi_bf16(v[q][3]), S);
-        }
-        u32x4* out = (u32x4*)codes.p[m] + b * 2;
-        out[0] = o[0];
-        out[1] = o[1];
-        int64_t si = b;
-        if (scales_t) {                               // block-major: [cols/32][rows]
-            int64_t r = b / bpr, kb = b - r * bpr;
-            si = kb * rows + r;
-        }
-        ((uint8_t*)scales.p[m])[si] = (uint8_t)S;
-    }
-}
-
+// ---------------------------------------------------------------- dequantization, rowwise
 __global__ __launch_bounds__(256) void dequant_rows_kernel(const u32x4* __restrict__ codes,
                                                            const uint8_t* __restrict__ scales,
                                                            int64_t nblocks,
@@ -127,56 +85,161 @@ __device__ ColBlock locate_col_block(const int32_t* __restrict__ sizes, int ngro
     return cb;
 }
 
-// 256 threads x 4 columns; grid (ceil(cols/1024), upper bound of 32-row
-// blocks, nmat).
-__global__ __launch_bounds__(256) void quant_cols_kernel(MatTable src, MatTable codes,
-                                                         MatTable scales,
-                                                         const int32_t* __restrict__ sizes,
-                                                         int ngroups, int64_t rows,
-                                                         int64_t cols, int scales_t) {
+// ---------------------------------------------------------------- quantization
+// One launch quantizes a bf16 matrix (or one per expert) rowwise, grouped
+// columnwise, or both from a single read of its values.
+//
+// A wave takes one 32-row block of the grouped walk (the blocks of the
+// columnwise layout; one group of all rows when there are no groups) and 512
+// columns: lane l loads columns c0 = 512 * blockIdx.x + 8 l .. c0 + 7 of every
+// row of the block, one 16-byte load per row (1 KiB per wave and row).
+//   rowwise     a 32-value block is 4 neighbouring lanes; their maxima meet by
+//               a quad reduction (DPP), and each lane encodes its 8 values and
+//               stores them as 8 bytes (512 contiguous bytes per wave and row).
+//   columnwise  a lane owns 8 whole 32-row column blocks: the maximum is a
+//               per-lane reduction and each column's 32 codes leave as two
+//               16-byte stores.  Block q of the walk goes to wave q % 4 of
+//               workgroup q / 4, so the four waves of a workgroup write the
+//               four neighbouring 32-byte pieces of a column's 128-byte line.
+// Block maxima are taken on the bf16 bit patterns with the sign cleared
+// (ordered like the magnitudes), two at a time with packed 16-bit maxima.
+struct QuantTileArgs {
+    MatTable src;               // bf16 [rows, cols] per matrix
+    MatTable rcodes, rscales;   // rowwise codes [rows, cols]; scales [rows][cols/32]
+                                // or block-major [cols/32][rows]
+    MatTable ccodes, cscales;   // grouped columnwise codes; scales [cols][P_g/32] or
+                                // block-major [P_g/32][cols] per group
+    const int32_t* sizes;       // group sizes (device), NULL = one group
+    int ngroups;
+    int64_t rows, cols;
+    int rscales_t, cscales_t;
+};
+
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
+// magnitude bits of the two bf16 halves of w
+__device__ __forceinline__ uint32_t abs2(uint32_t w) { return w & 0x7fff7fffu; }
+
+template <bool ROWS, bool COLS>
+__global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
     __shared__ int lds[192];
     const int m = blockIdx.z;
-    ColBlock cb = locate_col_block(sizes, ngroups, rows, blockIdx.y, lds);
-    if (cb.valid <= 0) return;
-    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (c0 >= cols) return;
-    const bf16_t* in = (const bf16_t*)src.p[m];
-    u32x2 v[kMxBlock];
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const ColBlock cb = locate_col_block(a.sizes, a.ngroups, a.rows,
+                                         (int64_t)blockIdx.y * 4 + wv, lds);
+    // every field is the same across the wave
+    const int valid = __builtin_amdgcn_readfirstlane(cb.valid);
+    if (valid <= 0) return;
+    const int64_t r0 = __builtin_amdgcn_readfirstlane((int)cb.r0);
+    const int64_t i0 = __builtin_amdgcn_readfirstlane((int)cb.i0);
+    const int64_t pad = __builtin_amdgcn_readfirstlane((int)cb.pad_rows);
+    const int64_t pbase = __builtin_amdgcn_readfirstlane((int)cb.pbase);
+    const int64_t cols = a.cols;
+    const int64_t c0 = (int64_t)blockIdx.x * 512 + lane * 8;
+    if (c0 >= cols) return;   // whole 32-column blocks: cols is a multiple of 32 for rows
+
+    const char* in = (const char*)a.src.p[m] + r0 * cols * 2;
+    u32x4 v[kMxBlock];
 #pragma unroll
-    for (int i = 0; i < kMxBlock; ++i) {
-        v[i] = (u32x2){0u, 0u};
-        if (i < cb.valid) v[i] = *(const u32x2*)(in + (cb.r0 + i) * cols + c0);
+    for (int j = 0; j < kMxBlock; ++j) {
+        v[j] = (u32x4){0u, 0u, 0u, 0u};
+        if (j < valid)
+            v[j] = __builtin_nontemporal_load((const u32x4*)(in + (j * cols + c0) * 2));
     }
-    uint8_t* cout = (uint8_t*)codes.p[m] + cb.pbase * cols + cb.i0;
-    // scale of (column c, block i0/32): [c][P/32] (public) or [P/32][c] (block-major)
-    uint8_t* sout = (uint8_t*)scales.p[m] + cb.pbase / kMxBlock * cols +
-                    (scales_t ? cb.i0 / kMxBlock * cols : cb.i0 / kMxBlock);
-    const int64_t sstride = scales_t ? 1 : cb.pad_rows / kMxBlock;
+
+    if constexpr (ROWS) {
+        uint8_t* rc = (uint8_t*)a.rcodes.p[m] + r0 * cols + c0;
+        const int64_t kb = c0 >> 5;
+        const int s = lane & 3;
+        uint32_t sp[2] = {0u, 0u};   // block-major: scale bytes of rows 8s .. 8s+7
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        float amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < kMxBlock; ++i) {
-            uint32_t w = v[i][j >> 1];
-            float f = (j & 1) ? hi_bf16(w) : lo_bf16(w);
-            amax = fmaxf(amax, __builtin_fabsf(f));
-        }
-        uint32_t S = mx_scale_byte(amax);
-        u32x4 o[2];
-#pragma unroll
-        for (int i = 0; i < kMxBlock; i += 4) {
-            float f[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uint32_t w = v[i + r][j >> 1];
-                f[r] = (j & 1) ? hi_bf16(w) : lo_bf16(w);
+        for (int j = 0; j < kMxBlock; ++j) {
+            if (j < valid) {
+                uint32_t mw = pk_max_u16(pk_max_u16(abs2(v[j][0]), abs2(v[j][1])),
+                                         pk_max_u16(abs2(v[j][2]), abs2(v[j][3])));
+                uint32_t am = max(mw & 0xffffu, mw >> 16);
+                // quad_perm [1,0,3,2] then [2,3,0,1]: the 4 lanes of a block
+                am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0xB1, 0xF, 0xF, true));
+                am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0x4E, 0xF, 0xF, true));
+                const uint32_t S = mx_scale_byte(__uint_as_float(am << 16));
+                u32x2 o;
+                o[0] = mx_encode4(lo_bf16(v[j][0]), hi_bf16(v[j][0]), lo_bf16(v[j][1]),
+                                  hi_bf16(v[j][1]), S);
+                o[1] = mx_encode4(lo_bf16(v[j][2]), hi_bf16(v[j][2]), lo_bf16(v[j][3]),
+                                  hi_bf16(v[j][3]), S);
+                *(u32x2*)(rc + j * cols) = o;
+                if (a.rscales_t) {
+                    if ((j >> 3) == s) sp[(j >> 2) & 1] |= S << (8 * (j & 3));
+                } else if (s == 0) {
+                    ((uint8_t*)a.rscales.p[m])[(r0 + j) * (cols >> 5) + kb] = (uint8_t)S;
+                }
             }
-            o[i >> 4][(i >> 2) & 3] = mx_encode4(f[0], f[1], f[2], f[3], S);
         }
-        u32x4* dst = (u32x4*)(cout + (c0 + j) * cb.pad_rows);
-        dst[0] = o[0];
-        dst[1] = o[1];
-        sout[(c0 + j) * sstride] = (uint8_t)S;
+        if (a.rscales_t) {
+            // [cols/32][rows]: this block's 32 rows of column block kb are
+            // contiguous; lane s of the quad stores rows 8s .. 8s+7
+            uint8_t* rs = (uint8_t*)a.rscales.p[m] + kb * a.rows + r0 + 8 * s;
+            const int nv = min(8, valid - 8 * s);
+            if (nv == 8 && ((uintptr_t)rs & 7u) == 0) {
+                *(u32x2*)rs = (u32x2){sp[0], sp[1]};
+            } else {
+                for (int t = 0; t < nv; ++t) rs[t] = (uint8_t)(sp[t >> 2] >> (8 * (t & 3)));
+            }
+        }
+    }
+
+    if constexpr (ROWS && COLS) {
+        // keeps the compiler from holding the rowwise pass's 256 widened
+        // floats live for reuse here (that would cost the occupancy)
+#pragma unroll
+        for (int j = 0; j < kMxBlock; ++j) asm volatile("" : "+v"(v[j]));
+    }
+
+    if constexpr (COLS) {
+        uint32_t mw[4] = {0u, 0u, 0u, 0u};   // column maxima, two columns per word
+#pragma unroll
+        for (int j = 0; j < kMxBlock; ++j)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) mw[w] = pk_max_u16(mw[w], abs2(v[j][w]));
+        // group g stored as [cols, P_g] at cols * P_0..g-1; rows past the
+        // group's end were loaded as zeros and encode to 0x00
+        uint8_t* cc = (uint8_t*)a.ccodes.p[m] + pbase * cols + i0;
+        uint32_t sc[2] = {0u, 0u};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const uint32_t am = (t & 1) ? (mw[t >> 1] >> 16) : (mw[t >> 1] & 0xffffu);
+            const uint32_t S = mx_scale_byte(__uint_as_float(am << 16));
+            u32x4 o[2];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {   // rows 4q .. 4q+3
+                float f[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t w = v[4 * q + r][t >> 1];
+                    f[r] = (t & 1) ? hi_bf16(w) : lo_bf16(w);
+                }
+                o[q >> 2][q & 3] = mx_encode4(f[0], f[1], f[2], f[3], S);
+            }
+            u32x4* dst = (u32x4*)(cc + (c0 + t) * pad);
+            dst[0] = o[0];
+            dst[1] = o[1];
+            sc[t >> 2] |= S << (8 * (t & 3));
+        }
+        uint8_t* cs = (uint8_t*)a.cscales.p[m] + pbase / kMxBlock * cols;
+        if (a.cscales_t) {   // [P_g/32][cols]: 8 neighbouring columns, 8 bytes
+            *(u32x2*)(cs + i0 / kMxBlock * cols + c0) = (u32x2){sc[0], sc[1]};
+        } else {             // [cols][P_g/32]
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                cs[(c0 + t) * (pad / kMxBlock) + i0 / kMxBlock] =
+                    (uint8_t)(sc[t >> 2] >> (8 * (t & 3)));
+        }
     }
 }
 
@@ -229,27 +292,45 @@ int64_t colwise_block_bound(int64_t rows, int ngroups) {
     return (rows + kMxBlock - 1) / kMxBlock + (ngroups > 1 ? ngroups : 1);
 }
 
+// Quantizes nmat matrices of [rows, cols]: rowwise where rcodes is given,
+// grouped columnwise where ccodes is given, both from one read.
+hipError_t launch_quant(const MatTable& src, int nmat, const int32_t* sizes, int ngroups,
+                        int64_t rows, int64_t cols, const MatTable* rcodes,
+                        const MatTable* rscales, bool rscales_t, const MatTable* ccodes,
+                        const MatTable* cscales, bool cscales_t, hipStream_t s,
+                        const char* name) {
+    if (rows == 0 || cols == 0 || nmat == 0 || (!rcodes && !ccodes)) return hipSuccess;
+    QuantTileArgs a{};
+    a.src = src;
+    if (rcodes) a.rcodes = *rcodes, a.rscales = *rscales;
+    if (ccodes) a.ccodes = *ccodes, a.cscales = *cscales;
+    a.sizes = sizes;
+    a.ngroups = sizes ? ngroups : 1;
+    a.rows = rows;
+    a.cols = cols;
+    a.rscales_t = rscales_t ? 1 : 0;
+    a.cscales_t = cscales_t ? 1 : 0;
+    const int64_t nblk = colwise_block_bound(rows, a.ngroups);
+    dim3 grid((unsigned)((cols + 511) / 512), (unsigned)((nblk + 3) / 4), (unsigned)nmat);
+    TraceScope ts(name, s);
+    if (rcodes && ccodes) quant_tile_kernel<true, true><<<grid, 256, 0, s>>>(a);
+    else if (rcodes) quant_tile_kernel<true, false><<<grid, 256, 0, s>>>(a);
+    else quant_tile_kernel<false, true><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_rows(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, int64_t rows, int64_t cols, hipStream_t s,
                              const char* name, bool scales_t) {
-    int64_t n = (int64_t)nmat * rows * (cols / kMxBlock);
-    if (n == 0) return hipSuccess;
-    TraceScope ts(name, s);
-    quant_rows_kernel<<<grid_1d(n, 256), 256, 0, s>>>(src, codes, scales, nmat, rows, cols,
-                                                      scales_t ? 1 : 0);
-    return hipGetLastError();
+    return launch_quant(src, nmat, nullptr, 1, rows, cols, &codes, &scales, scales_t, nullptr,
+                        nullptr, false, s, name);
 }
 
 hipError_t launch_quant_cols(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, const int32_t* sizes, int ngroups, int64_t rows,
                              int64_t cols, hipStream_t s, const char* name, bool scales_t) {
-    if (rows == 0 || cols == 0 || nmat == 0) return hipSuccess;
-    dim3 grid((unsigned)((cols + 1023) / 1024), (unsigned)colwise_block_bound(rows, ngroups),
-              (unsigned)nmat);
-    TraceScope ts(name, s);
-    quant_cols_kernel<<<grid, 256, 0, s>>>(src, codes, scales, sizes, ngroups, rows, cols,
-                                           scales_t ? 1 : 0);
-    return hipGetLastError();
+    return launch_quant(src, nmat, sizes, ngroups, rows, cols, nullptr, nullptr, false, &codes,
+                        &scales, scales_t, s, name);
 }
 
 hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,

@@ -14,9 +14,9 @@ from . import (MOE_BF16, MOE_OP_MLP_BWD, MOE_OP_MLP_FWD, alloc_saved, grouped_ml
 
 
 class LayerBuffers:
-    def __init__(self, T, H, I, E, k, precision, device):
+    def __init__(self, T, H, I, E, k, precision, device, weight_cols=True):
         rows = T * k
-        self.saved = alloc_saved(rows, H, I, E, precision, device)
+        self.saved = alloc_saved(rows, H, I, E, precision, device, weight_cols)
         self.ws_fwd = torch.empty(max(256, moe_workspace_bytes(MOE_OP_MLP_FWD, T, H, I, E, k, precision)),
                                   dtype=torch.uint8, device=device)
         self.ws_bwd = torch.empty(max(256, moe_workspace_bytes(MOE_OP_MLP_BWD, T, H, I, E, k, precision)),

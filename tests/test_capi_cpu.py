@@ -30,7 +30,7 @@ def _declared_functions():
 def test_header_declares_the_path():
     names = _declared_functions()
     for n in ["moe_route", "moe_route_bwd", "moe_permute", "moe_unpermute", "mxfp8_quantize",
-              "mxfp8_dequantize", "grouped_mlp_fwd", "grouped_mlp_bwd", "moe_workspace_bytes",
+              "mxfp8_quantize_both", "mxfp8_dequantize", "grouped_mlp_fwd", "grouped_mlp_bwd", "moe_workspace_bytes",
               "moe_status_string", "moe_device_supported", "mxfp8_colwise_bytes"]:
         assert n in names, n
 
@@ -76,6 +76,10 @@ def test_host_validation_before_launch(L):
     # quantize: bad axis, cols not a multiple of 32
     assert L.mxfp8_quantize(p, 4, 64, 2, None, 0, p, p, None) == ARG
     assert L.mxfp8_quantize(p, 4, 48, 1, None, 0, p, p, None) == SHAPE
+    # both orientations: cols a multiple of 32, four aligned outputs
+    assert L.mxfp8_quantize_both(p, 4, 48, None, 0, p, p, p, p, None) == SHAPE
+    assert L.mxfp8_quantize_both(p, 4, 64, None, 0, p, p, None, p, None) == N
+    assert L.mxfp8_quantize_both(p, 4, 64, None, 0, p, p, mis, p, None) == ALIGN
     # grouped MLP: H not a multiple of 128, bad precision, null tables
     saved = moe._Saved(4096, 4096, 4096, 4096, 4096, 4096)
     tab = (ctypes.c_void_p * 2)(4096, 4096)
@@ -87,6 +91,12 @@ def test_host_validation_before_launch(L):
                              1 << 30, None) == N
     assert L.grouped_mlp_fwd(0, 2, 128, 256, 8, p, p, tab, tab, p, p, ctypes.byref(saved), p,
                              16, None) == WS
+    # the weights' columnwise buffers: all four or none
+    part = moe._Saved(4096, 4096, 4096, 4096, 4096, 4096, 4096, None, None, None)
+    assert L.grouped_mlp_fwd(1, 2, 128, 256, 8, p, p, tab, tab, p, p, ctypes.byref(part), p,
+                             1 << 30, None) == ARG
+    assert L.grouped_mlp_bwd(1, 2, 128, 256, 8, p, p, p, tab, tab, p, ctypes.byref(part), p, tab,
+                             tab, p, p, 1 << 30, None) == ARG
 
 
 def test_no_gpu_means_unsupported(L):

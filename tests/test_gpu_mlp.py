@@ -10,7 +10,7 @@ import torch
 
 import mxfp8_block_scaled_top_amd as moe
 from mxfp8_block_scaled_top_amd import synth
-from mxfp8_block_scaled_top_amd.layer import layer_step
+from mxfp8_block_scaled_top_amd.layer import LayerBuffers, layer_step
 from oracle import mlp as omlp
 from oracle import mx as omx
 from oracle import route as oroute
@@ -83,6 +83,16 @@ def _layer_compare(inp, k, precision, tag):
         assert np.array_equal(np_(got["saved"]["xp_col_codes"])[: xc.size], xc)
         got_s = np_(got["saved"]["xp_col_scales"])
         assert np.array_equal(_block_major_to_public(got_s, r["split_sizes"], H)[: xs.size], xs)
+        # the weights' columnwise copies the forward saved for the backward
+        I = inp["w2"][0].shape[1]
+        wc = {"w_gate_up": (inp["w1"], 2 * I * H, H), "w_down": (inp["w2"], H * I, I)}
+        for name, (ws, n, C) in wc.items():
+            codes, scales = np_(got["saved"][name + "_col_codes"]), np_(got["saved"][name + "_col_scales"])
+            for e, W in enumerate(ws):
+                oc, os_ = omx.quantize_cols_grouped(W, [W.shape[0]])
+                assert np.array_equal(codes[e * n:(e + 1) * n], oc), (name, e)
+                got_s = scales[e * n // 32:(e + 1) * n // 32]
+                assert np.array_equal(_block_major_to_public(got_s, [W.shape[0]], C), os_), (name, e)
     return got, ref
 
 
@@ -114,6 +124,27 @@ def test_single_expert_dense(precision):
 def test_many_experts_topk8(precision):
     inp = _inputs(T=512, H=256, I=384, E=64, seed=3)
     _layer_compare(inp, 8, precision, "e64k8")
+
+
+def test_weight_cols_saved_or_quantized_in_backward():
+    """The backward reading the forward's columnwise weight copies and the
+    backward quantizing the weights itself give the same bytes."""
+    T, H, I, E, k = 700, 384, 640, 6, 2
+    inp = _inputs(T=T, H=H, I=I, E=E, seed=6, dead=(4,))
+    dev = {n: (v.cuda() if isinstance(v, torch.Tensor) else [w.cuda() for w in v]) for n, v in inp.items()}
+    res = []
+    for wc in (True, False):
+        say(f"layer weight_cols={wc}")
+        bufs = LayerBuffers(T, H, I, E, k, moe.MOE_MXFP8, "cuda", weight_cols=wc)
+        a = layer_step(dev["logits"], dev["x"], dev["w1"], dev["w2"], dev["dy"], k, moe.MOE_MXFP8,
+                       bufs=bufs)
+        res.append({key: (v.clone() if isinstance(v, torch.Tensor) else [w.clone() for w in v])
+                    for key, v in a.items() if key in ("y", "dx", "dpp", "dlogits", "dw1", "dw2")})
+    for key in ("y", "dx", "dpp", "dlogits"):
+        assert torch.equal(res[0][key], res[1][key]), key
+    for e in range(E):
+        assert torch.equal(res[0]["dw1"][e], res[1]["dw1"][e]), e
+        assert torch.equal(res[0]["dw2"][e], res[1]["dw2"][e]), e
 
 
 def test_deterministic_bf16_and_mx():

@@ -91,3 +91,30 @@ def test_quant_deterministic():
     a = moe.mxfp8_quantize(x)
     b = moe.mxfp8_quantize(x)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("sizes,C", [([0, 5, 32, 0, 70, 1], 64), ([300], 608), (None, 1408),
+                                     ([2816] * 2, 2048), ("skewed", 96)])
+def test_quant_both_orientations(sizes, C):
+    """Both orientations from one read equal the oracle's rowwise and grouped
+    columnwise quantization (and so the two separate calls) byte for byte,
+    including column tiles cut short (C not a multiple of 512) and groups with
+    no rows or a partial last block."""
+    rng = np.random.default_rng(5)
+    if sizes == "skewed":
+        sh = synth.SHAPES["skewed"]
+        from oracle import route as oroute
+        sizes = list(oroute.route(synth.router_logits(sh).numpy(), sh.k)["split_sizes"])
+    R = 1000 if sizes is None else int(sum(sizes))
+    say(f"quant both R={R} C={C} groups={None if sizes is None else len(sizes)}")
+    x = torch.from_numpy((rng.standard_normal((R, C)) * np.exp2(rng.uniform(-8, 8, (R, 1))))
+                         .astype(np.float32)).to(torch.bfloat16)
+    gs = None if sizes is None else torch.tensor(sizes, dtype=torch.int32, device="cuda")
+    rcode, rscale, ccode, cscale = moe.mxfp8_quantize_both(x.cuda(), group_sizes=gs)
+    osz = [R] if sizes is None else sizes
+    orc, ors = omx.quantize_rows(x)
+    assert np.array_equal(np_(rscale), ors), "row scales"
+    assert np.array_equal(np_(rcode), orc), "row codes"
+    occ, ocs = omx.quantize_cols_grouped(x, osz)
+    assert np.array_equal(np_(ccode)[: occ.size], occ), "column codes"
+    assert np.array_equal(np_(cscale)[: ocs.size], ocs), "column scales"
