@@ -30,9 +30,11 @@ Modules:
             unpermute, routing backward.
   mlp    -- grouped gate_up -> ScaledSwiGLU -> down, forward and backward,
             in BF16 and MXFP8, and the full layer step.
+  router -- the router linear layer (logits = X W_r^T) in front of the
+            routing, its backward, and the layer step with it.
 
 Parity status of each function is stated in its docstring; the conventions the
 pages leave open (gate/up half order, softmax over the selected k) are marked
 "parity unpinned" where no pin beyond internal consistency exists.
 """
-from . import mx, route, mlp  # noqa: F401
+from . import mx, route, mlp, router  # noqa: F401
