@@ -82,7 +82,9 @@ typedef enum moe_precision {
 typedef enum moe_op {
     MOE_OP_ROUTE = 0,
     MOE_OP_MLP_FWD = 1,
-    MOE_OP_MLP_BWD = 2
+    MOE_OP_MLP_BWD = 2,
+    MOE_OP_ROUTER_FWD = 3,    /* T, E, k used */
+    MOE_OP_ROUTER_BWD = 4     /* T, H, E used (k must still be valid) */
 } moe_op;
 
 /* Limits of this version. */
@@ -137,6 +139,46 @@ int moe_route(const float* logits, int64_t T, int E, int k, uint32_t flags,
 int moe_route_bwd(const float* topk_prob, const float* dprob_perm, const int32_t* dest_row,
                   const int32_t* topk_expert, const float* logits, int64_t T, int E, int k,
                   uint32_t flags, float* dlogits, hipStream_t stream);
+
+/*
+ * moe_router_fwd -- the router linear layer fused with the routing: logits =
+ * x W_r^T, then exactly what moe_route does with those logits.
+ * [AutoModel, "MoE 微调的痛点": every token is routed to a few experts.  The
+ *  pages do not give the router; it is read as a bias-free linear map of the
+ *  token's hidden state, as in the MoE models that page names.]
+ *
+ * x            bf16 [T, H], H a multiple of 64.   w_router: bf16 [E, H].
+ * logits       fp32 [T, E] out: sum_h x[t,h] w_router[e,h] with fp32
+ *              accumulation (the order of the sum is unspecified); kept for
+ *              moe_route_bwd with MOE_ROUTE_SOFTMAX_ALL and for the caller.
+ * k, flags, topk_expert .. src_token, workspace: as moe_route (workspace of
+ *              moe_workspace_bytes(MOE_OP_ROUTER_FWD, T, 0, 0, E, k, 0) bytes).
+ */
+int moe_router_fwd(const uint16_t* x, const uint16_t* w_router, int64_t T, int H, int E, int k,
+                   uint32_t flags, float* logits, int32_t* topk_expert, float* topk_prob,
+                   int32_t* split_sizes, int32_t* expert_offsets, int32_t* dest_row,
+                   int32_t* src_token, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/*
+ * moe_router_bwd -- backward of the router linear layer, fused with the
+ * combine of the expert path's token gradient.
+ *
+ * dlogits      fp32 [T, E] (moe_route_bwd).   x, w_router: as in the forward.
+ * dxp          bf16 [T*k, H] gradient of the grouped rows from grouped_mlp_bwd,
+ *              or NULL (then dx holds the router term alone).
+ * dest_row     int32 [T, k] (moe_route); required when dxp is given.
+ * dx           bf16 [T, H] out: bf16( sum_j dxp[dest_row[t][j]]  (slot order)
+ *              + sum_e dlogits[t,e] w_router[e] ), one fp32 sum, one rounding.
+ * dw_router    bf16 [E, H] out: sum_t dlogits[t,e] x[t], fp32 partial sums
+ *              over fixed token splits added in a fixed order (deterministic);
+ *              zeros when T = 0.
+ * workspace    moe_workspace_bytes(MOE_OP_ROUTER_BWD, T, H, 0, E, k, 0) bytes.
+ */
+int moe_router_bwd(const float* dlogits, const uint16_t* x, const uint16_t* w_router, int64_t T,
+                   int H, int E, int k, const int32_t* dest_row, const uint16_t* dxp,
+                   uint16_t* dx, uint16_t* dw_router, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
 
 /*
  * moe_permute -- dispatch: copy each token row to the grouped row of every

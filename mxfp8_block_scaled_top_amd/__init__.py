@@ -7,8 +7,8 @@ There is no CPU fallback: calls fail when the library is not built or the
 device is not a gfx950.
 
 The functions carry the names of the C entry points (include/moe_mi355x.h):
-moe_route, moe_route_bwd, moe_permute, moe_unpermute, mxfp8_quantize,
-mxfp8_quantize_both, mxfp8_dequantize, grouped_mlp_fwd, grouped_mlp_bwd, moe_workspace_bytes.
+moe_route, moe_route_bwd, moe_router_fwd, moe_router_bwd, moe_permute,
+moe_unpermute, mxfp8_quantize, mxfp8_quantize_both, mxfp8_dequantize, grouped_mlp_fwd, grouped_mlp_bwd, moe_workspace_bytes.
 """
 from __future__ import annotations
 
@@ -22,7 +22,7 @@ LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(_PKG, "_lib", "libmo
 
 MOE_BF16, MOE_MXFP8 = 0, 1
 MOE_ROUTE_RENORM, MOE_ROUTE_SOFTMAX_ALL = 0, 1
-MOE_OP_ROUTE, MOE_OP_MLP_FWD, MOE_OP_MLP_BWD = 0, 1, 2
+MOE_OP_ROUTE, MOE_OP_MLP_FWD, MOE_OP_MLP_BWD, MOE_OP_ROUTER_FWD, MOE_OP_ROUTER_BWD = 0, 1, 2, 3, 4
 MAX_EXPERTS = 64
 
 _lib = None
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
             "moe_unpermute": (I32, [P, I64, I32, I32, P, P, P, P]),
             "mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, P, P, P]),
             "mxfp8_quantize_both": (I32, [P, I64, I64, P, I32, P, P, P, P, P]),
+            "moe_router_fwd": (I32, [P, P, I64, I32, I32, I32, U32, P, P, P, P, P, P, P, P, SZ, P]),
+            "moe_router_bwd": (I32, [P, P, P, I64, I32, I32, I32, P, P, P, P, P, SZ, P]),
             "mxfp8_dequantize": (I32, [P, P, I64, I64, I32, P, I32, P, P]),
             "mxfp8_colwise_bytes": (None, [I64, I64, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
             "grouped_mlp_fwd": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P,
@@ -134,6 +136,52 @@ def moe_route(logits: torch.Tensor, k: int, softmax_all: bool = False) -> dict:
                            _ptr(out["src_token"]), _ptr(ws), ws.numel(), _stream(dev)),
            "moe_route")
     return out
+
+
+def moe_router_fwd(x: torch.Tensor, w_router: torch.Tensor, k: int,
+                   softmax_all: bool = False) -> dict:
+    """Router linear layer + top-k routing.  Returns the outputs of moe_route
+    and the fp32 logits [T, E]."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(w_router, torch.bfloat16, "w_router")
+    T, H = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    out = {
+        "logits": torch.empty((T, E), dtype=torch.float32, device=dev),
+        "topk_expert": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "topk_prob": torch.empty((T, k), dtype=torch.float32, device=dev),
+        "split_sizes": torch.empty(E, dtype=torch.int32, device=dev),
+        "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "dest_row": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "src_token": torch.empty(T * k, dtype=torch.int32, device=dev),
+    }
+    ws = _workspace(moe_workspace_bytes(MOE_OP_ROUTER_FWD, T, H, 0, E, k, 0), dev)
+    _check(lib().moe_router_fwd(_ptr(x), _ptr(w_router), T, H, E, k, int(softmax_all),
+                                _ptr(out["logits"]), _ptr(out["topk_expert"]),
+                                _ptr(out["topk_prob"]), _ptr(out["split_sizes"]),
+                                _ptr(out["expert_offsets"]), _ptr(out["dest_row"]),
+                                _ptr(out["src_token"]), _ptr(ws), ws.numel(), _stream(dev)),
+           "moe_router_fwd")
+    return out
+
+
+def moe_router_bwd(dlogits, x, w_router, dest_row=None, dxp=None, workspace=None):
+    """Returns (dx bf16 [T, H], dw_router bf16 [E, H]); dx includes the combine
+    of dxp (the expert path) when it is given."""
+    _dev(x, torch.bfloat16, "x")
+    T, H = x.shape
+    E = w_router.shape[0]
+    k = dest_row.shape[1] if dest_row is not None else 1
+    dev = x.device
+    if workspace is None:
+        workspace = _workspace(moe_workspace_bytes(MOE_OP_ROUTER_BWD, T, H, 0, E, k, 0), dev)
+    dx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((E, H), dtype=torch.bfloat16, device=dev)
+    _check(lib().moe_router_bwd(_ptr(dlogits), _ptr(x), _ptr(w_router), T, H, E, k,
+                                _ptr(dest_row), _ptr(dxp), _ptr(dx), _ptr(dw), _ptr(workspace),
+                                workspace.numel(), _stream(dev)), "moe_router_bwd")
+    return dx, dw
 
 
 def moe_route_bwd(topk_prob, dprob_perm, dest_row, topk_expert, E: int, logits=None,

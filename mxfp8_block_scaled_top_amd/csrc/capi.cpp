@@ -61,6 +61,8 @@ size_t moe_workspace_bytes(int op, int64_t T, int H, int I, int E, int k, int pr
         case MOE_OP_ROUTE: return route_workspace_bytes(T, E, k);
         case MOE_OP_MLP_FWD: return mlp_fwd_workspace_bytes(T * k, H, I, E, precision);
         case MOE_OP_MLP_BWD: return mlp_bwd_workspace_bytes(T * k, H, I, E, precision);
+        case MOE_OP_ROUTER_FWD: return route_workspace_bytes(T, E, k);
+        case MOE_OP_ROUTER_BWD: return router_bwd_workspace_bytes(T, H, E);
         default: return 0;
     }
 }
@@ -79,6 +81,47 @@ int moe_route(const float* logits, int64_t T, int E, int k, uint32_t flags, int3
     return hip_status(launch_route(logits, (int)T, E, k, flags, topk_expert, topk_prob,
                                    split_sizes, expert_offsets, dest_row, src_token, workspace,
                                    stream));
+}
+
+int moe_router_fwd(const uint16_t* x, const uint16_t* w_router, int64_t T, int H, int E, int k,
+                   uint32_t flags, float* logits, int32_t* topk_expert, float* topk_prob,
+                   int32_t* split_sizes, int32_t* expert_offsets, int32_t* dest_row,
+                   int32_t* src_token, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+    if (T < 0 || E < 1 || E > kMaxExperts || k < 1 || k > E || T * k > INT32_MAX || H < 64 ||
+        (H % 64))
+        return MOE_ERR_SHAPE;
+    if (flags > MOE_ROUTE_SOFTMAX_ALL) return MOE_ERR_ARG;
+    if (!split_sizes || !expert_offsets || !workspace) return MOE_ERR_NULL;
+    if (T > 0 && (!x || !w_router || !logits || !topk_expert || !topk_prob || !dest_row ||
+                  !src_token))
+        return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_ALIGN;
+    if (workspace_bytes < route_workspace_bytes(T, E, k)) return MOE_ERR_WORKSPACE;
+    if (!device_ok()) return MOE_ERR_UNSUPPORTED;
+    hipError_t e = launch_router_logits(x, w_router, (int)T, H, E, logits, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(launch_route(logits, (int)T, E, k, flags, topk_expert, topk_prob,
+                                   split_sizes, expert_offsets, dest_row, src_token, workspace,
+                                   stream));
+}
+
+int moe_router_bwd(const float* dlogits, const uint16_t* x, const uint16_t* w_router, int64_t T,
+                   int H, int E, int k, const int32_t* dest_row, const uint16_t* dxp,
+                   uint16_t* dx, uint16_t* dw_router, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+    if (T < 0 || E < 1 || E > kMaxExperts || k < 1 || k > E || T * k > INT32_MAX || H < 64 ||
+        (H % 64))
+        return MOE_ERR_SHAPE;
+    if (!w_router || !dw_router || !workspace) return MOE_ERR_NULL;
+    if (T > 0 && (!dlogits || !x || !dx || (dxp && !dest_row))) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(dxp) || !aligned16(dx) ||
+        !aligned16(dw_router))
+        return MOE_ERR_ALIGN;
+    if (workspace_bytes < router_bwd_workspace_bytes(T, H, E)) return MOE_ERR_WORKSPACE;
+    if (!device_ok()) return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_router_bwd(dlogits, x, w_router, (int)T, H, E, k, dest_row, dxp, dx,
+                                        dw_router, workspace, stream));
 }
 
 int moe_route_bwd(const float* topk_prob, const float* dprob_perm, const int32_t* dest_row,

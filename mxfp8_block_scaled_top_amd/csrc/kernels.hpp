@@ -32,6 +32,14 @@ hipError_t launch_permute(const bf16_t* x, int T, int H, int k, const int32_t* d
 hipError_t launch_unpermute(const bf16_t* yp, int T, int H, int k, const int32_t* dest_row,
                             const float* topk_prob, bf16_t* y, hipStream_t s);
 
+// ---- router linear layer
+size_t router_bwd_workspace_bytes(int64_t T, int H, int E);
+hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w, int T, int H, int E,
+                                float* logits, hipStream_t s);
+hipError_t launch_router_bwd(const float* dlogits, const bf16_t* x, const bf16_t* w, int T,
+                             int H, int E, int k, const int32_t* dest_row, const bf16_t* dxp,
+                             bf16_t* dx, bf16_t* dw, void* ws, hipStream_t s);
+
 // ---- MXFP8
 int64_t colwise_block_bound(int64_t rows, int ngroups);
 // scales_t: store the E8M0 scales block-major ([K/32][rows] for rowwise,

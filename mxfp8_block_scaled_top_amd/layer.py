@@ -9,8 +9,8 @@ from __future__ import annotations
 import torch
 
 from . import (MOE_BF16, MOE_OP_MLP_BWD, MOE_OP_MLP_FWD, alloc_saved, grouped_mlp_bwd,
-               grouped_mlp_fwd, moe_permute, moe_route, moe_route_bwd, moe_unpermute,
-               moe_workspace_bytes)
+               grouped_mlp_fwd, moe_permute, moe_route, moe_route_bwd, moe_router_bwd,
+               moe_router_fwd, moe_unpermute, moe_workspace_bytes)
 
 
 class LayerBuffers:
@@ -25,14 +25,8 @@ class LayerBuffers:
         self.dw2 = [torch.empty((H, I), dtype=torch.bfloat16, device=device) for _ in range(E)]
 
 
-def layer_step(logits, x, w1, w2, dy, k, precision=MOE_BF16, bufs: LayerBuffers | None = None,
-               with_backward=True, softmax_all=False) -> dict:
+def _expert_step(r, x, w1, w2, dy, k, precision, bufs, with_backward):
     T, H = x.shape
-    E = len(w1)
-    I = w2[0].shape[1]
-    if bufs is None:
-        bufs = LayerBuffers(T, H, I, E, k, precision, x.device)
-    r = moe_route(logits, k, softmax_all)
     xp, pp = moe_permute(x, r["dest_row"], r["topk_prob"])
     yp, saved = grouped_mlp_fwd(xp, r["split_sizes"], w1, w2, pp, precision, bufs.saved, bufs.ws_fwd)
     y = moe_unpermute(yp, r["dest_row"])
@@ -42,9 +36,48 @@ def layer_step(logits, x, w1, w2, dy, k, precision=MOE_BF16, bufs: LayerBuffers 
     dyp, _ = moe_permute(dy, r["dest_row"])
     dxp, dw1, dw2, dpp = grouped_mlp_bwd(dyp, xp, r["split_sizes"], w1, w2, pp, saved, precision,
                                          bufs.ws_bwd, bufs.dw1, bufs.dw2)
-    dx = moe_unpermute(dxp, r["dest_row"])
-    dlogits = moe_route_bwd(r["topk_prob"], dpp, r["dest_row"], r["topk_expert"], E,
-                            logits if softmax_all else None, softmax_all)
-    out.update({"dyp": dyp, "dxp": dxp, "dw1": dw1, "dw2": dw2, "dpp": dpp, "dx": dx,
-                "dlogits": dlogits})
+    out.update({"dyp": dyp, "dxp": dxp, "dw1": dw1, "dw2": dw2, "dpp": dpp})
+    return out
+
+
+def _buffers(x, w1, w2, k, precision, bufs):
+    T, H = x.shape
+    if bufs is None:
+        bufs = LayerBuffers(T, H, w2[0].shape[1], len(w1), k, precision, x.device)
+    return bufs
+
+
+def layer_step(logits, x, w1, w2, dy, k, precision=MOE_BF16, bufs: LayerBuffers | None = None,
+               with_backward=True, softmax_all=False) -> dict:
+    """From router logits and tokens to Y; then dY to dX, dW1, dW2, dlogits."""
+    E = len(w1)
+    bufs = _buffers(x, w1, w2, k, precision, bufs)
+    r = moe_route(logits, k, softmax_all)
+    out = _expert_step(r, x, w1, w2, dy, k, precision, bufs, with_backward)
+    if not with_backward:
+        return out
+    out["dx"] = moe_unpermute(out["dxp"], r["dest_row"])
+    out["dlogits"] = moe_route_bwd(r["topk_prob"], out["dpp"], r["dest_row"], r["topk_expert"], E,
+                                   logits if softmax_all else None, softmax_all)
+    return out
+
+
+def layer_step_router(x, w_router, w1, w2, dy, k, precision=MOE_BF16,
+                      bufs: LayerBuffers | None = None, with_backward=True,
+                      softmax_all=False) -> dict:
+    """The same step with the router linear layer in front: logits = x W_r^T
+    and the routing in one call; in the backward, dlogits gives dW_r and the
+    router's share of dX, which is added to the combine of dXp before its one
+    rounding."""
+    E = len(w1)
+    bufs = _buffers(x, w1, w2, k, precision, bufs)
+    r = moe_router_fwd(x, w_router, k, softmax_all)
+    out = _expert_step(r, x, w1, w2, dy, k, precision, bufs, with_backward)
+    out["logits"] = r["logits"]
+    if not with_backward:
+        return out
+    out["dlogits"] = moe_route_bwd(r["topk_prob"], out["dpp"], r["dest_row"], r["topk_expert"], E,
+                                   r["logits"] if softmax_all else None, softmax_all)
+    out["dx"], out["dw_router"] = moe_router_bwd(out["dlogits"], x, w_router, r["dest_row"],
+                                                 out["dxp"])
     return out

@@ -34,6 +34,7 @@ CHUNK = 1 << 22
 TAG_LOGITS, TAG_X, TAG_W1, TAG_W2, TAG_DY = 1, 2, 3, 4, 5
 TAG_Q_BASE, TAG_Q_ROWEXP, TAG_Q_MASK, TAG_Q_SIGN, TAG_Q_OUTLIER = 6, 7, 8, 9, 10
 TAG_BIAS_PERM = 11
+TAG_WR = 12
 
 _POOL_THREADS = 16
 
@@ -119,6 +120,13 @@ def router_logits(shape: MoEShape, seed: int = 0) -> torch.Tensor:
         bias = (-shape.zipf_log_scale * shape.zipf_s * np.log(rank)).astype(np.float32)
         lg = lg + bias[None, :]
     return torch.from_numpy(np.ascontiguousarray(lg, dtype=np.float32))
+
+
+def router_weight(shape: MoEShape, seed: int = 0) -> torch.Tensor:
+    """bf16 [E, H] router weight: N(0, 1/H) entries, so that with N(0,1)
+    tokens the logits X W_r^T have about unit variance, like the logits
+    workload's."""
+    return normal_bf16((shape.E, shape.H), seed, TAG_WR, 0, float(shape.H) ** -0.5)
 
 
 def tokens(shape: MoEShape, seed: int = 0) -> torch.Tensor:

@@ -30,7 +30,7 @@ def _declared_functions():
 def test_header_declares_the_path():
     names = _declared_functions()
     for n in ["moe_route", "moe_route_bwd", "moe_permute", "moe_unpermute", "mxfp8_quantize",
-              "mxfp8_quantize_both", "mxfp8_dequantize", "grouped_mlp_fwd", "grouped_mlp_bwd", "moe_workspace_bytes",
+              "mxfp8_quantize_both", "mxfp8_dequantize", "moe_router_fwd", "moe_router_bwd", "grouped_mlp_fwd", "grouped_mlp_bwd", "moe_workspace_bytes",
               "moe_status_string", "moe_device_supported", "mxfp8_colwise_bytes"]:
         assert n in names, n
 
@@ -73,6 +73,17 @@ def test_host_validation_before_launch(L):
     # permute: H not a multiple of 8, misaligned
     assert L.moe_permute(p, 10, 12, 2, p, None, p, None, None) == SHAPE
     assert L.moe_permute(mis, 10, 16, 2, p, None, p, None, None) == ALIGN
+    # router: H not a multiple of 64, k > E, bad flags, dxp without dest_row, misaligned, workspace
+    assert L.moe_router_fwd(p, p, 10, 96, 4, 2, 0, p, p, p, p, p, p, p, p, 1 << 20, None) == SHAPE
+    assert L.moe_router_fwd(p, p, 10, 128, 4, 5, 0, p, p, p, p, p, p, p, p, 1 << 20, None) == SHAPE
+    assert L.moe_router_fwd(p, p, 10, 128, 4, 2, 5, p, p, p, p, p, p, p, p, 1 << 20, None) == ARG
+    assert L.moe_router_fwd(p, None, 10, 128, 4, 2, 0, p, p, p, p, p, p, p, p, 1 << 20, None) == N
+    assert L.moe_router_fwd(mis, p, 10, 128, 4, 2, 0, p, p, p, p, p, p, p, p, 1 << 20, None) == ALIGN
+    assert L.moe_router_fwd(p, p, 10, 128, 4, 2, 0, p, p, p, p, p, p, p, p, 1, None) == WS
+    assert L.moe_router_bwd(p, p, p, 10, 128, 4, 2, None, p, p, p, p, 1 << 30, None) == N
+    assert L.moe_router_bwd(p, p, p, 10, 100, 4, 2, p, p, p, p, p, 1 << 30, None) == SHAPE
+    assert L.moe_router_bwd(p, p, p, 10, 128, 4, 2, p, p, p, mis, p, 1 << 30, None) == ALIGN
+    assert L.moe_router_bwd(p, p, p, 10, 128, 4, 2, p, p, p, p, p, 1, None) == WS
     # quantize: bad axis, cols not a multiple of 32
     assert L.mxfp8_quantize(p, 4, 64, 2, None, 0, p, p, None) == ARG
     assert L.mxfp8_quantize(p, 4, 48, 1, None, 0, p, p, None) == SHAPE
