@@ -17,6 +17,10 @@ roofline        the dominant kernel (largest total time in the step): its
                 launch on the launch stream during the timed steps
 cpu_baseline    the CPU oracle (tests only otherwise) timed on a bounded
                 sample of the same workload on this host's cores
+router          the router linear layer (logits = x W_r^T fused with the
+                routing; its backward) at the same shape, per launch
+loop_baseline   a per-expert torch loop (BF16, autograd) on the same inputs,
+                and the grouped path's speedup over it
 """
 from __future__ import annotations
 
@@ -44,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--cpu-inter", type=int, default=768)
+    ap.add_argument("--no-router", action="store_true", help="skip the router linear layer line")
+    ap.add_argument("--no-loop", action="store_true", help="skip the per-expert loop baseline")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -181,6 +187,112 @@ def run_gpu(args, prec_name, inp_dev, shape):
     }
 
 
+def router_bytes(name: str, T: int, H: int, E: int, k: int, ns: int) -> float:
+    """Algorithmic HBM bytes of one launch of a router kernel."""
+    return {"router_logits": T * H * 2 + E * H * 2 + T * E * 4,
+            "router_dx": T * k * H * 2 + T * k * 4 + T * E * 4 + E * H * 2 + T * H * 2,
+            "router_dw": T * H * 2 + T * E * 4 + ns * E * H * 4,
+            "router_dw_reduce": ns * E * H * 4 + E * H * 2}.get(name, 0.0)
+
+
+def run_router(args, inp_dev, shape):
+    """The router linear layer at the workload's shape:
+    moe_router_fwd (logits on MFMA + routing) and moe_router_bwd (router share
+    of dX fused with the combine of dXp, and dW_r), timed per launch."""
+    import torch
+    import mxfp8_block_scaled_top_amd as moe
+    from mxfp8_block_scaled_top_amd import synth
+
+    T, H, E, k = shape.T, shape.H, shape.E, shape.k
+    wr = synth.router_weight(shape).cuda()
+    x = inp_dev["x"]
+    dxp = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda").normal_()
+    ws = torch.empty(moe.moe_workspace_bytes(moe.MOE_OP_ROUTER_BWD, T, H, 0, E, k, 0),
+                     dtype=torch.uint8, device="cuda")
+    ns = (ws.numel() - 256) // (E * H * 4)
+
+    def step():
+        r = moe.moe_router_fwd(x, wr, k)
+        dl = torch.empty((T, E), dtype=torch.float32, device="cuda").normal_()
+        moe.moe_router_bwd(dl, x, wr, r["dest_row"], dxp, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    moe.trace_enable(max(64, 16 * args.steps))
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    trace = moe.trace_read()
+    moe.trace_disable()
+    per = {}
+    for name, d in trace:
+        per.setdefault(name, []).append(d)
+    out = {}
+    for name, ds in per.items():
+        mean = sum(ds) / len(ds)
+        by = router_bytes(name, T, H, E, k, ns)
+        out[name] = {"mean_ms": round(mean, 4)}
+        if by:
+            out[name]["gbs"] = round(by / (mean * 1e-3) / 1e9, 1)
+    fwd_names = ("router_logits", "route_topk", "route_scan", "route_scatter")
+    fwd = sum(out[n]["mean_ms"] for n in out if n in fwd_names)
+    bwd = sum(out[n]["mean_ms"] for n in out if n.startswith("router_d"))
+    lg = out.get("router_logits", {})
+    return {"workload": f"{shape.name}: T={T}, H={H}, E={E}, k={k}", "fwd_ms": round(fwd, 4),
+            "bwd_ms": round(bwd, 4), "kernels": out,
+            "roofline_logits": {"bound": "hbm", "achieved": lg.get("gbs"), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s",
+                                "frac": round(lg.get("gbs", 0) / PEAK_HBM_GBS, 4)}}
+
+
+def run_loop_baseline(args, inp_dev, shape):
+    """Per-expert loop: the structure of the Hugging Face
+    MoE block the pages compare against -- torch softmax + top-k, then for
+    each expert an index of its tokens, nn.Linear-style GEMMs (torch ->
+    hipBLASLt), SwiGLU, probability scale and index_add -- forward and
+    backward through torch autograd, in BF16.  A measurement baseline only;
+    the product path never runs it."""
+    import torch
+    import torch.nn.functional as F
+
+    T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
+    w1 = [w.detach().clone().requires_grad_(True) for w in inp_dev["w1"]]
+    w2 = [w.detach().clone().requires_grad_(True) for w in inp_dev["w2"]]
+    logits = inp_dev["logits"].detach().clone().requires_grad_(True)
+    x = inp_dev["x"].detach().clone().requires_grad_(True)
+    dy = inp_dev["dy"]
+
+    def step():
+        probs, sel = torch.topk(logits, k, dim=1)
+        probs = torch.softmax(probs, dim=1)
+        y = torch.zeros_like(x)
+        for e in range(E):
+            tok, slot = torch.where(sel == e)
+            if tok.numel() == 0:
+                continue
+            xe = x[tok]
+            h = F.linear(xe, w1[e])
+            a = F.silu(h[:, :I]) * h[:, I:]
+            ye = F.linear(a, w2[e]) * probs[tok, slot, None].to(x.dtype)
+            y = y.index_add(0, tok, ye)
+        y.backward(dy)
+        for t in [x, logits, *w1, *w2]:
+            t.grad = None
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    n = max(1, min(args.steps, 5))
+    t0 = time.perf_counter()
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    return {"kind": "per-expert loop, torch BF16 (autograd)", "steps": n, "ms_per_step": round(ms, 3),
+            "tokens_per_s": round(T / (ms * 1e-3), 1)}
+
+
 def cpu_baseline(args, inp_host, shape, prec_name):
     """The oracle on a bounded sample: the first `cpu_tokens` tokens and the
     first `cpu_inter` intermediate columns (gate rows [0, Is), up rows
@@ -274,6 +386,14 @@ def main():
                   "frac_of_mfma_peak": round(q["frac_of_peak"], 4), "roofline": q["roofline"],
                   "gemm_only": {"ms": round(q["gemm_ms"], 3), "tflops": round(q["gemm_tflops"], 1)},
                   "kernels": q["kernels"]}
+    if not args.no_router:
+        out["router"] = run_router(args, dev, shape)
+        log(args, f"router: fwd {out['router']['fwd_ms']} ms, bwd {out['router']['bwd_ms']} ms")
+    if not args.no_loop:
+        lb = run_loop_baseline(args, dev, shape)
+        lb["grouped_speedup"] = {p: round(lb["ms_per_step"] / res[p]["ms_per_step"], 2) for p in precs}
+        out["loop_baseline"] = lb
+        log(args, f"per-expert loop: {lb['ms_per_step']} ms/step; grouped speedup {lb['grouped_speedup']}")
     if not args.no_cpu:
         del dev
         torch.cuda.empty_cache()

@@ -174,8 +174,9 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict_
     }
 }
 
-// part[s][e][c] = sum over the tokens of split s (ascending within each of
-// the 4 waves' interleaved subsets, the waves then added in order).
+// part[s][e][c] = sum over the tokens of split s (wave w takes tokens
+// w, w+4, .. of the split in ascending order; the 4 waves are then added in
+// order).
 __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict__ G,
                                                         const bf16_t* __restrict__ x, int T,
                                                         int H, int E, int tps,
@@ -196,18 +197,29 @@ __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict_
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[e][q] = 0.f;
         if (c < H) {
-            for (int t = tb + wave; t < te; t += 4) {
-                const u32x2 xv = *(const u32x2*)(x + (int64_t)t * H + c);
-                const float xf[4] = {lo_bf16(xv[0]), hi_bf16(xv[0]), lo_bf16(xv[1]),
-                                     hi_bf16(xv[1])};
-                const float* g = G + (int64_t)t * E + e0;
+            // 8 of the wave's tokens per iteration, all loads first (bytes in
+            // flight); tokens past the split's end load row tb with weight 0
+            for (int t = tb + wave; t < te; t += 32) {
+                u32x2 xv[8];
+                float gw[8][kDwExperts];
 #pragma unroll
-                for (int e = 0; e < kDwExperts; ++e) {
-                    if (e < ne) {
-                        const float ge = g[e];
+                for (int u = 0; u < 8; ++u) {
+                    const int tu = t + 4 * u;
+                    const bool ok = tu < te;
+                    xv[u] = *(const u32x2*)(x + (int64_t)(ok ? tu : tb) * H + c);
+                    const float* g = G + (int64_t)(ok ? tu : tb) * E + e0;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) acc[e][q] = __builtin_fmaf(ge, xf[q], acc[e][q]);
-                    }
+                    for (int e = 0; e < kDwExperts; ++e) gw[u][e] = (ok && e < ne) ? g[e] : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float xf[4] = {lo_bf16(xv[u][0]), hi_bf16(xv[u][0]), lo_bf16(xv[u][1]),
+                                         hi_bf16(xv[u][1])};
+#pragma unroll
+                    for (int e = 0; e < kDwExperts; ++e)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[e][q] = __builtin_fmaf(gw[u][e], xf[q], acc[e][q]);
                 }
             }
         }
