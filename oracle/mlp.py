@@ -33,6 +33,13 @@ Xp_e (M_e rows), pp_e the permuted probabilities:
     dW1_e = bf16(dA1_e^T Xp_e)
   experts with no rows: nothing in Yp, dW1_e = dW2_e = 0.
 
+FP8 mode (per-tensor scaling, see mx.quantize_tensor) quantizes every GEMM
+operand with one scale per tensor: xp and dYp (all experts' rows), each
+expert's W1_e and W2_e, and A2 and dA1 (all rows).  The amax of A2 and dA1
+is only known once every expert's values exist, so they are materialized in
+bf16 first and then cast; the transposed copies the other GEMMs use carry the
+same values.
+
 MXFP8 mode quantizes every GEMM operand along that GEMM's contraction axis:
 forward Xp and W1 along H, A2 and W2 along I (rowwise); dgrad dYp along H
 (rowwise) with W2 along H (columnwise of [H, I]), dA1 along 2I with W1 along
@@ -63,9 +70,11 @@ def _sigmoid(g: torch.Tensor) -> torch.Tensor:
 
 class _Mode:
     def __init__(self, precision: str, exact: bool, fast_quant: bool = False):
-        assert precision in ("bf16", "mxfp8")
+        assert precision in ("bf16", "mxfp8", "fp8")
         assert not (exact and precision != "bf16")
         self.mx = precision == "mxfp8"
+        self.fp8 = precision == "fp8"
+        self.q_tensor = _mx.qdq_tensor_fast if fast_quant else _mx.qdq_tensor
         self.exact = exact
         self.acc = torch.float64 if exact else torch.float32
         # the vectorized quantizers give the reference values bit for bit
@@ -93,6 +102,9 @@ class _Mode:
             return self.val(t)
         return self.q_cols_grouped(t, [t.shape[0]]).to(self.acc)
 
+    def tensor_op(self, t):         # FP8: one scale for the whole tensor
+        return self.q_tensor(t).to(self.acc)
+
 
 def grouped_mlp_fwd(xp, split, w1, w2, pp, precision="bf16", exact=False,
                     fast_quant=False, experts=None) -> dict:
@@ -114,6 +126,9 @@ def grouped_mlp_fwd(xp, split, w1, w2, pp, precision="bf16", exact=False,
     a2s = torch.zeros((A, I), dtype=m.acc)
     a2w = torch.zeros((A, I), dtype=m.acc)
     xpw = torch.zeros((A, H), dtype=m.acc)
+    if m.fp8:
+        xq = m.tensor_op(xp)
+        a2pre = torch.zeros((A, I), dtype=torch.bfloat16)
     r0 = 0
     for e, n in enumerate(split):
         if n == 0:
@@ -122,12 +137,16 @@ def grouped_mlp_fwd(xp, split, w1, w2, pp, precision="bf16", exact=False,
             r0 += n
             continue
         rs = slice(r0, r0 + n)
-        X = m.rows_op(xp[rs])
-        W1 = m.rows_op(w1[e])
+        X = xq[rs] if m.fp8 else m.rows_op(xp[rs])
+        W1 = m.tensor_op(w1[e]) if m.fp8 else m.rows_op(w1[e])
         A1 = X @ W1.T
         g, u = A1[:, :I], A1[:, I:]
         A2 = pp[rs].to(m.acc)[:, None] * _silu(g) * u
         a1s[rs] = m.store(A1)
+        if m.fp8:                      # cast after every expert's A2 exists
+            a2pre[rs] = A2.to(torch.bfloat16)
+            r0 += n
+            continue
         if m.mx:
             a2op = m.rows_op(A2)
             a2w[rs] = m.group_cols_op(A2)
@@ -139,6 +158,16 @@ def grouped_mlp_fwd(xp, split, w1, w2, pp, precision="bf16", exact=False,
         yp[rs] = m.store(a2op @ W2.T)
         xpw[rs] = m.group_cols_op(xp[rs])
         r0 += n
+    if m.fp8:
+        a2q = m.tensor_op(a2pre)
+        r0 = 0
+        for e, n in enumerate(split):
+            rs = slice(r0, r0 + n)
+            r0 += n
+            if n == 0 or (experts is not None and e not in experts):
+                continue
+            yp[rs] = m.store(a2q[rs] @ m.tensor_op(w2[e]).T)
+        a2s, a2w, xpw = a2q, a2q, xq
     return {"yp": yp, "a1": a1s, "a2": a2s, "a2_w": a2w, "xp_w": xpw}
 
 
@@ -157,6 +186,9 @@ def grouped_mlp_bwd(dyp, xp, split, w1, w2, pp, saved, precision="bf16", exact=F
     dpp = torch.zeros(A, dtype=m.acc)
     dw1 = [torch.zeros((2 * I, H), dtype=out_dt) for _ in range(E)]
     dw2 = [torch.zeros((H, I), dtype=out_dt) for _ in range(E)]
+    if m.fp8:
+        dyq = m.tensor_op(dyp)
+        da1pre = torch.zeros((A, 2 * I), dtype=torch.bfloat16)
     r0 = 0
     for e, n in enumerate(split):
         if n == 0:
@@ -165,9 +197,10 @@ def grouped_mlp_bwd(dyp, xp, split, w1, w2, pp, saved, precision="bf16", exact=F
             r0 += n
             continue
         rs = slice(r0, r0 + n)
-        dY = m.rows_op(dyp[rs])
-        dA2 = dY @ m.cols_op(w2[e])
-        dw2[e] = m.store(m.group_cols_op(dyp[rs]).T @ saved["a2_w"][rs].to(m.acc))
+        dY = dyq[rs] if m.fp8 else m.rows_op(dyp[rs])
+        dA2 = dY @ (m.tensor_op(w2[e]) if m.fp8 else m.cols_op(w2[e]))
+        dYw = dY if m.fp8 else m.group_cols_op(dyp[rs])
+        dw2[e] = m.store(dYw.T @ saved["a2_w"][rs].to(m.acc))
         a1 = saved["a1"][rs].to(m.acc)
         g, u = a1[:, :I], a1[:, I:]
         s, sig = _silu(g), _sigmoid(g)
@@ -176,6 +209,10 @@ def grouped_mlp_bwd(dyp, xp, split, w1, w2, pp, saved, precision="bf16", exact=F
         du = dA2 * p * s
         dpp[rs] = (dA2 * s * u).sum(dim=1)
         dA1 = torch.cat([dg, du], dim=1)
+        if m.fp8:                      # cast after every expert's dA1 exists
+            da1pre[rs] = dA1.to(torch.bfloat16)
+            r0 += n
+            continue
         if m.mx:
             dA1op = m.rows_op(dA1)
             dA1w = m.group_cols_op(dA1)
@@ -185,6 +222,16 @@ def grouped_mlp_bwd(dyp, xp, split, w1, w2, pp, saved, precision="bf16", exact=F
         dxp[rs] = m.store(dA1op @ m.cols_op(w1[e]))
         dw1[e] = m.store(dA1w.T @ saved["xp_w"][rs].to(m.acc))
         r0 += n
+    if m.fp8:
+        da1q = m.tensor_op(da1pre)
+        r0 = 0
+        for e, n in enumerate(split):
+            rs = slice(r0, r0 + n)
+            r0 += n
+            if n == 0 or (experts is not None and e not in experts):
+                continue
+            dxp[rs] = m.store(da1q[rs] @ m.tensor_op(w1[e]))
+            dw1[e] = m.store(da1q[rs].T @ saved["xp_w"][rs].to(m.acc))
     return {"dxp": dxp, "dw1": dw1, "dw2": dw2, "dpp": dpp.to(torch.float32) if not exact else dpp}
 
 
@@ -197,7 +244,9 @@ def layer_step(logits, x, w1, w2, dy, k, precision="bf16", exact=False,
     experts: compute the expert MLPs of these experts only (the rows of the
     others stay zero; every value of the chosen experts' rows and weights, and
     of the tokens routed only to them, is the full step's).  fast_quant: the
-    vectorized quantizers (same values)."""
+    vectorized quantizers (same values).  FP8 mode takes no ``experts``: its
+    per-tensor scales of A2 and dA1 depend on every expert's values."""
+    assert not (precision == "fp8" and experts is not None)
     r = _route.route(logits, k, softmax_all, np.float64 if exact else np.float32)
     xp = _route.permute(x, r["src_token"])
     pp = _route.permute_probs(r["topk_prob"], r["dest_row"])

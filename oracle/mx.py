@@ -28,6 +28,9 @@ Layouts:
   C * (P_0 + ... + P_{g-1}) / 32.  The contraction axis of the weight-gradient
   GEMMs (tokens) is then the contiguous one.
 
+Per-tensor FP8 (quantize_tensor / qdq_tensor, at the end): the same element
+and scale encoding with the whole tensor as the one block.
+
 Parity: pinned by brute force (nearest of all finite codes), by torch's own
 float8_e4m3fn conversion over every bf16 bit pattern, by the closed-form scale
 values, and by the round-trip and power-of-two-shift invariants (tests).
@@ -254,3 +257,45 @@ def qdq_cols_grouped_fast(x, sizes) -> torch.Tensor:
 def dequantize_rows_bf16(codes, scales) -> torch.Tensor:
     """Rowwise dequantization to bf16: exact fp32 value, then RNE to bf16."""
     return torch.from_numpy(dequantize_rows(codes, scales).astype(np.float32)).to(torch.bfloat16)
+
+
+# ---------------------------------------------------------------- per-tensor FP8
+# [BioNeMo, bottleneck section: FP8 and MXFP8 differ in the granularity of the
+# scaling, MXFP8 giving every 32 consecutive values their own scale.]  Reading
+# taken: per-tensor FP8 is the same encoding with the whole tensor as the one
+# block -- one power-of-two scale chosen by the block rule above from the
+# tensor's amax (current scaling: the amax of the values being cast), E4M3
+# elements rounded to nearest even.  A tensor's transposed copy (the other
+# GEMM orientation) uses the same scale, so it holds the same values.
+
+def quantize_tensor(x):
+    """Per-tensor FP8: (codes u8 of x's shape, scale byte S) with S from the
+    amax of the whole tensor."""
+    v = _as_f64(x)
+    amax = float(np.max(np.abs(v))) if v.size else 0.0
+    S = int(block_scale_exponent(np.array(amax)))
+    y = np.abs(v) * np.exp2(127.0 - S)        # exact power-of-two scaling
+    mag = e4m3_encode_magnitude(y)
+    codes = (mag | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+    return codes, S
+
+
+def dequantize_tensor(codes, S: int) -> np.ndarray:
+    """float64 values decode(code) * 2^(S - 127) (exact)."""
+    return e4m3_decode(codes) * np.exp2(float(S) - 127.0)
+
+
+def qdq_tensor(x) -> torch.Tensor:
+    """dequant(quantize_tensor(x)) as an fp32 tensor (exact values)."""
+    c, S = quantize_tensor(x)
+    return torch.from_numpy(dequantize_tensor(c, S).astype(np.float32))
+
+
+def qdq_tensor_fast(x) -> torch.Tensor:
+    """Same values as qdq_tensor(x), vectorized in torch float32: the same
+    scale rule, the exact power-of-two unscale, torch's float8_e4m3fn cast."""
+    v = x.detach().to(torch.float32)
+    amax = float(v.abs().max()) if v.numel() else 0.0
+    sh = int(block_scale_exponent(np.array(amax))) - 127
+    q = torch.ldexp(v, torch.tensor(float(-sh))).to(torch.float8_e4m3fn).to(torch.float32)
+    return torch.ldexp(q, torch.tensor(float(sh)))

@@ -130,7 +130,7 @@ def test_finite_differences():
             assert abs(num - float(r["bwd"]["dw2"][e][a, b])) < 1e-6 * max(1, abs(num))
 
 
-@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8", "fp8"])
 def test_empty_expert(precision):
     c = _case(T=40, H=64, I=64, E=4, seed=41)
     c["logits"][:, 2] = -100.0           # expert 2 never picked
@@ -144,7 +144,7 @@ def test_empty_expert(precision):
     assert torch.equal(r["y"], r2["y"])
 
 
-@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8", "fp8"])
 def test_prob_scaling_is_exact(precision):
     c = _case(T=32, H=64, I=64, E=3, seed=51)
     r = route.route(c["logits"], 2)
@@ -206,3 +206,50 @@ def test_fast_quant_and_expert_subset_give_the_same_values():
     assert both.any()
     assert torch.equal(sub["y"][both], ref["y"][both])
     assert np.array_equal(np.asarray(sub["dlogits"])[both], np.asarray(ref["dlogits"])[both])
+
+
+def _on_fp8_grid(t, rng):
+    """Round a tensor to values per-tensor FP8 represents exactly."""
+    return mx.qdq_tensor(t).to(torch.bfloat16)
+
+
+def test_fp8_equals_bf16_on_representable_gate_up():
+    """Operands already on the per-tensor E4M3 grid: the FP8 gate_up GEMM is
+    the BF16 one (the cast is the identity on them)."""
+    rng = np.random.default_rng(91)
+    c = _case(T=48, H=64, I=64, E=2, seed=92)
+    c["x"] = _on_fp8_grid(c["x"], rng)
+    c["w1"] = [_on_fp8_grid(w, rng) for w in c["w1"]]
+    assert torch.equal(mx.qdq_tensor(c["x"]), c["x"].float())
+    rb = mlp.layer_step(c["logits"], c["x"], c["w1"], c["w2"], c["dy"], 2, "bf16", with_backward=False)
+    rf = mlp.layer_step(c["logits"], c["x"], c["w1"], c["w2"], c["dy"], 2, "fp8", with_backward=False)
+    assert torch.equal(rb["fwd"]["a1"], rf["fwd"]["a1"])
+
+
+def test_fp8_close_to_bf16_and_coarser_than_mx():
+    """Per-tensor scaling loses more than 32-value blocks on data whose rows
+    span many binades, and stays near BF16 on plain Gaussian data."""
+    c = _case(T=64, H=64, I=128, E=4, seed=71)
+    rb = mlp.layer_step(c["logits"], c["x"], c["w1"], c["w2"], c["dy"], 2, "bf16")
+    rf = mlp.layer_step(c["logits"], c["x"], c["w1"], c["w2"], c["dy"], 2, "fp8")
+    for key in ("y", "dx"):
+        rel = (rf[key].float() - rb[key].float()).norm() / rb[key].float().norm()
+        assert 0 < rel < 0.15, (key, rel)
+    rng = np.random.default_rng(93)
+    x = torch.from_numpy((rng.standard_normal((64, 256)) * np.exp2(rng.uniform(-10, 10, (64, 1))))
+                         .astype(np.float32)).to(torch.bfloat16)
+    def row_rel(q):
+        return ((q - x.float()).norm(dim=1) / x.float().norm(dim=1)).mean()
+    assert row_rel(mx.qdq_rows(x)) < 0.05 < row_rel(mx.qdq_tensor(x))
+
+
+def test_fp8_transposed_operands_carry_the_same_values():
+    """The weight-gradient operands in FP8 mode are the transposed copies of
+    the same per-tensor casts (one scale per tensor, any orientation)."""
+    c = _case(T=40, H=64, I=64, E=3, seed=94)
+    r = route.route(c["logits"], 2)
+    xp = route.permute(c["x"], r["src_token"])
+    pp = route.permute_probs(r["topk_prob"], r["dest_row"])
+    f = mlp.grouped_mlp_fwd(xp, r["split_sizes"], c["w1"], c["w2"], pp, "fp8")
+    assert torch.equal(f["xp_w"], mx.qdq_tensor(xp))
+    assert torch.equal(f["a2_w"], f["a2"])

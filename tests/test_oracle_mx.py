@@ -274,3 +274,47 @@ def test_fast_cols_grouped_equals_reference():
     v = (rng.standard_normal((sum(sizes), 64)) * np.exp2(rng.integers(-6, 6, size=(1, 64)))).astype(np.float32)
     x = torch.from_numpy(v).to(torch.bfloat16)
     assert torch.equal(mx.qdq_cols_grouped_fast(x, sizes), mx.qdq_cols_grouped(x, sizes))
+
+
+# ---------------------------------------------------------------- per-tensor FP8
+
+def test_tensor_quant_equals_block_quant_when_blocks_share_amax():
+    """A tensor whose every 32-value block holds the tensor's amax: the
+    per-tensor cast is the (pinned) block cast with all scales equal."""
+    rng = np.random.default_rng(101)
+    x = rng.standard_normal((48, 128)).astype(np.float32)
+    M = float(np.abs(x).max()) * 1.5
+    x.reshape(48, 4, 32)[:, :, 5] = M * rng.choice([-1.0, 1.0], (48, 4))
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    c, S = mx.quantize_tensor(xb)
+    rc, rs = mx.quantize_rows(xb)
+    assert np.all(rs == S)
+    assert np.array_equal(c, rc)
+
+
+@pytest.mark.parametrize("amax,S", [(1.0, 119), (448.0, 127), (449.0, 128), (1.75, 119),
+                                    (1.76, 120), (65536.0, 135), (0.0, 0)])
+def test_tensor_scale_closed_form(amax, S):
+    x = torch.tensor([[amax, -amax / 4, 0.0]], dtype=torch.float32)
+    assert mx.quantize_tensor(x)[1] == S
+
+
+def test_tensor_quant_shift_invariance_and_roundtrip():
+    rng = np.random.default_rng(102)
+    x = torch.from_numpy(rng.standard_normal((16, 64)).astype(np.float32)).to(torch.bfloat16)
+    c0, S0 = mx.quantize_tensor(x)
+    for n in (-20, -3, 5, 30):
+        c, S = mx.quantize_tensor(x.float() * 2.0 ** n)
+        assert S == S0 + n and np.array_equal(c, c0)
+    q = mx.qdq_tensor(x)
+    assert torch.equal(mx.qdq_tensor(q), q)
+
+
+def test_tensor_fast_equals_reference_all_bf16_patterns():
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    v = bits.view(torch.bfloat16)
+    v = v[torch.isfinite(v.float())]
+    # tensors of neighbouring magnitudes (the cast sees one scale per tensor)
+    v = v[v.float().abs().argsort()]
+    for chunk in v.split(2048):
+        assert torch.equal(mx.qdq_tensor(chunk[None, :]), mx.qdq_tensor_fast(chunk[None, :]))
