@@ -1,6 +1,6 @@
 """Benchmark of the grouped MoE expert-MLP layer step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--precision mxfp8|bf16|both]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--precision mxfp8|bf16|fp8|all]
                     [--no-cpu] [--workload mixtral|skewed|tiny]
 
 One step = the whole hot path on one batch: route, permute, grouped MLP
@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"mxfp8": 5000.0, "bf16": 2500.0}   # MI355X dense MFMA (published)
+PEAK_TFLOPS = {"mxfp8": 5000.0, "fp8": 5000.0, "bf16": 2500.0}   # MI355X dense MFMA (published)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--precision", default="both", choices=["mxfp8", "bf16", "both"])
+    ap.add_argument("--precision", default="all", choices=["mxfp8", "bf16", "fp8", "all"])
     ap.add_argument("--workload", default="mixtral", choices=["mixtral", "skewed", "tiny"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
@@ -75,6 +75,12 @@ def kernel_work(name: str, T: int, H: int, I: int, E: int, k: int):
         "gemm_mx_gateup_dgrad": (2 * A * 2 * I * H, 0),
         "gemm_bf16_gateup_dgrad": (2 * A * 2 * I * H, 0),
         "gemm_mx_gateup_wgrad": (2 * 2 * I * H * A, 0),
+        "gemm_fp8_gateup_fwd_swiglu": (2 * A * 2 * I * H, 0),
+        "gemm_fp8_down_fwd": (2 * A * H * I, 0),
+        "gemm_fp8_down_dgrad_swiglu_bwd": (2 * A * I * H, 0),
+        "gemm_fp8_down_wgrad": (2 * H * I * A, 0),
+        "gemm_fp8_gateup_dgrad": (2 * A * 2 * I * H, 0),
+        "gemm_fp8_gateup_wgrad": (2 * 2 * I * H * A, 0),
         "gemm_bf16_gateup_wgrad": (2 * 2 * I * H * A, 0),
         "route_topk": (0, T * E * 4 + A * 12),
         "route_scan": (0, 0),
@@ -87,6 +93,14 @@ def kernel_work(name: str, T: int, H: int, I: int, E: int, k: int):
         "mx_quant_dyp": (0, A * H * (2 + 2 * mx)),
         "mx_quant_w1": (0, E * 2 * I * H * (2 + 2 * mx)),
         "mx_quant_w2": (0, E * H * I * (2 + 2 * mx)),
+        # per-tensor FP8: amax passes read the bf16 tensor; casts as the MXFP8 ones
+        "fp8_amax_xp": (0, A * H * 2), "fp8_amax_dyp": (0, A * H * 2),
+        "fp8_amax_w1": (0, E * 2 * I * H * 2), "fp8_amax_w2": (0, E * H * I * 2),
+        "fp8_amax_a2": (0, A * I * 2), "fp8_amax_da1": (0, A * 2 * I * 2),
+        "fp8_quant_xp": (0, A * H * (2 + 2 * mx)), "fp8_quant_dyp": (0, A * H * (2 + 2 * mx)),
+        "fp8_quant_w1": (0, E * 2 * I * H * (2 + 2 * mx)),
+        "fp8_quant_w2": (0, E * H * I * (2 + 2 * mx)),
+        "fp8_quant_a2": (0, A * I * (2 + 2 * mx)), "fp8_quant_da1": (0, A * 2 * I * (2 + 2 * mx)),
         "mx_quant_rows_xp": (0, A * H * (2 + mx)),
         "mx_quant_cols_xp": (0, A * H * (2 + mx)),
         "mx_quant_rows_dyp": (0, A * H * (2 + mx)),
@@ -123,7 +137,7 @@ def run_gpu(args, prec_name, inp_dev, shape):
     import mxfp8_block_scaled_top_amd as moe
     from mxfp8_block_scaled_top_amd.layer import LayerBuffers, layer_step
 
-    prec = moe.MOE_MXFP8 if prec_name == "mxfp8" else moe.MOE_BF16
+    prec = {"mxfp8": moe.MOE_MXFP8, "fp8": moe.MOE_FP8, "bf16": moe.MOE_BF16}[prec_name]
     T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
     bufs = LayerBuffers(T, H, I, E, k, prec, "cuda")
 
@@ -348,7 +362,7 @@ def main():
            for n, v in inp.items()}
     torch.cuda.synchronize()
 
-    precs = ["mxfp8", "bf16"] if args.precision == "both" else [args.precision]
+    precs = ["mxfp8", "bf16", "fp8"] if args.precision == "all" else [args.precision]
     res = {}
     for p in precs:
         res[p] = run_gpu(args, p, dev, shape)
@@ -368,7 +382,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3" if head == "mxfp8" else "bf16",
+        "dtype": "bf16" if head == "bf16" else "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": f"{shape.name} layer fwd+bwd, {head}", "T": shape.T, "H": shape.H,
                    "I": shape.I, "E": shape.E, "k": shape.k, "precision": head},

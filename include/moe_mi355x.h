@@ -71,7 +71,8 @@ typedef enum moe_status {
 
 typedef enum moe_precision {
     MOE_BF16 = 0,             /* BF16 operands, fp32 accumulation                 */
-    MOE_MXFP8 = 1             /* E4M3 operands, E8M0 scale per 32 K-values        */
+    MOE_MXFP8 = 1,            /* E4M3 operands, E8M0 scale per 32 K-values        */
+    MOE_FP8 = 2               /* E4M3 operands, one power-of-two scale per tensor */
 } moe_precision;
 
 /* moe_route flags */
@@ -311,8 +312,16 @@ typedef struct moe_saved {
  * the gate_up GEMM's epilogue), and also saves the columnwise MXFP8 of xp and
  * A2 for the weight gradients (and of W1 and W2 for the data gradients, when
  * moe_saved holds their buffers).
+ * FP8 mode [BioNeMo, bottleneck section: FP8 differs from MXFP8 in the
+ * scaling granularity] casts the same operands with one scale per tensor:
+ * xp, each W1_e and W2_e, and A2, each from the tensor's own amax (current
+ * scaling; the scale rule of an MXFP8 block applied to the whole tensor).
+ * A2 is written in bf16 by the gate_up epilogue and cast once its amax is
+ * known.  The saved buffers and their layouts are those of MXFP8 mode (every
+ * block scale of a tensor holds the tensor's scale); the backward must be
+ * called with the same precision.
  *
- * precision    MOE_BF16 or MOE_MXFP8.
+ * precision    MOE_BF16, MOE_MXFP8 or MOE_FP8.
  * E            experts, 1..64.   H, I: hidden and intermediate sizes,
  *              multiples of 128.
  * rows         T*k, 0 <= rows <= INT32_MAX, with rows * max(H, 2I) * 2 and
@@ -343,7 +352,9 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
  *   dg = dA2 p u sig (1 + g (1 - sig)),  du = dA2 p s,  dprob = sum_i dA2 s u
  *   dA1 = [dg, du];  dxp_e = dA1 W1_e;  dW1_e = dA1^T xp_e
  * Experts with no rows get exact zeros in dW1_e and dW2_e.  MXFP8 mode
- * quantizes every GEMM operand along that GEMM's contraction axis.
+ * quantizes every GEMM operand along that GEMM's contraction axis; FP8 mode
+ * casts dyp, the weights (when not saved) and dA1 with one scale per tensor,
+ * dA1 after its bf16 materialization.
  *
  * dyp          bf16 [rows, H] (moe_permute of the upstream gradient).
  * xp, split_sizes, w_gate_up, w_down, prob_perm, saved: as in the forward.

@@ -20,7 +20,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(_PKG, "_lib", "libmoe_mi355x.so")
 
-MOE_BF16, MOE_MXFP8 = 0, 1
+MOE_BF16, MOE_MXFP8, MOE_FP8 = 0, 1, 2
 MOE_ROUTE_RENORM, MOE_ROUTE_SOFTMAX_ALL = 0, 1
 MOE_OP_ROUTE, MOE_OP_MLP_FWD, MOE_OP_MLP_BWD, MOE_OP_ROUTER_FWD, MOE_OP_ROUTER_BWD = 0, 1, 2, 3, 4
 MAX_EXPERTS = 64

@@ -454,7 +454,7 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
                 a1g[b] = pack8_bf16(gt);
                 a1u[b] = pack8_bf16(up);
             }
-            if (DT == DT_BF16) {
+            if (DT != DT_MX) {          // bf16 A2 (BF16, and FP8: cast later)
                 u32x4* o = (u32x4*)(g.act + gr * I + j0);
 #pragma unroll
                 for (int b = 0; b < 4; ++b) o[b] = pack8_bf16(a2 + 8 * b);
@@ -503,7 +503,7 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
     const bool slab = jw < I;                              // I % 128 == 0: all or nothing
     const int row = lane >> 1, h = lane & 1;
     float part = 0.f;
-    if (DT == DT_BF16) {
+    if (DT != DT_MX) {
 #pragma unroll 1
         for (int blk = 0; blk < 2; ++blk) {
             const int cb = 64 * h + 32 * blk;               // staged column of the block
@@ -685,7 +685,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
             mb.k_valid = g.K;
             mb.mn_valid = g.N - tl.n0;
         }
-        if (DT == DT_MX) {
+        if (DT != DT_BF16) {
             nblk = g.K / 32;
             sbase_a = g.a_scale;
             soff_a = r4 < ka.rows_valid ? (uint32_t)(tl.row0 + tl.m0 + r4) : kOob;
@@ -696,7 +696,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
             sld_b = (uint32_t)kb.rows_valid;
         }
     } else {
-        kext = DT == DT_MX ? tl.pad_e : tl.rows_e;
+        kext = DT != DT_BF16 ? tl.pad_e : tl.rows_e;
         if (DT == DT_BF16) {
             ma.base = (const uint8_t*)g.a + (tl.row0 * g.lda + tl.m0) * 2;
             ma.stride = g.lda * 2;
@@ -741,7 +741,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     // number (DMA A: 4, DMA B: 4, MXFP8 scales: 1) so that "wait until at
     // most two batches are outstanding" is a fixed vmcnt.  Steps past the end
     // read zeros into stages that are never consumed.
-    constexpr int kBatch = 8 + (DT == DT_MX ? 1 : 0);
+    constexpr int kBatch = 8 + (DT != DT_BF16 ? 1 : 0);
     constexpr int kWait2 = 2 * kBatch;                           // vmcnt(2 batches)
     const i32x4 rs_a = make_rsrc(LA == L_KMAJ ? (const void*)ka.base : (const void*)ma.base);
     const i32x4 rs_b = make_rsrc(LB == L_KMAJ ? (const void*)kb.base : (const void*)mb.base);
@@ -759,7 +759,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         else dma_mnop(ma, rs_a, kt * 32, base);
         if (LB == L_KMAJ) dma_kop(kb, rs_b, kt * kRowB, base + kTileB);
         else dma_mnop(mb, rs_b, kt * 32, base + kTileB);
-        if (DT == DT_MX)
+        if (DT != DT_BF16)
             dma_scales(rs_sa, rs_sb, soff_a, soff_b, sld_a, sld_b, kt, nblk, ssc[st]);
     };
 
@@ -949,6 +949,10 @@ static hipError_t run(const GemmArgs& g, hipStream_t s) {
 }
 
 hipError_t launch_gemm(int dtype, int use, const GemmArgs& g, hipStream_t s) {
+    // FP8 (per-tensor scales, stored as uniform block scales) differs from
+    // MXFP8 only where an epilogue produces the next GEMM's operand: there it
+    // writes bf16, cast once the tensor's amax is known
+    if (dtype == DT_FP8 && use != U_GATEUP_FWD && use != U_DOWN_DGRAD) dtype = DT_MX;
 #define MOE_GEMM_CASE(DT, USE, LA, LB, GRP, EPI) \
     if (dtype == DT && use == USE) return run<DT, LA, LB, GRP, EPI, USE>(g, s);
     // bf16: the backward reads W1, W2 and both weight-gradient operands in
@@ -966,6 +970,8 @@ hipError_t launch_gemm(int dtype, int use, const GemmArgs& g, hipStream_t s) {
     MOE_GEMM_CASE(DT_MX, U_DOWN_WGRAD, L_KMAJ, L_KMAJ, G_K, EPI_STORE)
     MOE_GEMM_CASE(DT_MX, U_GATEUP_DGRAD, L_KMAJ, L_KMAJ, G_M, EPI_STORE)
     MOE_GEMM_CASE(DT_MX, U_GATEUP_WGRAD, L_KMAJ, L_KMAJ, G_K, EPI_STORE)
+    MOE_GEMM_CASE(DT_FP8, U_GATEUP_FWD, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_FWD)
+    MOE_GEMM_CASE(DT_FP8, U_DOWN_DGRAD, L_KMAJ, L_KMAJ, G_M, EPI_SWIGLU_BWD)
 #undef MOE_GEMM_CASE
     return hipErrorInvalidValue;
 }

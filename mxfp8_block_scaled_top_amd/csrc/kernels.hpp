@@ -51,7 +51,14 @@ hipError_t launch_quant(const MatTable& src, int nmat, const int32_t* sizes, int
                         int64_t rows, int64_t cols, const MatTable* rcodes,
                         const MatTable* rscales, bool rscales_t, const MatTable* ccodes,
                         const MatTable* cscales, bool cscales_t, hipStream_t s,
-                        const char* name);
+                        const char* name, const float* fixed_amax = nullptr);
+// Per-tensor FP8: fixed_amax (device, one float per matrix) replaces the block
+// maxima, so every block of matrix m gets the scale of amax[m].
+// amax[m] = max |x| over matrix m's n values (n a multiple of 8); ws holds
+// amax_workspace_bytes(nmat) bytes.
+size_t amax_workspace_bytes(int nmat);
+hipError_t launch_amax(const MatTable& src, int nmat, int64_t n, void* ws, float* amax,
+                       hipStream_t s, const char* name);
 hipError_t launch_quant_rows(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, int64_t rows, int64_t cols, hipStream_t s,
                              const char* name = "mx_quant_rows", bool scales_t = false);

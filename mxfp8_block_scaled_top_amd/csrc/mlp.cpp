@@ -48,13 +48,17 @@ size_t colwise_codes(int64_t rows, int64_t cols, int E) {
 
 struct FwdWs {
     uint8_t *xq, *xq_s, *w1q, *w1q_s, *w2q, *w2q_s, *a2q, *a2q_s;
+    // FP8: bf16 A2 before its cast, the tensor maxima (xp, W1_e, W2_e, A2) and
+    // the amax reduction's partials
+    uint8_t *a2bf, *amax_ws;
+    float* amax;
     size_t bytes;
 };
 
 FwdWs carve_fwd(void* base, int64_t rows, int H, int I, int E, int precision) {
     Carve c(base);
     FwdWs w{};
-    if (precision == MOE_MXFP8) {
+    if (precision != MOE_BF16) {
         w.xq = c.take((size_t)rows * H);
         w.xq_s = c.take((size_t)rows * H / 32);
         w.w1q = c.take((size_t)E * 2 * I * H);
@@ -64,13 +68,20 @@ FwdWs carve_fwd(void* base, int64_t rows, int H, int I, int E, int precision) {
         w.a2q = c.take((size_t)rows * I);
         w.a2q_s = c.take((size_t)rows * I / 32);
     }
+    if (precision == MOE_FP8) {
+        w.a2bf = c.take((size_t)rows * I * 2);
+        w.amax = (float*)c.take((size_t)(2 * E + 2) * sizeof(float));
+        w.amax_ws = c.take(amax_workspace_bytes(E));
+    }
     c.take(256);
     w.bytes = c.off;
     return w;
 }
 
 struct BwdWs {
-    uint8_t *da1;           // bf16 [rows, 2I] (BF16 mode)
+    uint8_t *da1;           // bf16 [rows, 2I] (BF16 mode; FP8: before its cast)
+    float* amax;            // FP8: maxima of dYp, W2_e, W1_e, dA1
+    uint8_t* amax_ws;
     uint8_t *dyq, *dyq_s;   // rowwise dYp
     uint8_t *dyc, *dyc_s;   // grouped columnwise dYp
     uint8_t *w2c, *w2c_s;   // W2 quantized along H: [E][I, H]
@@ -103,6 +114,11 @@ BwdWs carve_bwd(void* base, int64_t rows, int H, int I, int E, int precision) {
         size_t ci = colwise_codes(rows, 2 * (int64_t)I, E);
         w.da1c = c.take(ci);
         w.da1c_s = c.take(ci / 32);
+    }
+    if (precision == MOE_FP8) {
+        w.da1 = c.take((size_t)rows * 2 * I * 2);
+        w.amax = (float*)c.take((size_t)(2 * E + 2) * sizeof(float));
+        w.amax_ws = c.take(amax_workspace_bytes(E));
     }
     c.take(256);
     w.bytes = c.off;
@@ -142,7 +158,8 @@ WeightCols weight_cols(const moe_saved* s, int E, int H, int I) {
 }
 
 int check_common(int precision, int E, int H, int I, int64_t rows) {
-    if (precision != MOE_BF16 && precision != MOE_MXFP8) return MOE_ERR_ARG;
+    if (precision != MOE_BF16 && precision != MOE_MXFP8 && precision != MOE_FP8)
+        return MOE_ERR_ARG;
     if (E < 1 || E > kMaxExperts) return MOE_ERR_SHAPE;
     if (H < 128 || I < 128 || (H % 128) || (I % 128)) return MOE_ERR_SHAPE;
     if (rows < 0 || rows > INT32_MAX) return MOE_ERR_SHAPE;
@@ -188,8 +205,8 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     if (rows > 0) {
         if (!xp || !prob_perm || !yp || !saved->a1) return MOE_ERR_NULL;
         if (precision == MOE_BF16 && !saved->a2) return MOE_ERR_NULL;
-        if (precision == MOE_MXFP8 && (!saved->a2_col_codes || !saved->a2_col_scales ||
-                                       !saved->xp_col_codes || !saved->xp_col_scales))
+        if (precision != MOE_BF16 && (!saved->a2_col_codes || !saved->a2_col_scales ||
+                                      !saved->xp_col_codes || !saved->xp_col_scales))
             return MOE_ERR_NULL;
     }
     if ((st = check_weight_cols(saved)) != MOE_OK) return st;
@@ -235,15 +252,18 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     }
     // MXFP8: quantize operands along their contraction axis.  xp: rowwise for
     // gate_up, grouped columnwise (saved) for the gate_up weight gradient, from
-    // one read.
+    // one read.  FP8: the same casts with one scale per tensor, from its amax.
+    const bool fp8 = precision == MOE_FP8;
+    const int dt8 = fp8 ? DT_FP8 : DT_MX;
     MatTable src{}, cd{}, sc{}, ccd{}, csc{};
     src.p[0] = xp;
     cd.p[0] = w.xq;
     sc.p[0] = w.xq_s;
     ccd.p[0] = saved->xp_col_codes;
     csc.p[0] = saved->xp_col_scales;
+    if (fp8) MOE_TRY(launch_amax(src, 1, rows * H, w.amax_ws, w.amax, stream, "fp8_amax_xp"));
     MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, H, &cd, &sc, true, &ccd, &csc, true, stream,
-                         "mx_quant_xp"));
+                         fp8 ? "fp8_quant_xp" : "mx_quant_xp", fp8 ? w.amax : nullptr));
     // weights: rowwise (along H for W1, along I for W2) for these GEMMs; with
     // the saved columnwise buffers, also the backward's copies from the same read
     MatTable w1t{}, w1c{}, w1s{}, w2t{}, w2c{}, w2s{};
@@ -255,16 +275,26 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
         w2c.p[e] = w.w2q + (size_t)e * H * I;
         w2s.p[e] = w.w2q_s + (size_t)e * H * I / 32;
     }
+    const float* aw1 = fp8 ? w.amax + 1 : nullptr;       // per-expert tensor maxima
+    const float* aw2 = fp8 ? w.amax + 1 + E : nullptr;
+    if (fp8) {
+        MOE_TRY(launch_amax(w1t, E, 2 * (int64_t)I * H, w.amax_ws, w.amax + 1, stream,
+                            "fp8_amax_w1"));
+        MOE_TRY(launch_amax(w2t, E, (int64_t)H * I, w.amax_ws, w.amax + 1 + E, stream,
+                            "fp8_amax_w2"));
+    }
     if (saved->w_gate_up_col_codes) {
         WeightCols wc = weight_cols(saved, E, H, I);
         MOE_TRY(launch_quant(w1t, E, nullptr, 1, 2 * (int64_t)I, H, &w1c, &w1s, true, &wc.w1c,
-                             &wc.w1s, true, stream, "mx_quant_w1"));
+                             &wc.w1s, true, stream, fp8 ? "fp8_quant_w1" : "mx_quant_w1", aw1));
         MOE_TRY(launch_quant(w2t, E, nullptr, 1, H, I, &w2c, &w2s, true, &wc.w2c, &wc.w2s, true,
-                             stream, "mx_quant_w2"));
+                             stream, fp8 ? "fp8_quant_w2" : "mx_quant_w2", aw2));
     } else {
-        MOE_TRY(launch_quant_rows(w1t, w1c, w1s, E, 2 * (int64_t)I, H, stream, "mx_quant_rows_w1",
-                                  true));
-        MOE_TRY(launch_quant_rows(w2t, w2c, w2s, E, H, I, stream, "mx_quant_rows_w2", true));
+        MOE_TRY(launch_quant(w1t, E, nullptr, 1, 2 * (int64_t)I, H, &w1c, &w1s, true, nullptr,
+                             nullptr, false, stream, fp8 ? "fp8_quant_rows_w1" : "mx_quant_rows_w1",
+                             aw1));
+        MOE_TRY(launch_quant(w2t, E, nullptr, 1, H, I, &w2c, &w2s, true, nullptr, nullptr, false,
+                             stream, fp8 ? "fp8_quant_rows_w2" : "mx_quant_rows_w2", aw2));
     }
 
     g.a = w.xq;
@@ -278,12 +308,28 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     g.N = 2 * I;
     g.K = H;
     g.a1 = saved->a1;
-    g.q_row = w.a2q;
-    g.q_row_s = w.a2q_s;
-    g.q_col = saved->a2_col_codes;
-    g.q_col_s = saved->a2_col_scales;
-    g.name = "gemm_mx_gateup_fwd_swiglu";
-    MOE_TRY(launch_gemm(DT_MX, U_GATEUP_FWD, g, stream));
+    if (fp8) {
+        g.act = (bf16_t*)w.a2bf;
+        g.name = "gemm_fp8_gateup_fwd_swiglu";
+    } else {
+        g.q_row = w.a2q;
+        g.q_row_s = w.a2q_s;
+        g.q_col = saved->a2_col_codes;
+        g.q_col_s = saved->a2_col_scales;
+        g.name = "gemm_mx_gateup_fwd_swiglu";
+    }
+    MOE_TRY(launch_gemm(dt8, U_GATEUP_FWD, g, stream));
+    if (fp8) {   // A2: its amax, then rowwise (down GEMM) and grouped columnwise (saved)
+        src.p[0] = w.a2bf;
+        cd.p[0] = w.a2q;
+        sc.p[0] = w.a2q_s;
+        ccd.p[0] = saved->a2_col_codes;
+        csc.p[0] = saved->a2_col_scales;
+        float* aa2 = w.amax + 2 * E + 1;
+        MOE_TRY(launch_amax(src, 1, rows * I, w.amax_ws, aa2, stream, "fp8_amax_a2"));
+        MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, I, &cd, &sc, true, &ccd, &csc, true,
+                             stream, "fp8_quant_a2", aa2));
+    }
     GemmArgs d{};
     d.split = split_sizes;
     d.E = E;
@@ -301,8 +347,8 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     d.K = I;
     d.c = yp;
     d.ldc = H;
-    d.name = "gemm_mx_down_fwd";
-    MOE_TRY(launch_gemm(DT_MX, U_DOWN_FWD, d, stream));
+    d.name = fp8 ? "gemm_fp8_down_fwd" : "gemm_mx_down_fwd";
+    MOE_TRY(launch_gemm(dt8, U_DOWN_FWD, d, stream));
     return MOE_OK;
 }
 
@@ -322,8 +368,8 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     if (rows > 0) {
         if (!dyp || !xp || !prob_perm || !dxp || !dprob_perm || !saved->a1) return MOE_ERR_NULL;
         if (precision == MOE_BF16 && !saved->a2) return MOE_ERR_NULL;
-        if (precision == MOE_MXFP8 && (!saved->a2_col_codes || !saved->a2_col_scales ||
-                                       !saved->xp_col_codes || !saved->xp_col_scales))
+        if (precision != MOE_BF16 && (!saved->a2_col_codes || !saved->a2_col_scales ||
+                                      !saved->xp_col_codes || !saved->xp_col_scales))
             return MOE_ERR_NULL;
     }
     if ((st = check_weight_cols(saved)) != MOE_OK) return st;
@@ -419,7 +465,9 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         return MOE_OK;
     }
 
-    // ---- MXFP8
+    // ---- MXFP8 and FP8 (per-tensor scales from each tensor's amax)
+    const bool fp8 = precision == MOE_FP8;
+    const int dt8 = fp8 ? DT_FP8 : DT_MX;
     MatTable src{}, cd{}, sc{};
     if (rows > 0) {
         // rowwise for the down dgrad, grouped columnwise for the down wgrad
@@ -429,8 +477,10 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         sc.p[0] = w.dyq_s;
         ccd.p[0] = w.dyc;
         csc.p[0] = w.dyc_s;
+        if (fp8) MOE_TRY(launch_amax(src, 1, rows * H, w.amax_ws, w.amax, stream, "fp8_amax_dyp"));
         MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, H, &cd, &sc, true, &ccd, &csc, true,
-                             stream, "mx_quant_dyp"));
+                             stream, fp8 ? "fp8_quant_dyp" : "mx_quant_dyp",
+                             fp8 ? w.amax : nullptr));
     }
     MatTable w1t{}, w1c{}, w1s{}, w2t{}, w2c{}, w2s{};
     for (int e = 0; e < E; ++e) {
@@ -451,10 +501,20 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     if (rows > 0) {
         if (!saved->w_gate_up_col_codes) {
             // W2 [H, I] along H -> [I, H];  W1 [2I, H] along 2I -> [H, 2I]
-            MOE_TRY(launch_quant_cols(w2t, w2c, w2s, E, nullptr, 1, H, I, stream,
-                                      "mx_quant_cols_w2", true));
-            MOE_TRY(launch_quant_cols(w1t, w1c, w1s, E, nullptr, 1, 2 * (int64_t)I, H, stream,
-                                      "mx_quant_cols_w1", true));
+            const float* aw2 = fp8 ? w.amax + 1 : nullptr;
+            const float* aw1 = fp8 ? w.amax + 1 + E : nullptr;
+            if (fp8) {
+                MOE_TRY(launch_amax(w2t, E, (int64_t)H * I, w.amax_ws, w.amax + 1, stream,
+                                    "fp8_amax_w2"));
+                MOE_TRY(launch_amax(w1t, E, 2 * (int64_t)I * H, w.amax_ws, w.amax + 1 + E,
+                                    stream, "fp8_amax_w1"));
+            }
+            MOE_TRY(launch_quant(w2t, E, nullptr, 1, H, I, nullptr, nullptr, false, &w2c, &w2s,
+                                 true, stream, fp8 ? "fp8_quant_cols_w2" : "mx_quant_cols_w2",
+                                 aw2));
+            MOE_TRY(launch_quant(w1t, E, nullptr, 1, 2 * (int64_t)I, H, nullptr, nullptr, false,
+                                 &w1c, &w1s, true, stream,
+                                 fp8 ? "fp8_quant_cols_w1" : "mx_quant_cols_w1", aw1));
         }
         GemmArgs g{};
         g.split = split_sizes;
@@ -473,14 +533,31 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         g.N = I;
         g.K = H;
         g.a1 = saved->a1;
-        g.q_row = w.da1q;
-        g.q_row_s = w.da1q_s;
-        g.q_col = w.da1c;
-        g.q_col_s = w.da1c_s;
         g.dprob_part = w.part;
-        g.name = "gemm_mx_down_dgrad_swiglu_bwd";
-        MOE_TRY(launch_gemm(DT_MX, U_DOWN_DGRAD, g, stream));
+        if (fp8) {
+            g.act = (bf16_t*)w.da1;
+            g.name = "gemm_fp8_down_dgrad_swiglu_bwd";
+        } else {
+            g.q_row = w.da1q;
+            g.q_row_s = w.da1q_s;
+            g.q_col = w.da1c;
+            g.q_col_s = w.da1c_s;
+            g.name = "gemm_mx_down_dgrad_swiglu_bwd";
+        }
+        MOE_TRY(launch_gemm(dt8, U_DOWN_DGRAD, g, stream));
         MOE_TRY(launch_dprob_reduce(w.part, rows, ntn, dprob_perm, stream));
+        if (fp8) {   // dA1: its amax, then rowwise (gate_up dgrad) and grouped columnwise
+            MatTable ccd{}, csc{};
+            src.p[0] = w.da1;
+            cd.p[0] = w.da1q;
+            sc.p[0] = w.da1q_s;
+            ccd.p[0] = w.da1c;
+            csc.p[0] = w.da1c_s;
+            float* ad = w.amax + 2 * E + 1;
+            MOE_TRY(launch_amax(src, 1, rows * 2 * I, w.amax_ws, ad, stream, "fp8_amax_da1"));
+            MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, 2 * (int64_t)I, &cd, &sc, true,
+                                 &ccd, &csc, true, stream, "fp8_quant_da1", ad));
+        }
     }
     // down wgrad: dW2 [H, I] = dYp^T A2 over grouped columnwise operands
     GemmArgs wg{};
@@ -495,8 +572,8 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     wg.N = I;
     wg.c_tab = dw2;
     wg.ldc = I;
-    wg.name = "gemm_mx_down_wgrad";
-    MOE_TRY(launch_gemm(DT_MX, U_DOWN_WGRAD, wg, stream));
+    wg.name = fp8 ? "gemm_fp8_down_wgrad" : "gemm_mx_down_wgrad";
+    MOE_TRY(launch_gemm(dt8, U_DOWN_WGRAD, wg, stream));
     if (rows > 0) {
         GemmArgs dg{};
         dg.split = split_sizes;
@@ -514,8 +591,8 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         dg.K = 2 * I;
         dg.c = dxp;
         dg.ldc = H;
-        dg.name = "gemm_mx_gateup_dgrad";
-        MOE_TRY(launch_gemm(DT_MX, U_GATEUP_DGRAD, dg, stream));
+        dg.name = fp8 ? "gemm_fp8_gateup_dgrad" : "gemm_mx_gateup_dgrad";
+        MOE_TRY(launch_gemm(dt8, U_GATEUP_DGRAD, dg, stream));
     }
     GemmArgs wg1{};
     wg1.split = split_sizes;
@@ -529,8 +606,8 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     wg1.N = H;
     wg1.c_tab = dw1;
     wg1.ldc = H;
-    wg1.name = "gemm_mx_gateup_wgrad";
-    MOE_TRY(launch_gemm(DT_MX, U_GATEUP_WGRAD, wg1, stream));
+    wg1.name = fp8 ? "gemm_fp8_gateup_wgrad" : "gemm_mx_gateup_wgrad";
+    MOE_TRY(launch_gemm(dt8, U_GATEUP_WGRAD, wg1, stream));
     return MOE_OK;
 }
 

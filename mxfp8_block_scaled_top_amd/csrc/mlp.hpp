@@ -5,7 +5,10 @@
 
 namespace moe {
 
-enum GemmDType { DT_BF16 = 0, DT_MX = 1 };
+// Operand types: BF16; MXFP8 (E4M3 + E8M0 per 32 K-values, epilogues emit the
+// next operand as MXFP8); FP8 (E4M3 with one scale per tensor, stored as
+// uniform block scales, epilogues emit bf16 for a later per-tensor cast).
+enum GemmDType { DT_BF16 = 0, DT_MX = 1, DT_FP8 = 2 };
 enum GemmLayout { L_KMAJ = 0, L_MNMAJ = 1 };   // operand contiguous along K / along M or N
 enum GemmGroup { G_M = 0, G_K = 1 };           // ragged rows (fwd, dgrad) / ragged K (wgrad)
 enum GemmEpi { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };

@@ -113,6 +113,8 @@ struct QuantTileArgs {
     int ngroups;
     int64_t rows, cols;
     int rscales_t, cscales_t;
+    const float* amax;          // per-tensor mode: amax of matrix m (one scale for all
+                                // its blocks, still written to every scale slot)
 };
 
 typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
@@ -125,7 +127,7 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
 // magnitude bits of the two bf16 halves of w
 __device__ __forceinline__ uint32_t abs2(uint32_t w) { return w & 0x7fff7fffu; }
 
-template <bool ROWS, bool COLS>
+template <bool ROWS, bool COLS, bool FIXED>
 __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
     __shared__ int lds[192];
     const int m = blockIdx.z;
@@ -153,6 +155,9 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
             v[j] = __builtin_nontemporal_load((const u32x4*)(in + (j * cols + c0) * 2));
     }
 
+    uint32_t Sfix = 0;
+    if constexpr (FIXED) Sfix = mx_scale_byte(a.amax[m]);
+
     if constexpr (ROWS) {
         uint8_t* rc = (uint8_t*)a.rcodes.p[m] + r0 * cols + c0;
         const int64_t kb = c0 >> 5;
@@ -161,13 +166,16 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
 #pragma unroll
         for (int j = 0; j < kMxBlock; ++j) {
             if (j < valid) {
-                uint32_t mw = pk_max_u16(pk_max_u16(abs2(v[j][0]), abs2(v[j][1])),
-                                         pk_max_u16(abs2(v[j][2]), abs2(v[j][3])));
-                uint32_t am = max(mw & 0xffffu, mw >> 16);
-                // quad_perm [1,0,3,2] then [2,3,0,1]: the 4 lanes of a block
-                am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0xB1, 0xF, 0xF, true));
-                am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0x4E, 0xF, 0xF, true));
-                const uint32_t S = mx_scale_byte(__uint_as_float(am << 16));
+                uint32_t S = Sfix;
+                if constexpr (!FIXED) {
+                    uint32_t mw = pk_max_u16(pk_max_u16(abs2(v[j][0]), abs2(v[j][1])),
+                                             pk_max_u16(abs2(v[j][2]), abs2(v[j][3])));
+                    uint32_t am = max(mw & 0xffffu, mw >> 16);
+                    // quad_perm [1,0,3,2] then [2,3,0,1]: the 4 lanes of a block
+                    am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0xB1, 0xF, 0xF, true));
+                    am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0x4E, 0xF, 0xF, true));
+                    S = mx_scale_byte(__uint_as_float(am << 16));
+                }
                 u32x2 o;
                 o[0] = mx_encode4(lo_bf16(v[j][0]), hi_bf16(v[j][0]), lo_bf16(v[j][1]),
                                   hi_bf16(v[j][1]), S);
@@ -214,7 +222,7 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const uint32_t am = (t & 1) ? (mw[t >> 1] >> 16) : (mw[t >> 1] & 0xffffu);
-            const uint32_t S = mx_scale_byte(__uint_as_float(am << 16));
+            const uint32_t S = FIXED ? Sfix : mx_scale_byte(__uint_as_float(am << 16));
             u32x4 o[2];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {   // rows 4q .. 4q+3
@@ -281,7 +289,69 @@ __global__ __launch_bounds__(256) void dequant_cols_kernel(const uint8_t* __rest
     }
 }
 
+// ---------------------------------------------------------------- per-tensor amax
+// Maximum magnitude of each of nmat bf16 matrices (n values each, n a
+// multiple of 8), in two launches: workgroup partials over 16-byte chunks
+// (magnitudes compared as bf16 bit patterns with the sign cleared), then one
+// workgroup per matrix over its partials.  The maximum does not depend on
+// the order, so the result is exact and deterministic.
+constexpr int kAmaxParts = 512;
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    v = red[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) v = max(v, red[w]);
+    return v;
+}
+
+__global__ __launch_bounds__(256) void amax_partial_kernel(MatTable src, int64_t n,
+                                                           uint32_t* __restrict__ part) {
+    __shared__ uint32_t red[4];
+    const int m = blockIdx.y;
+    const u32x4* p = (const u32x4*)src.p[m];
+    uint32_t mw = 0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n / 8;
+         i += (int64_t)gridDim.x * 256) {
+        const u32x4 v = __builtin_nontemporal_load(p + i);
+        mw = pk_max_u16(mw, pk_max_u16(pk_max_u16(abs2(v[0]), abs2(v[1])),
+                                       pk_max_u16(abs2(v[2]), abs2(v[3]))));
+    }
+    const uint32_t am = block_max_u32(max(mw & 0xffffu, mw >> 16), red);
+    if (threadIdx.x == 0) part[(int64_t)m * gridDim.x + blockIdx.x] = am;
+}
+
+__global__ __launch_bounds__(256) void amax_final_kernel(const uint32_t* __restrict__ part,
+                                                         int nparts, float* __restrict__ amax) {
+    __shared__ uint32_t red[4];
+    const int m = blockIdx.x;
+    uint32_t v = 0;
+    for (int i = threadIdx.x; i < nparts; i += 256) v = max(v, part[(int64_t)m * nparts + i]);
+    v = block_max_u32(v, red);
+    if (threadIdx.x == 0) amax[m] = __uint_as_float(v << 16);
+}
+
 // ---------------------------------------------------------------- launchers
+size_t amax_workspace_bytes(int nmat) { return (size_t)nmat * kAmaxParts * sizeof(uint32_t) + 256; }
+
+hipError_t launch_amax(const MatTable& src, int nmat, int64_t n, void* ws, float* amax,
+                       hipStream_t s, const char* name) {
+    if (nmat == 0) return hipSuccess;
+    int64_t parts = (n / 8 + 255) / 256;
+    if (parts > kAmaxParts) parts = kAmaxParts;
+    if (parts < 1) parts = 1;
+    TraceScope ts(name, s);
+    amax_partial_kernel<<<dim3((unsigned)parts, (unsigned)nmat), 256, 0, s>>>(src, n,
+                                                                            (uint32_t*)ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    amax_final_kernel<<<nmat, 256, 0, s>>>((const uint32_t*)ws, (int)parts, amax);
+    return hipGetLastError();
+}
+
 static unsigned grid_1d(int64_t n, int threads) {
     int64_t b = (n + threads - 1) / threads;
     int64_t cap = 256 * 32;
@@ -298,7 +368,7 @@ hipError_t launch_quant(const MatTable& src, int nmat, const int32_t* sizes, int
                         int64_t rows, int64_t cols, const MatTable* rcodes,
                         const MatTable* rscales, bool rscales_t, const MatTable* ccodes,
                         const MatTable* cscales, bool cscales_t, hipStream_t s,
-                        const char* name) {
+                        const char* name, const float* fixed_amax) {
     if (rows == 0 || cols == 0 || nmat == 0 || (!rcodes && !ccodes)) return hipSuccess;
     QuantTileArgs a{};
     a.src = src;
@@ -310,12 +380,19 @@ hipError_t launch_quant(const MatTable& src, int nmat, const int32_t* sizes, int
     a.cols = cols;
     a.rscales_t = rscales_t ? 1 : 0;
     a.cscales_t = cscales_t ? 1 : 0;
+    a.amax = fixed_amax;
     const int64_t nblk = colwise_block_bound(rows, a.ngroups);
     dim3 grid((unsigned)((cols + 511) / 512), (unsigned)((nblk + 3) / 4), (unsigned)nmat);
     TraceScope ts(name, s);
-    if (rcodes && ccodes) quant_tile_kernel<true, true><<<grid, 256, 0, s>>>(a);
-    else if (rcodes) quant_tile_kernel<true, false><<<grid, 256, 0, s>>>(a);
-    else quant_tile_kernel<false, true><<<grid, 256, 0, s>>>(a);
+    if (fixed_amax) {
+        if (rcodes && ccodes) quant_tile_kernel<true, true, true><<<grid, 256, 0, s>>>(a);
+        else if (rcodes) quant_tile_kernel<true, false, true><<<grid, 256, 0, s>>>(a);
+        else quant_tile_kernel<false, true, true><<<grid, 256, 0, s>>>(a);
+    } else {
+        if (rcodes && ccodes) quant_tile_kernel<true, true, false><<<grid, 256, 0, s>>>(a);
+        else if (rcodes) quant_tile_kernel<true, false, false><<<grid, 256, 0, s>>>(a);
+        else quant_tile_kernel<false, true, false><<<grid, 256, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 

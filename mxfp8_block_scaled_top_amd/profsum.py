@@ -52,7 +52,7 @@ def trace_name(symbol: str) -> str:
     m = re.search(r"gemm_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), (\d+)>", symbol)
     if m:
         dt, use = int(m.group(1)), int(m.group(6))
-        return f"gemm_{'mx' if dt else 'bf16'}_{GEMM_USES[use]}"
+        return f"gemm_{('bf16', 'mx', 'fp8')[dt]}_{GEMM_USES[use]}"
     m = re.search(r"moe::(\w+?)(_kernel)?\(", symbol)
     return m.group(1) if m else symbol[:40]
 

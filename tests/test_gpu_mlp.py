@@ -18,8 +18,10 @@ from tests.helpers import need_gpu, np_, rel_frob, say
 
 pytestmark = pytest.mark.gpu
 
-TOL = {moe.MOE_BF16: 1e-2, moe.MOE_MXFP8: 2e-2}
-PREC = {moe.MOE_BF16: "bf16", moe.MOE_MXFP8: "mxfp8"}
+TOL = {moe.MOE_BF16: 1e-2, moe.MOE_MXFP8: 2e-2, moe.MOE_FP8: 2e-2}
+PREC = {moe.MOE_BF16: "bf16", moe.MOE_MXFP8: "mxfp8", moe.MOE_FP8: "fp8"}
+ALL = [moe.MOE_BF16, moe.MOE_MXFP8, moe.MOE_FP8]
+IDS = ["bf16", "mxfp8", "fp8"]
 
 
 @pytest.fixture(autouse=True)
@@ -50,6 +52,41 @@ def _block_major_to_public(scales, sizes, C):
     return np.concatenate(out) if out else scales[:0]
 
 
+def _grouped_layout(codes, sizes):
+    """Codes [R, C] laid out as the grouped columnwise buffer: each group
+    transposed to [C, P_g], the padding rows 0x00."""
+    out, r0 = [], 0
+    C = codes.shape[1]
+    for n in sizes:
+        n = int(n)
+        p = (n + 31) // 32 * 32
+        blk = np.zeros((C, p), np.uint8)
+        blk[:, :n] = codes[r0:r0 + n].T
+        out.append(blk.reshape(-1))
+        r0 += n
+    return np.concatenate(out) if out else np.zeros(0, np.uint8)
+
+
+def _check_fp8_saved(got, ref, inp):
+    """Per-tensor FP8: the saved columnwise copies of xp and of the weights
+    are the oracle's per-tensor codes transposed, every scale slot the
+    tensor's scale byte."""
+    r = ref["route"]
+    xc, xs = omx.quantize_tensor(ref["xp"])
+    want = _grouped_layout(xc, r["split_sizes"])
+    assert np.array_equal(np_(got["saved"]["xp_col_codes"])[: want.size], want), "xp codes"
+    assert np.all(np_(got["saved"]["xp_col_scales"])[: want.size // 32] == xs), "xp scale"
+    H = inp["x"].shape[1]
+    I = inp["w2"][0].shape[1]
+    for name, ws, n in (("w_gate_up", inp["w1"], 2 * I * H), ("w_down", inp["w2"], H * I)):
+        codes = np_(got["saved"][name + "_col_codes"])
+        scales = np_(got["saved"][name + "_col_scales"])
+        for e, W in enumerate(ws):
+            c, s = omx.quantize_tensor(W)
+            assert np.array_equal(codes[e * n:(e + 1) * n], c.T.reshape(-1)), (name, e)
+            assert np.all(scales[e * n // 32:(e + 1) * n // 32] == s), (name, e)
+
+
 def _layer_compare(inp, k, precision, tag):
     say(f"layer {tag} prec={PREC[precision]} T={inp['x'].shape[0]} H={inp['x'].shape[1]} "
         f"I={inp['w2'][0].shape[1]} E={len(inp['w1'])} k={k}")
@@ -77,6 +114,8 @@ def _layer_compare(inp, k, precision, tag):
     say("  errors: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, bad
+    if precision == moe.MOE_FP8:
+        _check_fp8_saved(got, ref, inp)
     if precision == moe.MOE_MXFP8:
         H = inp["x"].shape[1]
         xc, xs = omx.quantize_cols_grouped(ref["xp"], r["split_sizes"])
@@ -96,14 +135,14 @@ def _layer_compare(inp, k, precision, tag):
     return got, ref
 
 
-@pytest.mark.parametrize("precision", [moe.MOE_BF16, moe.MOE_MXFP8], ids=["bf16", "mxfp8"])
+@pytest.mark.parametrize("precision", ALL, ids=IDS)
 def test_tiny_workload(precision):
     sh = synth.SHAPES["tiny"]
     inp = synth.layer_inputs(sh)
     _layer_compare(inp, sh.k, precision, "tiny")
 
 
-@pytest.mark.parametrize("precision", [moe.MOE_BF16, moe.MOE_MXFP8], ids=["bf16", "mxfp8"])
+@pytest.mark.parametrize("precision", ALL, ids=IDS)
 def test_ragged_tiles(precision):
     # several 256-row tiles per expert, ragged tails, an empty expert, an
     # expert with a single row, N not a multiple of 256
@@ -114,19 +153,20 @@ def test_ragged_tiles(precision):
     _layer_compare(inp, 2, precision, "ragged")
 
 
-@pytest.mark.parametrize("precision", [moe.MOE_BF16, moe.MOE_MXFP8], ids=["bf16", "mxfp8"])
+@pytest.mark.parametrize("precision", ALL, ids=IDS)
 def test_single_expert_dense(precision):
     inp = _inputs(T=300, H=256, I=256, E=1, seed=2)
     _layer_compare(inp, 1, precision, "dense")
 
 
-@pytest.mark.parametrize("precision", [moe.MOE_BF16, moe.MOE_MXFP8], ids=["bf16", "mxfp8"])
+@pytest.mark.parametrize("precision", ALL, ids=IDS)
 def test_many_experts_topk8(precision):
     inp = _inputs(T=512, H=256, I=384, E=64, seed=3)
     _layer_compare(inp, 8, precision, "e64k8")
 
 
-def test_weight_cols_saved_or_quantized_in_backward():
+@pytest.mark.parametrize("precision", [moe.MOE_MXFP8, moe.MOE_FP8], ids=["mxfp8", "fp8"])
+def test_weight_cols_saved_or_quantized_in_backward(precision):
     """The backward reading the forward's columnwise weight copies and the
     backward quantizing the weights itself give the same bytes."""
     T, H, I, E, k = 700, 384, 640, 6, 2
@@ -135,8 +175,8 @@ def test_weight_cols_saved_or_quantized_in_backward():
     res = []
     for wc in (True, False):
         say(f"layer weight_cols={wc}")
-        bufs = LayerBuffers(T, H, I, E, k, moe.MOE_MXFP8, "cuda", weight_cols=wc)
-        a = layer_step(dev["logits"], dev["x"], dev["w1"], dev["w2"], dev["dy"], k, moe.MOE_MXFP8,
+        bufs = LayerBuffers(T, H, I, E, k, precision, "cuda", weight_cols=wc)
+        a = layer_step(dev["logits"], dev["x"], dev["w1"], dev["w2"], dev["dy"], k, precision,
                        bufs=bufs)
         res.append({key: (v.clone() if isinstance(v, torch.Tensor) else [w.clone() for w in v])
                     for key, v in a.items() if key in ("y", "dx", "dpp", "dlogits", "dw1", "dw2")})
@@ -150,7 +190,7 @@ def test_weight_cols_saved_or_quantized_in_backward():
 def test_deterministic_bf16_and_mx():
     inp = _inputs(T=400, H=256, I=256, E=4, seed=4)
     dev = {n: (v.cuda() if isinstance(v, torch.Tensor) else [w.cuda() for w in v]) for n, v in inp.items()}
-    for prec in (moe.MOE_BF16, moe.MOE_MXFP8):
+    for prec in ALL:
         a = layer_step(dev["logits"], dev["x"], dev["w1"], dev["w2"], dev["dy"], 2, prec)
         a = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in a.items()}
         a_dw1 = [w.clone() for w in a["dw1"]]
