@@ -53,7 +53,7 @@ def trace_name(symbol: str) -> str:
     if m:
         dt, use = int(m.group(1)), int(m.group(6))
         return f"gemm_{('bf16', 'mx', 'fp8')[dt]}_{GEMM_USES[use]}"
-    m = re.search(r"moe::(\w+?)(_kernel)?\(", symbol)
+    m = re.search(r"moe::(\w+?)(_kernel)?[<(]", symbol)
     return m.group(1) if m else symbol[:40]
 
 
@@ -85,8 +85,9 @@ def _per_kernel(path: str):
 def gemm_algorithmic_bytes(name: str, T: int, H: int, I: int, E: int, k: int) -> float:
     """Each operand read once and the output written once, per launch."""
     A = T * k
-    mx = name.startswith("gemm_mx")
-    eb = 1 + 1 / 32 if mx else 2                     # operand bytes per element
+    mx = name.startswith("gemm_mx")                  # epilogues emit MXFP8
+    eight = mx or name.startswith("gemm_fp8")         # 8-bit operands
+    eb = 1 + 1 / 32 if eight else 2                  # operand bytes per element
     use = name.split("_", 2)[2]
     if use == "gateup_fwd_swiglu":
         # xp, W1 in; A1 bf16 + A2 (bf16, or MXFP8 rowwise + columnwise) out
