@@ -117,7 +117,20 @@ __device__ bool decode_tile(const GemmArgs& g, int ntn, int mtm, int t, int* sch
     __syncthreads();
     int e;
     int tloc;
-    if ((ntn & 7) == 0) {
+    if (GRP == G_K && (mtm & 7) == 0 && g.M > g.N) {
+        // Weight gradient whose first operand is the larger one (dW1 = dA1^T
+        // Xp: 2I rows against H): XCD x takes the row tiles m = 8m' + x of
+        // every expert, so each XCD reads its own eighth of that operand once
+        // and only the smaller one is read by all XCDs.
+        const int x = blockIdx.x & 7, i = blockIdx.x >> 3, mt8 = mtm >> 3;
+        const int per = mt8 * ntn;
+        e = i / per;
+        if (e >= g.E) return false;
+        tloc = i - e * per;
+        int m8;
+        grouped_order(tloc, mt8, ntn, m8, tl.n_tile);
+        tl.m0 = (m8 * 8 + x) * kGemmBM;
+    } else if ((ntn & 7) == 0) {
         // Expert-synchronous split over the 8 XCDs: XCD x takes the N-tiles
         // n = 8n' + x of every expert, experts in order, so that all XCDs
         // stream the same expert at the same time: the activation rows they
@@ -872,18 +885,29 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
             C = (bf16_t*)g.c_tab.p[tl.e] + (int64_t)tl.m0 * ldc + tl.n0;
             row_lim = g.M - tl.m0;
         }
+        // Each 32-row slice of the wave's 128 x 128 result goes through the
+        // wave's own LDS region (the pipeline has drained), so that a lane
+        // stores 8 neighbouring columns as one 16-byte write (4 rows x 256
+        // bytes per instruction) instead of 2-byte writes column by column.
+        float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
+        const int c8 = (lane & 15) * 8;
+        const int gcol = wn * 128 + c8;             // N is a multiple of 8: all or nothing
 #pragma unroll
-        for (int fi = 0; fi < 4; ++fi)
+        for (int fi = 0; fi < 4; ++fi) {
+            stage_fragments(R, acc[fi][0], acc[fi][1], acc[fi][2], acc[fi][3]);
+            __syncthreads();
 #pragma unroll
-            for (int fj = 0; fj < 4; ++fj) {
-                int col = wn * 128 + fj * 32 + fr;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    int row = wm * 128 + fi * 32 + 4 * hi + 8 * (v >> 2) + (v & 3);
-                    if (row < row_lim && col < col_lim)
-                        C[(int64_t)row * ldc + col] = (bf16_t)f32_to_bf16(acc[fi][fj][v]);
+            for (int i = 0; i < 8; ++i) {
+                const int row = (lane >> 4) + 4 * i;
+                const int grow = wm * 128 + fi * 32 + row;
+                if (grow < row_lim && gcol < col_lim) {
+                    float x[8];
+                    load_row8(R, row, c8, x);
+                    *(u32x4*)(C + (int64_t)grow * ldc + gcol) = pack8_bf16(x);
                 }
             }
+            __syncthreads();
+        }
         return;
     }
 
