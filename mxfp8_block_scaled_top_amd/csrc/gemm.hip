@@ -334,8 +334,12 @@ __device__ __forceinline__ void dma_scales(const i32x4& rs_a, const i32x4& rs_b,
     dma4(op ? rs_b : rs_a, o, lds_u32(&dst[op][wave & 1][0]));
 }
 
-__device__ __forceinline__ float silu_f(float x) { return x / (1.f + __expf(-x)); }
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
+// The reciprocal is the hardware's (about 1 ulp), not an IEEE division: the
+// results are rounded to bf16 or E4M3 right after.
+__device__ __forceinline__ float sigmoid_f(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
+__device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
 
 __device__ __forceinline__ float half_max32(float v) {
 #pragma unroll
@@ -432,6 +436,7 @@ struct EpiCtx {
     const GemmArgs& g;
     const Tile& tl;
     int wm, wn, ntn;
+    float pr[4];        // routing probability of the lane's row (lane / 2) in each slice
 };
 
 // ScaledSwiGLU forward of row slice fi of the wave's tile.  Staged columns
@@ -454,7 +459,7 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
         float a2[32];
         if (row < valid) {
             const int64_t gr = tl.row0 + frow0 + row;
-            const float p = g.prob[gr];
+            const float p = c.pr[fi];
             u32x4* a1g = (u32x4*)(g.a1 + gr * 2 * I + j0);
             u32x4* a1u = (u32x4*)(g.a1 + gr * 2 * I + I + j0);
 #pragma unroll
@@ -517,30 +522,34 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
     const int row = lane >> 1, h = lane & 1;
     float part = 0.f;
     if (DT != DT_MX) {
-#pragma unroll 1
-        for (int blk = 0; blk < 2; ++blk) {
-            const int cb = 64 * h + 32 * blk;               // staged column of the block
-            if (!(slab && row < valid)) continue;
+        if (slab && row < valid) {
             const int64_t gr = tl.row0 + frow0 + row;
-            const float p = g.prob[gr];
-            const u32x4* a1g = (const u32x4*)(g.a1 + gr * 2 * I + jw + cb);
-            const u32x4* a1u = (const u32x4*)(g.a1 + gr * 2 * I + I + jw + cb);
+            const float p = c.pr[fi];
+            // both blocks' saved values before any store (the stores may alias
+            // them for the compiler): one round trip
+            u32x4 wg[2][4], wu[2][4];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const int cb = 64 * h + 32 * blk;
+                const u32x4* a1g = (const u32x4*)(g.a1 + gr * 2 * I + jw + cb);
+                const u32x4* a1u = (const u32x4*)(g.a1 + gr * 2 * I + I + jw + cb);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    wg[blk][b] = a1g[b];
+                    wu[blk][b] = a1u[b];
+                }
+            }
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+            const int cb = 64 * h + 32 * blk;               // staged column of the block
             u32x4* og = (u32x4*)(g.act + gr * 2 * I + jw + cb);
             u32x4* ou = (u32x4*)(g.act + gr * 2 * I + I + jw + cb);
-            // all of the block's loads before its stores (which may alias them
-            // for the compiler): one round trip
-            u32x4 wg[4], wu[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                wg[b] = a1g[b];
-                wu[b] = a1u[b];
-            }
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 float d[8], gt[8], up[8], dg[8], du[8];
                 load_row8(R, row, cb + 8 * b, d);
-                unpack8_bf16(wg[b], gt);
-                unpack8_bf16(wu[b], up);
+                unpack8_bf16(wg[blk][b], gt);
+                unpack8_bf16(wu[blk][b], up);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     float sg = sigmoid_f(gt[i]);
@@ -553,33 +562,38 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
                 og[b] = pack8_bf16(dg);
                 ou[b] = pack8_bf16(du);
             }
+            }
         }
     } else {
         // phase 1, 8 values at a time: dg replaces the staged dA2 in R, du
         // goes to R2 (rows past the expert stay zero for the column blocks)
         const bool live = slab && row < valid;
         const int64_t gr = tl.row0 + frow0 + row;
-        const float p = live ? g.prob[gr] : 0.f;
-#pragma unroll 1
+        const float p = live ? c.pr[fi] : 0.f;
+        // both blocks' saved gate/up values in one round trip
+        u32x4 wg[2][4], wu[2][4];
+#pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             const int cb = 64 * h + 32 * blk;
             const u32x4* a1g = (const u32x4*)(g.a1 + gr * 2 * I + jw + cb);
             const u32x4* a1u = (const u32x4*)(g.a1 + gr * 2 * I + I + jw + cb);
-            // the block's saved gate/up values in one round trip
-            u32x4 wg[4], wu[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                wg[b] = live ? a1g[b] : (u32x4){0, 0, 0, 0};
-                wu[b] = live ? a1u[b] : (u32x4){0, 0, 0, 0};
+                wg[blk][b] = live ? a1g[b] : (u32x4){0, 0, 0, 0};
+                wu[blk][b] = live ? a1u[b] : (u32x4){0, 0, 0, 0};
             }
+        }
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int cb = 64 * h + 32 * blk;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 float d[8], dg[8], du[8];
                 load_row8(R, row, cb + 8 * b, d);
                 if (live) {
                     float gt[8], up[8];
-                    unpack8_bf16(wg[b], gt);
-                    unpack8_bf16(wu[b], up);
+                    unpack8_bf16(wg[blk][b], gt);
+                    unpack8_bf16(wu[blk][b], up);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         float sg = sigmoid_f(gt[i]);
@@ -889,6 +903,8 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         // wave's own LDS region (the pipeline has drained), so that a lane
         // stores 8 neighbouring columns as one 16-byte write (4 rows x 256
         // bytes per instruction) instead of 2-byte writes column by column.
+        // (The SwiGLU epilogues keep ordinary stores: their instructions write
+        // 16-byte pieces of a line, which L2 must merge.)
         float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         const int c8 = (lane & 15) * 8;
         const int gcol = wn * 128 + c8;             // N is a multiple of 8: all or nothing
@@ -903,7 +919,10 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
                 if (grow < row_lim && gcol < col_lim) {
                     float x[8];
                     load_row8(R, row, c8, x);
-                    *(u32x4*)(C + (int64_t)grow * ldc + gcol) = pack8_bf16(x);
+                    // streaming store: the output is not read again by this
+                    // kernel, so it should not evict the operands from L2
+                    __builtin_nontemporal_store(pack8_bf16(x),
+                                                (u32x4*)(C + (int64_t)grow * ldc + gcol));
                 }
             }
             __syncthreads();
@@ -911,8 +930,19 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         return;
     }
 
+    // the routing probability of the lane's row in each 32-row slice, loaded
+    // once for the whole epilogue (rows past the expert are never used)
+    float pr[4] = {0.f, 0.f, 0.f, 0.f};
+    if (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD) {
+#pragma unroll
+        for (int fi = 0; fi < 4; ++fi) {
+            const int frow = tl.m0 + wm * 128 + fi * 32 + (lane >> 1);
+            if (frow < tl.rows_e) pr[fi] = g.prob[tl.row0 + frow];
+        }
+    }
+
     if (EPI == EPI_SWIGLU_FWD) {
-        EpiCtx c{g, tl, wm, wn, ntn};
+        EpiCtx c{g, tl, wm, wn, ntn, {pr[0], pr[1], pr[2], pr[3]}};
         float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         swiglu_fwd_rows<DT>(c, R, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0);
         swiglu_fwd_rows<DT>(c, R, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1);
@@ -922,7 +952,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     }
 
     if (EPI == EPI_SWIGLU_BWD) {
-        EpiCtx c{g, tl, wm, wn, ntn};
+        EpiCtx c{g, tl, wm, wn, ntn, {pr[0], pr[1], pr[2], pr[3]}};
         float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         float* R2 = R + 32 * 128;
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0);
