@@ -17,6 +17,8 @@ roofline        the dominant kernel (largest total time in the step): its
                 launch on the launch stream during the timed steps
 cpu_baseline    the CPU oracle (tests only otherwise) timed on a bounded
                 sample of the same workload on this host's cores
+quantize        the standalone MXFP8 quantizer / dequantizer on the 8192 x 4096
+                quantize workload (HBM-bound; GB/s against the 8 TB/s peak)
 router          the router linear layer (logits = x W_r^T fused with the
                 routing; its backward) at the same shape, per launch
 loop_baseline   a per-expert torch loop (BF16, autograd) on the same inputs,
@@ -49,6 +51,7 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--cpu-inter", type=int, default=768)
     ap.add_argument("--no-router", action="store_true", help="skip the router linear layer line")
+    ap.add_argument("--no-quant", action="store_true", help="skip the standalone quantizer line")
     ap.add_argument("--no-loop", action="store_true", help="skip the per-expert loop baseline")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
@@ -260,6 +263,55 @@ def run_router(args, inp_dev, shape):
                                 "frac": round(lg.get("gbs", 0) / PEAK_HBM_GBS, 4)}}
 
 
+def run_quant(args):
+    """The standalone MXFP8 quantizer and dequantizer (rowwise) on the bf16
+    8192 x 4096 quantize workload, through the C ABI, rotating 6 input/output
+    buffer sets (about 600 MB, more than the 256 MB last-level cache) so that
+    every launch streams from HBM.  Algorithmic bytes per launch: 2 B read and
+    1 + 1/32 B written per element (quantize), the reverse for dequantize."""
+    import torch
+    import mxfp8_block_scaled_top_amd as moe
+    from mxfp8_block_scaled_top_amd import synth
+
+    R, C, nset = 8192, 4096, 6
+    L = moe.lib()
+    base = synth.quant_matrix(R, C).cuda()
+    xs = [base.roll(i, 0).contiguous() for i in range(nset)]
+    codes = [torch.empty((R, C), dtype=torch.uint8, device="cuda") for _ in range(nset)]
+    scales = [torch.empty((R, C // 32), dtype=torch.uint8, device="cuda") for _ in range(nset)]
+    outs = [torch.empty((R, C), dtype=torch.bfloat16, device="cuda") for _ in range(nset)]
+    st = torch.cuda.current_stream().cuda_stream
+
+    def one(i):
+        q = L.mxfp8_quantize(xs[i].data_ptr(), R, C, 1, None, 0, codes[i].data_ptr(),
+                             scales[i].data_ptr(), st)
+        d = L.mxfp8_dequantize(codes[i].data_ptr(), scales[i].data_ptr(), R, C, 1, None, 0,
+                               outs[i].data_ptr(), st)
+        if q or d:
+            raise RuntimeError(f"quantize status {q}, dequantize status {d}")
+
+    for i in range(nset):
+        one(i)
+    torch.cuda.synchronize()
+    n = max(3, args.steps) * nset
+    moe.trace_enable(2 * n + 8)
+    for k in range(n):
+        one(k % nset)
+    torch.cuda.synchronize()
+    per = {}
+    for name, d in moe.trace_read():
+        per.setdefault(name, []).append(d)
+    moe.trace_disable()
+    nbytes = R * C * (2 + 1 + 1 / 32)
+    out = {"workload": f"bf16 {R} x {C}, rowwise, {nset} rotating buffer sets"}
+    for name, key in (("mx_quant_rows", "quantize"), ("mx_dequant_rows", "dequantize")):
+        ms = sum(per[name]) / len(per[name])
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[key] = {"mean_us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+                    "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
+
+
 def run_loop_baseline(args, inp_dev, shape):
     """Per-expert loop: the structure of the Hugging Face
     MoE block the pages compare against -- torch softmax + top-k, then for
@@ -400,6 +452,9 @@ def main():
                   "frac_of_mfma_peak": round(q["frac_of_peak"], 4), "roofline": q["roofline"],
                   "gemm_only": {"ms": round(q["gemm_ms"], 3), "tflops": round(q["gemm_tflops"], 1)},
                   "kernels": q["kernels"]}
+    if not args.no_quant:
+        out["quantize"] = run_quant(args)
+        log(args, f"quantize: {out['quantize']}")
     if not args.no_router:
         out["router"] = run_router(args, dev, shape)
         log(args, f"router: fwd {out['router']['fwd_ms']} ms, bwd {out['router']['bwd_ms']} ms")
