@@ -15,6 +15,10 @@ roofline        the dominant kernel (largest total time in the step): its
                 algorithmic FLOPs per launch / its mean launch duration,
                 measured with HIP events recorded by the library around each
                 launch on the launch stream during the timed steps
+step_ms         median / min / max of the timed steps (events between steps);
+                ms_per_step is the whole timed region / steps
+sclk_mhz        the shader clock the driver reports, sampled during the timed
+                steps (null where its sysfs file is not readable)
 cpu_baseline    the CPU oracle (tests only otherwise) timed on a bounded
                 sample of the same workload on this host's cores
 quantize        the standalone MXFP8 quantizer / dequantizer on the 8192 x 4096
@@ -30,6 +34,7 @@ import argparse
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -135,6 +140,80 @@ def measured_traffic(kernel: str, workload: str):
                                 "source": os.path.relpath(path, ROOT)}
 
 
+class SclkSampler:
+    """Samples the GPU's current shader clock (the "S:" line of the amdgpu
+    driver's pp_dpm_sclk file of torch device 0) from a host thread while the
+    timed steps run.  Host-side only; `summary()` is None where the file is
+    not readable."""
+
+    def __init__(self, period_s=0.005):
+        self.period, self.mhz, self.path = period_s, [], None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import glob
+            import torch
+            pr = torch.cuda.get_device_properties(0)
+            bdf = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
+            for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+                if os.path.realpath(os.path.dirname(f)).endswith(bdf):
+                    self.path = f
+        except Exception:
+            self.path = None
+
+    @staticmethod
+    def _mhz(line):
+        for tok in line.split():
+            if tok.lower().endswith("mhz"):
+                return float(tok[:-3])
+        return None
+
+    def _read(self):
+        # the "S:" line (current clock) where the driver prints one, else the
+        # selected level (marked with '*')
+        cur = None
+        for line in open(self.path).read().splitlines():
+            if line.startswith("S:"):
+                return self._mhz(line)
+            if line.rstrip().endswith("*"):
+                cur = self._mhz(line)
+        return cur
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v is not None:
+                    self.mhz.append(v)
+            except Exception:
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread:
+            self._thread.join()
+
+    def summary(self):
+        if not self.mhz:
+            return None
+        v = sorted(self.mhz)
+        return {"mean": round(sum(v) / len(v), 1), "median": v[len(v) // 2], "min": v[0],
+                "max": v[-1], "samples": len(v), "spec": 2400.0}
+
+
+def step_stats(events):
+    """Median / min / max of the per-step times between consecutive events."""
+    d = sorted(a.elapsed_time(b) for a, b in zip(events[:-1], events[1:]))
+    return {"median": round(d[len(d) // 2], 4), "min": round(d[0], 4), "max": round(d[-1], 4)}
+
+
 def run_gpu(args, prec_name, inp_dev, shape):
     import torch
     import mxfp8_block_scaled_top_amd as moe
@@ -152,12 +231,16 @@ def run_gpu(args, prec_name, inp_dev, shape):
         step()
     torch.cuda.synchronize()
     moe.trace_enable(max(64, 64 * args.steps))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with SclkSampler() as clk:
+        t0 = time.perf_counter()
+        evs[0].record()
+        for i in range(args.steps):
+            step()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     trace = moe.trace_read()
     moe.trace_disable()
     ms = (t1 - t0) * 1e3 / args.steps
@@ -199,6 +282,8 @@ def run_gpu(args, prec_name, inp_dev, shape):
         "gemm_ms": gemm_ms,
         "gemm_tflops": flops / (gemm_ms * 1e-3) / 1e12,
         "kernel_ms_sum": sum(p["total_ms"] for p in per.values()) / args.steps,
+        "step_ms": step_stats(evs),
+        "sclk_mhz": clk.summary(),
         "roofline": roof,
         "kernels": kernels,
     }
@@ -371,6 +456,14 @@ def cpu_baseline(args, inp_host, shape, prec_name):
 
     cores = len(os.sched_getaffinity(0))
     torch.set_num_threads(cores)
+    cpu_model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     Ts, Is = min(args.cpu_tokens, shape.T), min(args.cpu_inter, shape.I)
     I = shape.I
     w1 = [torch.cat([w[:Is], w[I:I + Is]]).contiguous() for w in inp_host["w1"]]
@@ -380,7 +473,7 @@ def cpu_baseline(args, inp_host, shape, prec_name):
                     shape.k, prec_name)
     t = time.perf_counter() - t0
     return {"value": round(Ts * (Is / I) / t, 3), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+            "threads": torch.get_num_threads(), "cpu_model": cpu_model, "kind": "oracle",
             "sample": (f"oracle layer step ({prec_name}, fwd+bwd) on the first {Ts} tokens and "
                        f"the first {Is} of {I} intermediate columns of all {shape.E} experts "
                        f"(H={shape.H}, k={shape.k}); took {t:.1f} s; full-layer rate "
@@ -440,6 +533,8 @@ def main():
                    "I": shape.I, "E": shape.E, "k": shape.k, "precision": head},
         "tflops_per_layer": round(r["tflops"], 1),
         "frac_of_mfma_peak": round(r["frac_of_peak"], 4),
+        "step_ms": r["step_ms"],
+        "sclk_mhz": r["sclk_mhz"],
         "roofline": r["roofline"],
         "gemm_only": {"ms": round(r["gemm_ms"], 3), "tflops": round(r["gemm_tflops"], 1),
                       "frac_of_mfma_peak": round(r["gemm_tflops"] / PEAK_TFLOPS[head], 4)},
@@ -448,7 +543,8 @@ def main():
     for p in precs[1:]:
         q = res[p]
         out[p] = {"value": round(q["tokens_per_s"], 1), "unit": "tokens/s",
-                  "ms_per_step": round(q["ms_per_step"], 4), "tflops_per_layer": round(q["tflops"], 1),
+                  "ms_per_step": round(q["ms_per_step"], 4), "step_ms": q["step_ms"],
+                  "sclk_mhz": q["sclk_mhz"], "tflops_per_layer": round(q["tflops"], 1),
                   "frac_of_mfma_peak": round(q["frac_of_peak"], 4), "roofline": q["roofline"],
                   "gemm_only": {"ms": round(q["gemm_ms"], 3), "tflops": round(q["gemm_tflops"], 1)},
                   "kernels": q["kernels"]}
