@@ -366,8 +366,9 @@ __device__ __forceinline__ int st_idx(int row, int col) {
 }
 
 __device__ __forceinline__ void stage_fragments(float* R, const f32x16& f0, const f32x16& f1,
-                                                const f32x16& f2, const f32x16& f3) {
-    const int lane = threadIdx.x & 63, fr = lane & 31, hi = lane >> 5;
+                                                const f32x16& f2, const f32x16& f3,
+                                                int lane = threadIdx.x & 63) {
+    const int fr = lane & 31, hi = lane >> 5;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         int row = 4 * hi + 8 * (v >> 2) + (v & 3);
@@ -376,47 +377,6 @@ __device__ __forceinline__ void stage_fragments(float* R, const f32x16& f0, cons
         R[st_idx(row, 64 + fr)] = f2[v];
         R[st_idx(row, 96 + fr)] = f3[v];
     }
-}
-
-// The plain-store epilogue stages a 32 x 128 slice as bf16, transposed:
-// storage row c (a tile column) holds the slice's 32 rows in 8-byte chunks of
-// 4 rows; chunk k of row c sits at k ^ p(c), p a bit permutation of
-// (c >> 2) & 7, so that both the fragments' 8-byte writes and the transposing
-// reads of 16-lane groups touch 64 distinct banks.
-__device__ __forceinline__ int trs_off(int c, int k) {
-    const int u = (c >> 2) & 7;
-    return c * 64 + ((k ^ (((u & 2) << 1) | ((u & 4) >> 1) | (u & 1))) << 3);
-}
-
-// Lane (column fr, half hi) holds rows 4hi + 8m .. +3 of column fr of every
-// fragment: rounded to bf16, each run of 4 rows is one 8-byte chunk.
-__device__ __forceinline__ void stage_fragments_bf16(uint8_t* R, const f32x16 (&f)[4], int lane) {
-    const int fr = lane & 31, hi = lane >> 5;
-#pragma unroll
-    for (int fj = 0; fj < 4; ++fj)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            uint2 w;
-            w.x = pack_bf16x2(f[fj][4 * m], f[fj][4 * m + 1]);
-            w.y = pack_bf16x2(f[fj][4 * m + 2], f[fj][4 * m + 3]);
-            *(uint2*)(R + trs_off(32 * fj + fr, hi + 2 * m)) = w;
-        }
-}
-
-// Row r0 + q (q = lane & 15) of the slice, columns c0 .. c0 + 7, as 8 bf16:
-// two transposing reads, each of a 4-column x 16-row block in which lane q
-// supplies the address of column c0 + (q >> 2), rows r0 + 4 (q & 3) .. +3 and
-// receives row r0 + q of the 4 columns.  Every lane of the 16-lane group must
-// take part.
-__device__ __forceinline__ u32x4 load_row8_tr(const uint8_t* R, int r0, int c0, int lane) {
-    const int q = lane & 15;
-    const int k = (r0 >> 2) + (q & 3);
-    i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4_t*)(R + trs_off(c0 + (q >> 2), k)));
-    i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4_t*)(R + trs_off(c0 + 4 + (q >> 2), k)));
-    i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    return __builtin_bit_cast(u32x4, v);
 }
 
 __device__ __forceinline__ void load_row8(const float* R, int row, int col, float (&x)[8]) {
@@ -941,36 +901,36 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
             row_lim = g.M - tl.m0;
         }
         // Each 32-row slice of the wave's 128 x 128 result goes through the
-        // wave's own LDS region (the pipeline has drained), rounded to bf16
-        // and transposed (stage_fragments_bf16 / load_row8_tr), so that a
-        // lane stores 8 neighbouring columns of a row as one 16-byte write
-        // (16 rows x 64 bytes per instruction).  (The SwiGLU epilogues keep
-        // ordinary stores: their instructions write 16-byte pieces of a line,
-        // which L2 must merge.)
-        uint8_t* R = wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3;
+        // wave's own LDS region (the pipeline has drained), so that a lane
+        // stores 8 neighbouring columns as one 16-byte write (4 rows x 256
+        // bytes per instruction) instead of 2-byte writes column by column.
+        // (The SwiGLU epilogues keep ordinary stores: their instructions write
+        // 16-byte pieces of a line, which L2 must merge.)
+        float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         // the lane index through an empty asm: the addresses built on it are
         // then computed here, not hoisted above the K loop and kept live
         // (spilled) through it
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        const int q = ln & 15, cg = ln >> 4;
+        const int c8 = (ln & 15) * 8;
+        const int gcol = wn * 128 + c8;             // N is a multiple of 8: all or nothing
 #pragma unroll
         for (int fi = 0; fi < 4; ++fi) {
-            stage_fragments_bf16(R, acc[fi], ln);
+            stage_fragments(R, acc[fi][0], acc[fi][1], acc[fi][2], acc[fi][3], ln);
             __syncthreads();
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb) {
-                    const int col = 32 * cb + 8 * cg;       // in the wave's 128 columns
-                    const u32x4 v = load_row8_tr(R, 16 * rb, col, ln);
-                    const int grow = wm * 128 + fi * 32 + 16 * rb + q;
-                    const int gcol = wn * 128 + col;        // N is a multiple of 8
+            for (int i = 0; i < 8; ++i) {
+                const int row = (ln >> 4) + 4 * i;
+                const int grow = wm * 128 + fi * 32 + row;
+                if (grow < row_lim && gcol < col_lim) {
+                    float x[8];
+                    load_row8(R, row, c8, x);
                     // streaming store: the output is not read again by this
                     // kernel, so it should not evict the operands from L2
-                    if (grow < row_lim && gcol < col_lim)
-                        __builtin_nontemporal_store(v, (u32x4*)(C + (int64_t)grow * ldc + gcol));
+                    __builtin_nontemporal_store(pack8_bf16(x),
+                                                (u32x4*)(C + (int64_t)grow * ldc + gcol));
                 }
+            }
             __syncthreads();
         }
         return;
