@@ -438,6 +438,7 @@ struct EpiCtx {
     const Tile& tl;
     int wm, wn, ntn;
     float pr[4];        // routing probability of the lane's row (lane / 2) in each slice
+    int lane;           // lane index (lane_after_loop)
 };
 
 // ScaledSwiGLU forward of row slice fi of the wave's tile.  Staged columns
@@ -448,9 +449,9 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
                                                 const f32x16& f3, int fi) {
     const GemmArgs& g = c.g;
     const Tile& tl = c.tl;
-    const int lane = threadIdx.x & 63;
+    const int lane = c.lane;
     const int64_t I = g.I;
-    stage_fragments(R, f0, f1, f2, f3);
+    stage_fragments(R, f0, f1, f2, f3, lane);
     __syncthreads();
     const int frow0 = tl.m0 + c.wm * 128 + fi * 32;      // row inside the expert
     const int valid = min(32, tl.rows_e - frow0);          // rows of this slice that exist
@@ -512,9 +513,9 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
                                                 const f32x16& f2, const f32x16& f3, int fi) {
     const GemmArgs& g = c.g;
     const Tile& tl = c.tl;
-    const int lane = threadIdx.x & 63;
+    const int lane = c.lane;
     const int64_t I = g.I;
-    stage_fragments(R, f0, f1, f2, f3);
+    stage_fragments(R, f0, f1, f2, f3, lane);
     __syncthreads();
     const int frow0 = tl.m0 + c.wm * 128 + fi * 32;
     const int valid = min(32, tl.rows_e - frow0);
@@ -655,6 +656,16 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
     __syncthreads();
 }
 
+// The lane index recomputed from the execution mask (all lanes are active)
+// and passed through an empty asm, for the epilogues: it then depends on
+// nothing computed before the K loop, so neither the work-item id nor
+// addresses built on it are kept live (and spilled) through the loop.
+__device__ __forceinline__ int lane_after_loop() {
+    int l = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(l));
+    return l;
+}
+
 // ---------------------------------------------------------------- the kernel
 template <int DT, int LA, int LB, int GRP, int EPI, int USE>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -671,7 +682,8 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     __shared__ float red[2 * kGemmBM];                  // probability-gradient row partials
     __shared__ int sched[256];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // uniform
     const int wm = wave >> 1, wn = wave & 1;
 
     // XCD-aware remap: dispatch is round-robin over 8 XCDs; hand XCD x the
@@ -907,11 +919,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         // (The SwiGLU epilogues keep ordinary stores: their instructions write
         // 16-byte pieces of a line, which L2 must merge.)
         float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
-        // the lane index through an empty asm: the addresses built on it are
-        // then computed here, not hoisted above the K loop and kept live
-        // (spilled) through it
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
+        const int ln = lane_after_loop();
         const int c8 = (ln & 15) * 8;
         const int gcol = wn * 128 + c8;             // N is a multiple of 8: all or nothing
 #pragma unroll
@@ -938,17 +946,18 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
 
     // the routing probability of the lane's row in each 32-row slice, loaded
     // once for the whole epilogue (rows past the expert are never used)
+    const int ln = lane_after_loop();
     float pr[4] = {0.f, 0.f, 0.f, 0.f};
     if (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD) {
 #pragma unroll
         for (int fi = 0; fi < 4; ++fi) {
-            const int frow = tl.m0 + wm * 128 + fi * 32 + (lane >> 1);
+            const int frow = tl.m0 + wm * 128 + fi * 32 + (ln >> 1);
             if (frow < tl.rows_e) pr[fi] = g.prob[tl.row0 + frow];
         }
     }
 
     if (EPI == EPI_SWIGLU_FWD) {
-        EpiCtx c{g, tl, wm, wn, ntn, {pr[0], pr[1], pr[2], pr[3]}};
+        EpiCtx c{g, tl, wm, wn, ntn, {pr[0], pr[1], pr[2], pr[3]}, ln};
         float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         swiglu_fwd_rows<DT>(c, R, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0);
         swiglu_fwd_rows<DT>(c, R, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1);
@@ -958,16 +967,17 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     }
 
     if (EPI == EPI_SWIGLU_BWD) {
-        EpiCtx c{g, tl, wm, wn, ntn, {pr[0], pr[1], pr[2], pr[3]}};
+        EpiCtx c{g, tl, wm, wn, ntn, {pr[0], pr[1], pr[2], pr[3]}, ln};
         float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         float* R2 = R + 32 * 128;
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0);
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1);
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2);
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[3][0], acc[3][1], acc[3][2], acc[3][3], 3);
-        if (tl.m0 + tid < tl.rows_e)
-            g.dprob_part[(tl.row0 + tl.m0 + tid) * (int64_t)ntn + tl.n_tile] =
-                red[tid] + red[kGemmBM + tid];
+        const int t = wave * 64 + ln;
+        if (tl.m0 + t < tl.rows_e)
+            g.dprob_part[(tl.row0 + tl.m0 + t) * (int64_t)ntn + tl.n_tile] =
+                red[t] + red[kGemmBM + t];
         return;
     }
 }
