@@ -7,11 +7,12 @@
 // [BioNeMo MoE recipe page, section GroupedLinear].
 //
 // Three launches, all deterministic (integer atomics are not used):
-//   1. route_topk:    one thread per token.  Picks the k largest fp32 logits
-//                     (ties -> lower expert), softmax over the picks, and the
-//                     token's rank among the block's earlier tokens that
-//                     picked the same expert (wave ballots + a per-wave count
-//                     table in LDS).  Writes per-block expert counts.
+//   1. route_topk:    one thread per token, its row of logits in registers.
+//                     Picks the k largest fp32 logits (ties -> lower expert),
+//                     softmax over the picks, and the token's rank among the
+//                     block's earlier tokens that picked the same expert (wave
+//                     ballots per expert, kept in LDS with per-wave counts).
+//                     Writes per-block expert counts.
 //   2. route_scan:    one wave.  Per expert, exclusive scan of the block counts
 //                     (the blocks' base rows), split_sizes and offsets.
 //   3. route_scatter: one thread per pick: dest_row and src_token.
@@ -21,7 +22,7 @@
 
 namespace moe {
 
-constexpr int kRouteThreads = 512;          // tokens per block (8 waves)
+constexpr int kRouteThreads = 256;          // tokens per block (4 waves)
 constexpr int kRouteWaves = kRouteThreads / kWave;
 
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
@@ -29,6 +30,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     int32_t* __restrict__ topk_expert, float* __restrict__ topk_prob,
     int32_t* __restrict__ local_rank, int32_t* __restrict__ block_counts) {
     __shared__ int wave_cnt[kRouteWaves][kMaxExperts];
+    __shared__ uint64_t wave_bal[kRouteWaves][kMaxExperts];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int t = blockIdx.x * kRouteThreads + tid;
     const bool valid = t < T;
@@ -38,18 +40,31 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
         const float* row = logits + (size_t)t * E;
         int32_t* sel = topk_expert + (size_t)t * k;
         float* prob = topk_prob + (size_t)t * k;
-        // k scans of the row: strict '>' keeps the lowest index among equals.
+        // the row in registers (E <= kMaxExperts; E is uniform, so the tests
+        // below are scalar branches, and entries e >= E are neither loaded
+        // nor used)
+        float v[kMaxExperts];
+#pragma unroll
+        for (int e = 0; e < kMaxExperts; ++e) {
+            if (e < E) v[e] = row[e];
+            else v[e] = 0.f;
+        }
+        // k scans: strict '>' keeps the lowest index among equals.  The picked
+        // logits go to prob[] until the denominator is known.
         float top = 0.f, denom = 0.f;
         for (int j = 0; j < k; ++j) {
             float bv = 0.f;
             int be = -1;
-            for (int e = 0; e < E; ++e) {
-                if ((picked >> e) & 1ull) continue;
-                float v = row[e];
-                if (be < 0 || v > bv) { bv = v; be = e; }
+#pragma unroll
+            for (int e = 0; e < kMaxExperts; ++e) {
+                if (e < E && !((picked >> e) & 1ull) && (be < 0 || v[e] > bv)) {
+                    bv = v[e];
+                    be = e;
+                }
             }
             picked |= 1ull << be;
             sel[j] = be;
+            prob[j] = bv;
             if (j == 0) top = bv;
             denom += expf(bv - top);
         }
@@ -57,17 +72,23 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
             // softmax over all experts, taken at the picks
             float mx = top;                  // the first pick is the row maximum
             float s = 0.f;
-            for (int e = 0; e < E; ++e) s += expf(row[e] - mx);
-            for (int j = 0; j < k; ++j) prob[j] = expf(row[sel[j]] - mx) / s;
+#pragma unroll
+            for (int e = 0; e < kMaxExperts; ++e)
+                if (e < E) s += expf(v[e] - mx);
+            for (int j = 0; j < k; ++j) prob[j] = expf(prob[j] - mx) / s;
         } else {
-            for (int j = 0; j < k; ++j) prob[j] = expf(row[sel[j]] - top) / denom;
+            for (int j = 0; j < k; ++j) prob[j] = expf(prob[j] - top) / denom;
         }
     }
 
-    // Per-wave counts of each expert, then block-level prefix over waves.
+    // Per-wave ballots and counts of each expert, then the block-level prefix
+    // over waves.
     for (int e = 0; e < E; ++e) {
         uint64_t bal = __ballot((picked >> e) & 1ull);
-        if (lane == 0) wave_cnt[wave][e] = __popcll(bal);
+        if (lane == 0) {
+            wave_bal[wave][e] = bal;
+            wave_cnt[wave][e] = __popcll(bal);
+        }
     }
     __syncthreads();
     if (tid < E) {
@@ -80,14 +101,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
         block_counts[(size_t)blockIdx.x * E + tid] = run;
     }
     __syncthreads();
-    const uint64_t lt = lanemask_lt();
-    for (int e = 0; e < E; ++e) {
-        bool mine = (picked >> e) & 1ull;
-        uint64_t bal = __ballot(mine);
-        if (mine) {
-            int r = wave_cnt[wave][e] + __popcll(bal & lt);
-            for (int j = 0; j < k; ++j)
-                if (topk_expert[(size_t)t * k + j] == e) local_rank[(size_t)t * k + j] = r;
+    if (valid) {
+        const uint64_t lt = lanemask_lt();
+        for (int j = 0; j < k; ++j) {
+            const int e = topk_expert[(size_t)t * k + j];
+            local_rank[(size_t)t * k + j] = wave_cnt[wave][e] + __popcll(wave_bal[wave][e] & lt);
         }
     }
 }
@@ -99,14 +117,18 @@ __global__ __launch_bounds__(64) void route_scan_kernel(
     int32_t* __restrict__ expert_offsets) {
     const int e = threadIdx.x;
     int total = 0;
-    if (e < E)
+    if (e < E) {
+        // (unrolled so that several loads are in flight at once)
+#pragma unroll 8
         for (int b = 0; b < nblocks; ++b) total += block_counts[(size_t)b * E + e];
+    }
     int incl = wave_incl_scan(e < E ? total : 0);
     int off = incl - (e < E ? total : 0);
     if (e < E) {
         split_sizes[e] = total;
         expert_offsets[e] = off;
         int run = off;
+#pragma unroll 8
         for (int b = 0; b < nblocks; ++b) {
             int c = block_counts[(size_t)b * E + e];
             block_base[(size_t)b * E + e] = run;

@@ -133,19 +133,42 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict_
     if (c >= H) return;
     float acc[4][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + tg + 8 * i;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[i][q] = 0.f;
-        if (dxp && t < T) {
-            for (int j = 0; j < k; ++j) {      // expert path, slots in order
-                const int64_t row = dest_row[(int64_t)t * k + j];
-                const u32x4 v = *(const u32x4*)(dxp + row * H + c);
+    if (dxp) {
+        // expert path, slots in order; two tokens and up to 8 slots at a time,
+        // the grouped-row indices first, then all their rows, so that up to
+        // 16 row loads are in flight
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[i][2 * q] += lo_bf16(v[q]);
-                    acc[i][2 * q + 1] += hi_bf16(v[q]);
+        for (int i0 = 0; i0 < 4; i0 += 2) {
+            for (int j0 = 0; j0 < k; j0 += 8) {
+                int64_t rows[2][8];
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int t = t0 + tg + 8 * (i0 + ii);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        rows[ii][u] = (t < T && j0 + u < k) ? dest_row[(int64_t)t * k + j0 + u] : -1;
                 }
+                u32x4 v[2][8];
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        v[ii][u] = rows[ii][u] >= 0 ? *(const u32x4*)(dxp + rows[ii][u] * H + c)
+                                                    : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        if (rows[ii][u] < 0) continue;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            acc[i0 + ii][2 * q] += lo_bf16(v[ii][u][q]);
+                            acc[i0 + ii][2 * q + 1] += hi_bf16(v[ii][u][q]);
+                        }
+                    }
             }
         }
     }
@@ -238,6 +261,76 @@ __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict_
     }
 }
 
+// The same partial sums for more than kDwExperts experts, in one pass over x:
+// lane l of every wave holds G[t][l] (expert l) of the wave's tokens and 2
+// columns per lane for all 64 experts in registers; v_readlane hands each
+// expert's weight to the whole wave.  The 4 waves are added in order, 16
+// experts at a time through LDS.
+constexpr int kDwCols64 = 128;      // columns per workgroup (2 per lane)
+__global__ __launch_bounds__(256) void router_dw64_kernel(const float* __restrict__ G,
+                                                          const bf16_t* __restrict__ x, int T,
+                                                          int H, int E, int tps,
+                                                          float* __restrict__ part) {
+    __shared__ float red[4][16][kDwCols64 + 4];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
+    const int lane = tid & 63;
+    const int cb = blockIdx.x * kDwCols64;
+    const int c = cb + 2 * lane;
+    const int s = blockIdx.y;
+    const int tb = s * tps, te = min(T, tb + tps);
+    float acc[64][2];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) acc[e][0] = acc[e][1] = 0.f;
+    // Every lane stays active through the loop (v_readlane reads the lanes'
+    // weights whatever the execution mask); lanes past the last column load
+    // column 0 and use zeros.
+    const bool col_ok = c < H;
+    const int cl = col_ok ? c : 0;
+    // 4 of the wave's tokens per iteration, loads first; tokens past the
+    // split's end load row tb with weight 0
+    for (int t = tb + wave; t < te; t += 16) {
+        uint32_t xv[4];
+        float gv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int tu = t + 4 * u;
+            const bool ok = tu < te;
+            const uint32_t xl = *(const uint32_t*)(x + (int64_t)(ok ? tu : tb) * H + cl);
+            xv[u] = col_ok ? xl : 0u;
+            const float gl = G[(int64_t)(ok ? tu : tb) * E + (lane < E ? lane : 0)];
+            gv[u] = (ok && lane < E) ? gl : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float x0 = lo_bf16(xv[u]), x1 = hi_bf16(xv[u]);
+#pragma unroll
+            for (int e = 0; e < 64; ++e) {
+                const float g = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gv[u]), e));
+                acc[e][0] = __builtin_fmaf(g, x0, acc[e][0]);
+                acc[e][1] = __builtin_fmaf(g, x1, acc[e][1]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e0 = 0; e0 < 64; e0 += 16) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            red[wave][e][2 * lane] = acc[e0 + e][0];
+            red[wave][e][2 * lane + 1] = acc[e0 + e][1];
+        }
+        __syncthreads();
+        for (int i = tid; i < 16 * kDwCols64; i += 256) {
+            const int e = i / kDwCols64, cl = i - e * kDwCols64;
+            if (e0 + e < E && cb + cl < H)
+                part[((int64_t)s * E + e0 + e) * H + cb + cl] =
+                    ((red[0][e][cl] + red[1][e][cl]) + red[2][e][cl]) + red[3][e][cl];
+        }
+        __syncthreads();
+    }
+}
+
 __global__ __launch_bounds__(256) void router_dw_reduce_kernel(const float* __restrict__ part,
                                                                int ns, int64_t n,
                                                                bf16_t* __restrict__ dw) {
@@ -250,10 +343,15 @@ __global__ __launch_bounds__(256) void router_dw_reduce_kernel(const float* __re
 }
 
 // ---------------------------------------------------------------- launchers
+// Columns per weight-gradient workgroup: the many-expert kernel keeps all 64
+// experts in registers for 2 columns per lane.
+static int router_dw_cols(int E) { return E > kDwExperts ? kDwCols64 : kDxCols; }
+
 // Token splits of the weight gradient: enough workgroups to cover the chip
 // (about 512), at least 64 tokens each.
-static int router_dw_splits(int64_t T, int H) {
-    const int64_t ctiles = (H + kDxCols - 1) / kDxCols;
+static int router_dw_splits(int64_t T, int H, int E) {
+    const int cols = router_dw_cols(E);
+    const int64_t ctiles = (H + cols - 1) / cols;
     int64_t ns = (512 + ctiles - 1) / ctiles;
     const int64_t cap = (T + 63) / 64;
     if (ns > cap) ns = cap;
@@ -261,7 +359,7 @@ static int router_dw_splits(int64_t T, int H) {
 }
 
 size_t router_bwd_workspace_bytes(int64_t T, int H, int E) {
-    return (size_t)router_dw_splits(T, H) * E * H * sizeof(float) + 256;
+    return (size_t)router_dw_splits(T, H, E) * E * H * sizeof(float) + 256;
 }
 
 hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w, int T, int H, int E,
@@ -290,13 +388,17 @@ hipError_t launch_router_bwd(const float* dlogits, const bf16_t* x, const bf16_t
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int ns = router_dw_splits(T, H);
+    const int ns = router_dw_splits(T, H, E);
     const int tps = (T + ns - 1) / ns;
     float* part = (float*)ws;
     {
         TraceScope ts("router_dw", s);
-        dim3 grid((unsigned)((H + kDxCols - 1) / kDxCols), (unsigned)ns);
-        router_dw_kernel<<<grid, 256, 0, s>>>(dlogits, x, T, H, E, tps, part);
+        const int cols = router_dw_cols(E);
+        dim3 grid((unsigned)((H + cols - 1) / cols), (unsigned)ns);
+        if (E > kDwExperts)
+            router_dw64_kernel<<<grid, 256, 0, s>>>(dlogits, x, T, H, E, tps, part);
+        else
+            router_dw_kernel<<<grid, 256, 0, s>>>(dlogits, x, T, H, E, tps, part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
