@@ -443,10 +443,15 @@ struct EpiCtx {
 
 // ScaledSwiGLU forward of row slice fi of the wave's tile.  Staged columns
 // [64q, 64q+32) are gate and [64q+32, 64q+64) up for j = tile j0 + (2wn+q)*32.
+// Largest |bf16| bit pattern of the two values in a packed word, merged into m.
+__device__ __forceinline__ uint32_t max_abs_bf16x2(uint32_t m, uint32_t w) {
+    return max(m, max(w & 0x7fffu, (w >> 16) & 0x7fffu));
+}
+
 template <int DT>
 __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const f32x16& f0,
                                                 const f32x16& f1, const f32x16& f2,
-                                                const f32x16& f3, int fi) {
+                                                const f32x16& f3, int fi, uint32_t& amx) {
     const GemmArgs& g = c.g;
     const Tile& tl = c.tl;
     const int lane = c.lane;
@@ -477,7 +482,13 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
             if (DT != DT_MX) {          // bf16 A2 (BF16, and FP8: cast later)
                 u32x4* o = (u32x4*)(g.act + gr * I + j0);
 #pragma unroll
-                for (int b = 0; b < 4; ++b) o[b] = pack8_bf16(a2 + 8 * b);
+                for (int b = 0; b < 4; ++b) {
+                    const u32x4 pk = pack8_bf16(a2 + 8 * b);
+                    o[b] = pk;
+                    if (DT == DT_FP8)   // the tensor maximum of the cast that follows
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) amx = max_abs_bf16x2(amx, pk[q]);
+                }
             } else {
                 u32x4 c0, c1;
                 uint32_t S = quant32(a2, c0, c1);
@@ -510,7 +521,8 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
 template <int DT>
 __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float* R2,
                                                 float* red, const f32x16& f0, const f32x16& f1,
-                                                const f32x16& f2, const f32x16& f3, int fi) {
+                                                const f32x16& f2, const f32x16& f3, int fi,
+                                                uint32_t& amx) {
     const GemmArgs& g = c.g;
     const Tile& tl = c.tl;
     const int lane = c.lane;
@@ -561,8 +573,13 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
                     du[i] = dp * sl;
                     part += d[i] * sl * up[i];
                 }
-                og[b] = pack8_bf16(dg);
-                ou[b] = pack8_bf16(du);
+                const u32x4 pg = pack8_bf16(dg), pu = pack8_bf16(du);
+                og[b] = pg;
+                ou[b] = pu;
+                if (DT == DT_FP8)       // the tensor maximum of the cast that follows
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        amx = max_abs_bf16x2(max_abs_bf16x2(amx, pg[q]), pu[q]);
             }
             }
         }
@@ -666,6 +683,18 @@ __device__ __forceinline__ int lane_after_loop() {
     return l;
 }
 
+// Workgroup maximum of the lanes' values into part[blockIdx.x] (scratch: 4
+// words of LDS no longer in use).
+__device__ __forceinline__ void amax_to_part(uint32_t v, uint32_t* scratch, uint32_t* part) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) scratch[wave] = v;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        part[blockIdx.x] = max(max(scratch[0], scratch[1]), max(scratch[2], scratch[3]));
+}
+
 // ---------------------------------------------------------------- the kernel
 template <int DT, int LA, int LB, int GRP, int EPI, int USE>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -691,8 +720,12 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     const int G8 = gridDim.x >> 3;
     const int t = (blockIdx.x & 7) * G8 + (blockIdx.x >> 3);
 
+    constexpr bool kAmax = DT == DT_FP8 && (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD);
     Tile tl;
-    if (!decode_tile<GRP>(g, ntn, mtm, t, sched, tl)) return;
+    if (!decode_tile<GRP>(g, ntn, mtm, t, sched, tl)) {
+        if (kAmax && tid == 0) g.amax_part[blockIdx.x] = 0;
+        return;
+    }
 
     // ---- operand descriptors
     constexpr int kElemB = DT == DT_BF16 ? 2 : 1;
@@ -959,10 +992,12 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     if (EPI == EPI_SWIGLU_FWD) {
         EpiCtx c{g, tl, wm, wn, ntn, {pr[0], pr[1], pr[2], pr[3]}, ln};
         float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
-        swiglu_fwd_rows<DT>(c, R, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0);
-        swiglu_fwd_rows<DT>(c, R, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1);
-        swiglu_fwd_rows<DT>(c, R, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2);
-        swiglu_fwd_rows<DT>(c, R, acc[3][0], acc[3][1], acc[3][2], acc[3][3], 3);
+        uint32_t amx = 0;
+        swiglu_fwd_rows<DT>(c, R, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0, amx);
+        swiglu_fwd_rows<DT>(c, R, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1, amx);
+        swiglu_fwd_rows<DT>(c, R, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2, amx);
+        swiglu_fwd_rows<DT>(c, R, acc[3][0], acc[3][1], acc[3][2], acc[3][3], 3, amx);
+        if (kAmax) amax_to_part(amx, (uint32_t*)sched, g.amax_part);
         return;
     }
 
@@ -970,10 +1005,12 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         EpiCtx c{g, tl, wm, wn, ntn, {pr[0], pr[1], pr[2], pr[3]}, ln};
         float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         float* R2 = R + 32 * 128;
-        swiglu_bwd_rows<DT>(c, R, R2, red, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0);
-        swiglu_bwd_rows<DT>(c, R, R2, red, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1);
-        swiglu_bwd_rows<DT>(c, R, R2, red, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2);
-        swiglu_bwd_rows<DT>(c, R, R2, red, acc[3][0], acc[3][1], acc[3][2], acc[3][3], 3);
+        uint32_t amx = 0;
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0, amx);
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1, amx);
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2, amx);
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[3][0], acc[3][1], acc[3][2], acc[3][3], 3, amx);
+        if (kAmax) amax_to_part(amx, (uint32_t*)sched, g.amax_part);
         const int t = wave * 64 + ln;
         if (tl.m0 + t < tl.rows_e)
             g.dprob_part[(tl.row0 + tl.m0 + t) * (int64_t)ntn + tl.n_tile] =
@@ -998,21 +1035,22 @@ int gemm_n_tiles(int epi, int N, int I) {
     return (N + kGemmBN - 1) / kGemmBN;
 }
 
+int64_t gemm_slots(int grp, int epi, int64_t rows, int E, int M, int N, int I) {
+    const int ntn = gemm_n_tiles(epi, N, I);
+    int64_t tiles;
+    if (grp == G_M)   // upper bound of sum_e ceil(M_e / BM)
+        tiles = (rows + (int64_t)E * (kGemmBM - 1)) / kGemmBM * ntn;
+    else
+        tiles = (int64_t)E * ((M + kGemmBM - 1) / kGemmBM) * ntn;
+    return (tiles + 7) / 8 * 8;
+}
+
 template <int DT, int LA, int LB, int GRP, int EPI, int USE>
 static hipError_t run(const GemmArgs& g, hipStream_t s) {
     const int ntn = gemm_n_tiles(EPI, g.N, g.I);
-    int mtm = 0;
-    int64_t tiles;
-    if (GRP == G_M) {
-        // upper bound of sum_e ceil(M_e / BM)
-        int64_t mt = (g.rows + (int64_t)g.E * (kGemmBM - 1)) / kGemmBM;
-        tiles = mt * ntn;
-    } else {
-        mtm = (g.M + kGemmBM - 1) / kGemmBM;
-        tiles = (int64_t)g.E * mtm * ntn;
-    }
-    if (tiles == 0) return hipSuccess;
-    int64_t grid = (tiles + 7) / 8 * 8;
+    const int mtm = GRP == G_M ? 0 : (g.M + kGemmBM - 1) / kGemmBM;
+    const int64_t grid = gemm_slots(GRP, EPI, g.rows, g.E, g.M, g.N, g.I);
+    if (grid == 0) return hipSuccess;
     TraceScope ts(g.name ? g.name : "gemm", s);
     gemm_kernel<DT, LA, LB, GRP, EPI, USE><<<(unsigned)grid, kGemmThreads, 0, s>>>(g, ntn, mtm);
     return hipGetLastError();

@@ -59,6 +59,10 @@ hipError_t launch_quant(const MatTable& src, int nmat, const int32_t* sizes, int
 size_t amax_workspace_bytes(int nmat);
 hipError_t launch_amax(const MatTable& src, int nmat, int64_t n, void* ws, float* amax,
                        hipStream_t s, const char* name);
+// The final reduction alone, over per-workgroup partials written elsewhere
+// (the FP8 SwiGLU GEMM epilogues): amax[0] = the largest of part[0..nparts).
+hipError_t launch_amax_final(const uint32_t* part, int nparts, float* amax, hipStream_t s,
+                             const char* name);
 hipError_t launch_quant_rows(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, int64_t rows, int64_t cols, hipStream_t s,
                              const char* name = "mx_quant_rows", bool scales_t = false);

@@ -48,10 +48,12 @@ size_t colwise_codes(int64_t rows, int64_t cols, int E) {
 
 struct FwdWs {
     uint8_t *xq, *xq_s, *w1q, *w1q_s, *w2q, *w2q_s, *a2q, *a2q_s;
-    // FP8: bf16 A2 before its cast, the tensor maxima (xp, W1_e, W2_e, A2) and
-    // the amax reduction's partials
+    // FP8: bf16 A2 before its cast, the tensor maxima (xp, W1_e, W2_e, A2), the
+    // amax reduction's partials, and the gate_up GEMM's per-workgroup maxima of A2
     uint8_t *a2bf, *amax_ws;
     float* amax;
+    uint32_t* a2_part;
+    int a2_nparts;
     size_t bytes;
 };
 
@@ -72,6 +74,8 @@ FwdWs carve_fwd(void* base, int64_t rows, int H, int I, int E, int precision) {
         w.a2bf = c.take((size_t)rows * I * 2);
         w.amax = (float*)c.take((size_t)(2 * E + 2) * sizeof(float));
         w.amax_ws = c.take(amax_workspace_bytes(E));
+        w.a2_nparts = (int)gemm_slots(G_M, EPI_SWIGLU_FWD, rows, E, 0, 2 * I, I);
+        w.a2_part = (uint32_t*)c.take((size_t)w.a2_nparts * sizeof(uint32_t));
     }
     c.take(256);
     w.bytes = c.off;
@@ -82,6 +86,8 @@ struct BwdWs {
     uint8_t *da1;           // bf16 [rows, 2I] (BF16 mode; FP8: before its cast)
     float* amax;            // FP8: maxima of dYp, W2_e, W1_e, dA1
     uint8_t* amax_ws;
+    uint32_t* da1_part;     // FP8: the down dgrad GEMM's per-workgroup maxima of dA1
+    int da1_nparts;
     uint8_t *dyq, *dyq_s;   // rowwise dYp
     uint8_t *dyc, *dyc_s;   // grouped columnwise dYp
     uint8_t *w2c, *w2c_s;   // W2 quantized along H: [E][I, H]
@@ -119,6 +125,8 @@ BwdWs carve_bwd(void* base, int64_t rows, int H, int I, int E, int precision) {
         w.da1 = c.take((size_t)rows * 2 * I * 2);
         w.amax = (float*)c.take((size_t)(2 * E + 2) * sizeof(float));
         w.amax_ws = c.take(amax_workspace_bytes(E));
+        w.da1_nparts = (int)gemm_slots(G_M, EPI_SWIGLU_BWD, rows, E, 0, I, I);
+        w.da1_part = (uint32_t*)c.take((size_t)w.da1_nparts * sizeof(uint32_t));
     }
     c.take(256);
     w.bytes = c.off;
@@ -310,6 +318,7 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     g.a1 = saved->a1;
     if (fp8) {
         g.act = (bf16_t*)w.a2bf;
+        g.amax_part = w.a2_part;
         g.name = "gemm_fp8_gateup_fwd_swiglu";
     } else {
         g.q_row = w.a2q;
@@ -326,7 +335,8 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
         ccd.p[0] = saved->a2_col_codes;
         csc.p[0] = saved->a2_col_scales;
         float* aa2 = w.amax + 2 * E + 1;
-        MOE_TRY(launch_amax(src, 1, rows * I, w.amax_ws, aa2, stream, "fp8_amax_a2"));
+        // the maximum from the GEMM epilogue's per-workgroup partials
+        MOE_TRY(launch_amax_final(w.a2_part, w.a2_nparts, aa2, stream, "fp8_amax_a2"));
         MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, I, &cd, &sc, true, &ccd, &csc, true,
                              stream, "fp8_quant_a2", aa2));
     }
@@ -536,6 +546,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         g.dprob_part = w.part;
         if (fp8) {
             g.act = (bf16_t*)w.da1;
+            g.amax_part = w.da1_part;
             g.name = "gemm_fp8_down_dgrad_swiglu_bwd";
         } else {
             g.q_row = w.da1q;
@@ -554,7 +565,8 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
             ccd.p[0] = w.da1c;
             csc.p[0] = w.da1c_s;
             float* ad = w.amax + 2 * E + 1;
-            MOE_TRY(launch_amax(src, 1, rows * 2 * I, w.amax_ws, ad, stream, "fp8_amax_da1"));
+            // the maximum from the GEMM epilogue's per-workgroup partials
+            MOE_TRY(launch_amax_final(w.da1_part, w.da1_nparts, ad, stream, "fp8_amax_da1"));
             MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, 2 * (int64_t)I, &cd, &sc, true,
                                  &ccd, &csc, true, stream, "fp8_quant_da1", ad));
         }

@@ -59,6 +59,8 @@ struct GemmArgs {
     uint8_t* q_col;     // MXFP8 grouped columnwise codes of the epilogue output
     uint8_t* q_col_s;
     float* dprob_part;  // SWIGLU_BWD: [rows, n_tiles]
+    uint32_t* amax_part;  // FP8 SwiGLU epilogues: per workgroup, the largest |bf16| bit
+                          // pattern of the stored output ([gemm_slots(...)]; 0 if none)
     int I;              // intermediate size (SwiGLU epilogues)
     const char* name;   // kernel name in launch traces
 };
@@ -67,6 +69,8 @@ hipError_t launch_gemm(int dtype, int use, const GemmArgs& g, hipStream_t s);
 hipError_t launch_dprob_reduce(const float* part, int64_t rows, int ntiles, float* dprob,
                                hipStream_t s);
 int gemm_n_tiles(int epi, int N, int I);
+// Workgroups (tile slots, a multiple of 8) of one grouped GEMM launch.
+int64_t gemm_slots(int grp, int epi, int64_t rows, int E, int M, int N, int I);
 
 size_t mlp_fwd_workspace_bytes(int64_t rows, int H, int I, int E, int precision);
 size_t mlp_bwd_workspace_bytes(int64_t rows, int H, int I, int E, int precision);

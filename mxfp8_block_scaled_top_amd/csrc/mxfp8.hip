@@ -335,6 +335,13 @@ __global__ __launch_bounds__(256) void amax_final_kernel(const uint32_t* __restr
 }
 
 // ---------------------------------------------------------------- launchers
+hipError_t launch_amax_final(const uint32_t* part, int nparts, float* amax, hipStream_t s,
+                             const char* name) {
+    TraceScope ts(name, s);
+    amax_final_kernel<<<1, 256, 0, s>>>(part, nparts, amax);
+    return hipGetLastError();
+}
+
 size_t amax_workspace_bytes(int nmat) { return (size_t)nmat * kAmaxParts * sizeof(uint32_t) + 256; }
 
 hipError_t launch_amax(const MatTable& src, int nmat, int64_t n, void* ws, float* amax,
