@@ -64,6 +64,7 @@ constexpr int kStageB = 2 * kTileB;           // A + B
 constexpr int kLdsB = kStages * kStageB;      // 128 KiB
 constexpr int kMNRowB = kGemmBM * 2;          // M/N-contiguous LDS row: 256 bf16 = 512 B
 constexpr uint32_t kOob = 0x80000000u;        // buffer offset that reads zeros
+constexpr int kTailRows = 2;                  // fragment rows of a K step computed after its barrier
 
 // K-contiguous tile: row r, 16-byte chunk c (4 per row); XOR with (r>>2)&3
 // makes the 16-byte reads of 16 consecutive rows hit 16 distinct bank groups.
@@ -837,33 +838,35 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     };
 
     const int fr = lane & 31, hi = lane >> 5;
-    // compute one K step from stage S
-    auto compute = [&](auto S) {
+    // The operand fragments of one K step, held in registers.  Two sets
+    // alternate: while the MFMAs consume step k's set, the LDS reads of step
+    // k+1 fill the other, so LDS latency is hidden behind matrix work instead
+    // of stalling the wave before each group of MFMAs.
+    struct FragsMX { i32x8 a[4]; i32x8 b[4]; uint32_t sa[4]; uint32_t sb[4]; };
+    struct FragsBF { bf16x8_t a[2][4]; bf16x8_t b[2][4]; };
+    using Frags = std::conditional_t<DT == DT_BF16, FragsBF, FragsMX>;
+
+    // LDS -> registers: every fragment of the K step held in stage S
+    auto load = [&](auto S, Frags& F) {
         constexpr int st = decltype(S)::value % kStages;
         const uint8_t* A = stage_ptr(S);
         const uint8_t* B = A + kTileB;
-        if (DT == DT_BF16) {
+        if constexpr (DT == DT_BF16) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                bf16x8_t bfr[4];
 #pragma unroll
                 for (int fj = 0; fj < 4; ++fj) {
                     if (LB == L_KMAJ)
-                        bfr[fj] = *(const bf16x8_t*)(B + lds_off(wn * 128 + fj * 32 + fr, s * 2 + hi));
+                        F.b[s][fj] = *(const bf16x8_t*)(B + lds_off(wn * 128 + fj * 32 + fr, s * 2 + hi));
                     else
-                        bfr[fj] = mn_frag(B, s, wn * 128 + fj * 32);
+                        F.b[s][fj] = mn_frag(B, s, wn * 128 + fj * 32);
                 }
 #pragma unroll
                 for (int fi = 0; fi < 4; ++fi) {
-                    bf16x8_t af;
                     if (LA == L_KMAJ)
-                        af = *(const bf16x8_t*)(A + lds_off(wm * 128 + fi * 32 + fr, s * 2 + hi));
+                        F.a[s][fi] = *(const bf16x8_t*)(A + lds_off(wm * 128 + fi * 32 + fr, s * 2 + hi));
                     else
-                        af = mn_frag(A, s, wm * 128 + fi * 32);
-#pragma unroll
-                    for (int fj = 0; fj < 4; ++fj)
-                        acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[fj],
-                                                                              acc[fi][fj], 0, 0, 0);
+                        F.a[s][fi] = mn_frag(A, s, wm * 128 + fi * 32);
                 }
             }
         } else {
@@ -871,29 +874,44 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
             // holds K [16h, 16h+16) and [32+16h, 32+16h+16) of the 64-K step;
             // the E8M0 scale of K-block 0 of row r is taken from lane r, that
             // of block 1 from lane r+32 (byte h of the staged scale pair).
-            i32x8 bfr[4];
-            uint32_t sb[4];
 #pragma unroll
             for (int fj = 0; fj < 4; ++fj) {
                 int row = wn * 128 + fj * 32 + fr;
                 u32x4 lo = *(const u32x4*)(B + lds_off(row, hi));
                 u32x4 up = *(const u32x4*)(B + lds_off(row, 2 + hi));
-                bfr[fj] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                F.b[fj] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                   (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
-                sb[fj] = ssc[st][1][hi][row];           // byte -> low 8 bits
+                F.sb[fj] = ssc[st][1][hi][row];          // byte -> low 8 bits
             }
 #pragma unroll
             for (int fi = 0; fi < 4; ++fi) {
                 int row = wm * 128 + fi * 32 + fr;
                 u32x4 lo = *(const u32x4*)(A + lds_off(row, hi));
                 u32x4 up = *(const u32x4*)(A + lds_off(row, 2 + hi));
-                i32x8 af = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                   (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
-                uint32_t sa = ssc[st][0][hi][row];
+                F.a[fi] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                  (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+                F.sa[fi] = ssc[st][0][hi][row];
+            }
+        }
+    };
+    // the MFMAs of fragment rows [FI0, FI1) of one K step; each accumulator
+    // takes the step's K values in increasing order whatever the split
+    auto mma = [&](auto FI0, auto FI1, const Frags& F) {
+        constexpr int f0 = decltype(FI0)::value, f1 = decltype(FI1)::value;
+#pragma unroll
+        for (int fi = f0; fi < f1; ++fi) {
+            if constexpr (DT == DT_BF16) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int fj = 0; fj < 4; ++fj)
+                        acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            F.a[s][fi], F.b[s][fj], acc[fi][fj], 0, 0, 0);
+            } else {
 #pragma unroll
                 for (int fj = 0; fj < 4; ++fj)
                     acc[fi][fj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        af, bfr[fj], acc[fi][fj], 0, 0, 0, (int)sa, 0, (int)sb[fj]);
+                        F.a[fi], F.b[fj], acc[fi][fj], 0, 0, 0, (int)F.sa[fi], 0, (int)F.sb[fj]);
             }
         }
     };
@@ -901,13 +919,27 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
-    // one K step kt held in stage S: prefetch step kt+3 into stage S+3, compute,
-    // wait for step kt+1's batch, publish its scales
-    auto step = [&](auto S, int kt) {
+    using I4 = std::integral_constant<int, 4>;
+    // fragment rows whose MFMAs run after the barrier, under the next step's
+    // LDS reads
+    using ISplit = std::integral_constant<int, 4 - kTailRows>;
+    // One K step kt whose fragments are in Fc (read from stage S): prefetch
+    // step kt+3 into stage S+3 (whose reads all finished before the previous
+    // barrier), run most MFMAs, wait until batch kt+1 has landed in every
+    // wave, read its fragments into Fn, and run the remaining MFMAs.
+    Frags F0, F1;
+    auto step = [&](auto S, int kt, Frags& Fc, Frags& Fn) {
         constexpr int st = decltype(S)::value;
+        // (scheduling barriers keep the compiler from sinking the reads of Fn
+        // to their first use, which would stall the next step's MFMAs on LDS)
         issue(std::integral_constant<int, (st + 3) % kStages>{}, kt + 3);
-        compute(S);
+        mma(I0{}, ISplit{}, Fc);
+        __builtin_amdgcn_sched_barrier(0);
         pipe_barrier<kWait2>();                                  // batch kt+1 has landed
+        __builtin_amdgcn_sched_barrier(0);
+        load(std::integral_constant<int, (st + 1) % kStages>{}, Fn);
+        mma(ISplit{}, I4{}, Fc);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     if (nk > 0) {
@@ -916,19 +948,21 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         issue(I2{}, 2);
     }
     pipe_barrier<kWait2>();                                      // batch 0 has landed
+    load(I0{}, F0);
+    __builtin_amdgcn_sched_barrier(0);
     // whole groups of four steps, then the rest: a conditional step inside
     // the loop body makes the register allocator shuttle accumulators
     // between register files on every iteration
     int kt = 0;
     for (; kt + kStages <= nk; kt += kStages) {
-        step(I0{}, kt);
-        step(I1{}, kt + 1);
-        step(I2{}, kt + 2);
-        step(I3{}, kt + 3);
+        step(I0{}, kt, F0, F1);
+        step(I1{}, kt + 1, F1, F0);
+        step(I2{}, kt + 2, F0, F1);
+        step(I3{}, kt + 3, F1, F0);
     }
-    if (kt < nk) step(I0{}, kt);
-    if (kt + 1 < nk) step(I1{}, kt + 1);
-    if (kt + 2 < nk) step(I2{}, kt + 2);
+    if (kt < nk) step(I0{}, kt, F0, F1);
+    if (kt + 1 < nk) step(I1{}, kt + 1, F1, F0);
+    if (kt + 2 < nk) step(I2{}, kt + 2, F0, F1);
     // the look-ahead batches past the end still write LDS: drain them before
     // the epilogue reuses it
     pipe_barrier<0>();
