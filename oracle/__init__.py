@@ -1,7 +1,7 @@
 """CPU oracle for the grouped MoE expert MLP (BF16 and MXFP8, forward and backward).
 
-TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the tests, the smoke check of the
-graft entry point and the CPU-baseline leg of the benchmark may import, call or
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the tests, smoke() in
+__graft_entry__.py and the CPU-baseline leg of bench.py may import, call or
 execute anything in this package.  The HIP library never routes through it and
 shares no code with it (no kernels, headers, helpers, tables or constants); the
 two meet only at the seeded input generator, which holds none of the method's
