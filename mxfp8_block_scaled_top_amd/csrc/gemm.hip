@@ -420,13 +420,14 @@ __device__ __forceinline__ uint32_t quant32(const float* x, u32x4& c0, u32x4& c1
     return S;
 }
 
-// Columnwise MXFP8 of column `col` of the staged region (32 rows, rows at or
-// past `valid` count as zero) into the grouped columnwise layout.
-__device__ __forceinline__ void col_quant(const float* R, int col, int valid, uint8_t* codes,
+// Columnwise MXFP8 of column `col` of the staged region (32 rows; the
+// callers stage zeros for the rows past the expert, so all 32 are read
+// unconditionally) into the grouped columnwise layout.
+__device__ __forceinline__ void col_quant(const float* R, int col, uint8_t* codes,
                                           uint8_t* scale) {
     float x[32];
 #pragma unroll
-    for (int r = 0; r < 32; ++r) x[r] = r < valid ? R[st_idx(r, col)] : 0.f;
+    for (int r = 0; r < 32; ++r) x[r] = R[st_idx(r, col)];
     u32x4 c0, c1;
     uint32_t S = quant32(x, c0, c1);
     ((u32x4*)codes)[0] = c0;
@@ -510,7 +511,7 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
     if (DT == DT_MX && valid > 0) {
         const int q = lane >> 5, jj = lane & 31;
         const int64_t j = tl.n_tile * (kGemmBN / 2) + (2 * c.wn + q) * 32 + jj;
-        col_quant(R, 64 * q + jj, valid, g.q_col + tl.pbase * I + j * tl.pad_e + frow0,
+        col_quant(R, 64 * q + jj, g.q_col + tl.pbase * I + j * tl.pad_e + frow0,
                   g.q_col_s + tl.pbase / 32 * I + (frow0 / 32) * I + j);
     }
     __syncthreads();
@@ -666,7 +667,7 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
             const int col = lane + 64 * t;                  // 0..127 dg, 128..255 du
             const int cc = col & 127;
             const int64_t j = (col < 128 ? 0 : I) + jw + cc;
-            col_quant(col < 128 ? R : R2, cc, valid,
+            col_quant(col < 128 ? R : R2, cc,
                       g.q_col + tl.pbase * 2 * I + j * tl.pad_e + frow0,
                       g.q_col_s + tl.pbase / 32 * 2 * I + (frow0 / 32) * 2 * I + j);
         }
