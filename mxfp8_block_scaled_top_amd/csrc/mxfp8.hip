@@ -181,7 +181,8 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
                                   hi_bf16(v[j][1]), S);
                 o[1] = mx_encode4(lo_bf16(v[j][2]), hi_bf16(v[j][2]), lo_bf16(v[j][3]),
                                   hi_bf16(v[j][3]), S);
-                *(u32x2*)(rc + j * cols) = o;
+                // whole 512-byte runs per instruction: streamed past L2
+                __builtin_nontemporal_store(o, (u32x2*)(rc + j * cols));
                 if (a.rscales_t) {
                     if ((j >> 3) == s) sp[(j >> 2) & 1] |= S << (8 * (j & 3));
                 } else if (s == 0) {
