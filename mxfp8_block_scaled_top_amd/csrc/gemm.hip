@@ -362,6 +362,13 @@ __device__ __forceinline__ float half_sum32(float v) {
 //   phase 2  lane (row = lane/2, half = lane&1) handles 32-column blocks of
 //            one row: SwiGLU math, bf16 stores, rowwise MXFP8 (codes + scale);
 //   phase 3  lane = column: the 32 rows of one column -> columnwise MXFP8.
+// The epilogues stage through each wave's own LDS region: between their
+// phases a wave only waits for its own LDS accesses (a workgroup barrier
+// would make the four waves run their store bursts in lockstep).  The empty
+// asm's memory clobber also keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ int st_idx(int row, int col) {
     return row * 128 + ((((col >> 2) ^ (row & 7))) << 2) + (col & 3);
 }
@@ -459,7 +466,7 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
     const int lane = c.lane;
     const int64_t I = g.I;
     stage_fragments(R, f0, f1, f2, f3, lane);
-    __syncthreads();
+    wave_lds_sync();
     const int frow0 = tl.m0 + c.wm * 128 + fi * 32;      // row inside the expert
     const int valid = min(32, tl.rows_e - frow0);          // rows of this slice that exist
     {
@@ -507,14 +514,14 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
 #pragma unroll
             for (int b = 0; b < 4; ++b) store_row8(R, row, 64 * q + 8 * b, a2 + 8 * b);
     }
-    __syncthreads();
+    wave_lds_sync();
     if (DT == DT_MX && valid > 0) {
         const int q = lane >> 5, jj = lane & 31;
         const int64_t j = tl.n_tile * (kGemmBN / 2) + (2 * c.wn + q) * 32 + jj;
         col_quant(R, 64 * q + jj, g.q_col + tl.pbase * I + j * tl.pad_e + frow0,
                   g.q_col_s + tl.pbase / 32 * I + (frow0 / 32) * I + j);
     }
-    __syncthreads();
+    wave_lds_sync();
 }
 
 // SwiGLU backward of row slice fi: staged columns are dA2 for j = n0 + wn*128
@@ -530,7 +537,7 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
     const int lane = c.lane;
     const int64_t I = g.I;
     stage_fragments(R, f0, f1, f2, f3, lane);
-    __syncthreads();
+    wave_lds_sync();
     const int frow0 = tl.m0 + c.wm * 128 + fi * 32;
     const int valid = min(32, tl.rows_e - frow0);
     const int jw = tl.n0 + c.wn * 128;                      // first column of the wave
@@ -660,7 +667,7 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
     }
     part += __shfl_xor(part, 1);
     if (h == 0) red[c.wn * kGemmBM + c.wm * 128 + fi * 32 + row] = part;
-    __syncthreads();
+    wave_lds_sync();
     if (DT == DT_MX && slab && valid > 0) {
 #pragma unroll 1
         for (int t = 0; t < 4; ++t) {
@@ -672,7 +679,7 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
                       g.q_col_s + tl.pbase / 32 * 2 * I + (frow0 / 32) * 2 * I + j);
         }
     }
-    __syncthreads();
+    wave_lds_sync();
 }
 
 // The lane index recomputed from the execution mask (all lanes are active)
@@ -993,7 +1000,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
 #pragma unroll
         for (int fi = 0; fi < 4; ++fi) {
             stage_fragments(R, acc[fi][0], acc[fi][1], acc[fi][2], acc[fi][3], ln);
-            __syncthreads();
+            wave_lds_sync();
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int row = (ln >> 4) + 4 * i;
@@ -1007,7 +1014,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
                                                 (u32x4*)(C + (int64_t)grow * ldc + gcol));
                 }
             }
-            __syncthreads();
+            wave_lds_sync();
         }
         return;
     }
@@ -1046,6 +1053,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2, amx);
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[3][0], acc[3][1], acc[3][2], acc[3][3], 3, amx);
         if (kAmax) amax_to_part(amx, (uint32_t*)sched, g.amax_part);
+        __syncthreads();                    // red holds both column halves' partials
         const int t = wave * 64 + ln;
         if (tl.m0 + t < tl.rows_e)
             g.dprob_part[(tl.row0 + tl.m0 + t) * (int64_t)ntn + tl.n_tile] =
