@@ -470,14 +470,32 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
     const int frow0 = tl.m0 + c.wm * 128 + fi * 32;      // row inside the expert
     const int valid = min(32, tl.rows_e - frow0);          // rows of this slice that exist
     {
+        // A1, gate and up of the wave's 64 j: 8 lanes write one row's
+        // 128-byte line, 8 rows per instruction, streamed past L2 (whole
+        // lines, read again only by the backward)
+        const int c8 = lane & 7;
+        const int64_t jw0 = tl.n_tile * (kGemmBN / 2) + 2 * c.wn * 32 + 8 * c8;
+        const int scol = 64 * (c8 >> 2) + 8 * (c8 & 3);   // staged column of the 8 gate values
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (lane >> 3) + 8 * i;
+            if (row < valid) {
+                const int64_t gr = tl.row0 + frow0 + row;
+                float x[8];
+                load_row8(R, row, scol, x);
+                __builtin_nontemporal_store(pack8_bf16(x), (u32x4*)(g.a1 + gr * 2 * I + jw0));
+                load_row8(R, row, scol + 32, x);
+                __builtin_nontemporal_store(pack8_bf16(x), (u32x4*)(g.a1 + gr * 2 * I + I + jw0));
+            }
+        }
+    }
+    {
         const int row = lane >> 1, q = lane & 1;
         const int j0 = tl.n_tile * (kGemmBN / 2) + (2 * c.wn + q) * 32;
         float a2[32];
         if (row < valid) {
             const int64_t gr = tl.row0 + frow0 + row;
             const float p = c.pr[fi];
-            u32x4* a1g = (u32x4*)(g.a1 + gr * 2 * I + j0);
-            u32x4* a1u = (u32x4*)(g.a1 + gr * 2 * I + I + j0);
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 float gt[8], up[8];
@@ -485,8 +503,6 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
                 load_row8(R, row, 64 * q + 32 + 8 * b, up);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) a2[8 * b + i] = p * silu_f(gt[i]) * up[i];
-                a1g[b] = pack8_bf16(gt);
-                a1u[b] = pack8_bf16(up);
             }
             if (DT != DT_MX) {          // bf16 A2 (BF16, and FP8: cast later)
                 u32x4* o = (u32x4*)(g.act + gr * I + j0);
