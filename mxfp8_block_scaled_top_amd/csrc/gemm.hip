@@ -540,6 +540,49 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
     wave_lds_sync();
 }
 
+// The saved gate/up values of a backward slice (32 rows, the wave's 128 j),
+// read in whole 128-byte lines (8 lanes per line of a row, streamed past L2)
+// and staged as (gate, up) bf16 pairs, one pair per fp32 slot of R2, where
+// the row-per-lane arithmetic reads them.  Rows past the expert stage zeros.
+// (float4 accesses throughout, like the du stores that later reuse the
+// slots, so the compiler keeps their order.)
+__device__ __forceinline__ void stage_a1_pairs(const GemmArgs& g, const Tile& tl, float* R2,
+                                               int frow0, int valid, int jw, int lane) {
+    const int64_t I = g.I;
+    const int c8 = lane & 7;
+    u32x4 wg[4][2], wu[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int row = (lane >> 3) + 8 * i, col = 64 * s + 8 * c8;
+            wg[i][s] = wu[i][s] = (u32x4){0u, 0u, 0u, 0u};
+            if (row < valid) {
+                const bf16_t* a = g.a1 + (tl.row0 + frow0 + row) * 2 * I + jw + col;
+                wg[i][s] = __builtin_nontemporal_load((const u32x4*)a);
+                wu[i][s] = __builtin_nontemporal_load((const u32x4*)(a + I));
+            }
+        }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int row = (lane >> 3) + 8 * i, col = 64 * s + 8 * c8;
+            float x[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {      // word k: columns 2k, 2k+1
+                const uint32_t gw = wg[i][s][k], uw = wu[i][s][k];
+                x[2 * k] = __uint_as_float((gw & 0xffffu) | (uw << 16));
+                x[2 * k + 1] = __uint_as_float((gw >> 16) | (uw & 0xffff0000u));
+            }
+            store_row8(R2, row, col, x);
+        }
+}
+
+// (gate, up) of staged pair x
+__device__ __forceinline__ float pair_gate(float x) { return lo_bf16(__float_as_uint(x)); }
+__device__ __forceinline__ float pair_up(float x) { return hi_bf16(__float_as_uint(x)); }
+
 // SwiGLU backward of row slice fi: staged columns are dA2 for j = n0 + wn*128
 // + col.  Writes dA1 (bf16, or rowwise + columnwise MXFP8) and the row's
 // probability-gradient partial over these 128 columns into red.
@@ -559,25 +602,13 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
     const int jw = tl.n0 + c.wn * 128;                      // first column of the wave
     const bool slab = jw < I;                              // I % 128 == 0: all or nothing
     const int row = lane >> 1, h = lane & 1;
+    if (slab && valid > 0) stage_a1_pairs(g, tl, R2, frow0, valid, jw, lane);
+    wave_lds_sync();
     float part = 0.f;
     if (DT != DT_MX) {
         if (slab && row < valid) {
             const int64_t gr = tl.row0 + frow0 + row;
             const float p = c.pr[fi];
-            // both blocks' saved values before any store (the stores may alias
-            // them for the compiler): one round trip
-            u32x4 wg[2][4], wu[2][4];
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                const int cb = 64 * h + 32 * blk;
-                const u32x4* a1g = (const u32x4*)(g.a1 + gr * 2 * I + jw + cb);
-                const u32x4* a1u = (const u32x4*)(g.a1 + gr * 2 * I + I + jw + cb);
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    wg[blk][b] = a1g[b];
-                    wu[blk][b] = a1u[b];
-                }
-            }
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
             const int cb = 64 * h + 32 * blk;               // staged column of the block
@@ -585,10 +616,14 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
             u32x4* ou = (u32x4*)(g.act + gr * 2 * I + I + jw + cb);
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                float d[8], gt[8], up[8], dg[8], du[8];
+                float d[8], pr8[8], gt[8], up[8], dg[8], du[8];
                 load_row8(R, row, cb + 8 * b, d);
-                unpack8_bf16(wg[blk][b], gt);
-                unpack8_bf16(wu[blk][b], up);
+                load_row8(R2, row, cb + 8 * b, pr8);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    gt[i] = pair_gate(pr8[i]);
+                    up[i] = pair_up(pr8[i]);
+                }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     float sg = sigmoid_f(gt[i]);
@@ -610,34 +645,25 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
         }
     } else {
         // phase 1, 8 values at a time: dg replaces the staged dA2 in R, du
-        // goes to R2 (rows past the expert stay zero for the column blocks)
+        // replaces the staged gate/up pairs in R2 (rows past the expert stay
+        // zero for the column blocks)
         const bool live = slab && row < valid;
-        const int64_t gr = tl.row0 + frow0 + row;
         const float p = live ? c.pr[fi] : 0.f;
-        // both blocks' saved gate/up values in one round trip
-        u32x4 wg[2][4], wu[2][4];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const int cb = 64 * h + 32 * blk;
-            const u32x4* a1g = (const u32x4*)(g.a1 + gr * 2 * I + jw + cb);
-            const u32x4* a1u = (const u32x4*)(g.a1 + gr * 2 * I + I + jw + cb);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                wg[blk][b] = live ? a1g[b] : (u32x4){0, 0, 0, 0};
-                wu[blk][b] = live ? a1u[b] : (u32x4){0, 0, 0, 0};
-            }
-        }
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             const int cb = 64 * h + 32 * blk;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                float d[8], dg[8], du[8];
+                float d[8], pr8[8], dg[8], du[8];
                 load_row8(R, row, cb + 8 * b, d);
+                load_row8(R2, row, cb + 8 * b, pr8);     // read before du takes the slots
                 if (live) {
                     float gt[8], up[8];
-                    unpack8_bf16(wg[blk][b], gt);
-                    unpack8_bf16(wu[blk][b], up);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        gt[i] = pair_gate(pr8[i]);
+                        up[i] = pair_up(pr8[i]);
+                    }
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         float sg = sigmoid_f(gt[i]);
