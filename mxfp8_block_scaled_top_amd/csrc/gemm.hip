@@ -605,45 +605,7 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
     if (slab && valid > 0) stage_a1_pairs(g, tl, R2, frow0, valid, jw, lane);
     wave_lds_sync();
     float part = 0.f;
-    if (DT != DT_MX) {
-        if (slab && row < valid) {
-            const int64_t gr = tl.row0 + frow0 + row;
-            const float p = c.pr[fi];
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-            const int cb = 64 * h + 32 * blk;               // staged column of the block
-            u32x4* og = (u32x4*)(g.act + gr * 2 * I + jw + cb);
-            u32x4* ou = (u32x4*)(g.act + gr * 2 * I + I + jw + cb);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                float d[8], pr8[8], gt[8], up[8], dg[8], du[8];
-                load_row8(R, row, cb + 8 * b, d);
-                load_row8(R2, row, cb + 8 * b, pr8);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    gt[i] = pair_gate(pr8[i]);
-                    up[i] = pair_up(pr8[i]);
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    float sg = sigmoid_f(gt[i]);
-                    float sl = gt[i] * sg;
-                    float dp = d[i] * p;
-                    dg[i] = dp * up[i] * sg * (1.f + gt[i] * (1.f - sg));
-                    du[i] = dp * sl;
-                    part += d[i] * sl * up[i];
-                }
-                const u32x4 pg = pack8_bf16(dg), pu = pack8_bf16(du);
-                og[b] = pg;
-                ou[b] = pu;
-                if (DT == DT_FP8)       // the tensor maximum of the cast that follows
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        amx = max_abs_bf16x2(max_abs_bf16x2(amx, pg[q]), pu[q]);
-            }
-            }
-        }
-    } else {
+    {
         // phase 1, 8 values at a time: dg replaces the staged dA2 in R, du
         // replaces the staged gate/up pairs in R2 (rows past the expert stay
         // zero for the column blocks)
@@ -681,6 +643,37 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
                 store_row8(R2, row, cb + 8 * b, du);
             }
         }
+    }
+    if (DT != DT_MX) {
+        // bf16 dA1 = [dg, du] in whole 128-byte lines: 8 lanes per line of a
+        // row, 8 rows per instruction, streamed past L2
+        wave_lds_sync();
+        if (slab) {
+            const int c8 = lane & 7;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = (lane >> 3) + 8 * i;
+                if (r < valid) {
+                    const int64_t gr = tl.row0 + frow0 + r;
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const int col = 64 * s + 8 * c8;
+                        float x[8];
+                        load_row8(R, r, col, x);
+                        const u32x4 pg = pack8_bf16(x);
+                        load_row8(R2, r, col, x);
+                        const u32x4 pu = pack8_bf16(x);
+                        __builtin_nontemporal_store(pg, (u32x4*)(g.act + gr * 2 * I + jw + col));
+                        __builtin_nontemporal_store(pu, (u32x4*)(g.act + gr * 2 * I + I + jw + col));
+                        if (DT == DT_FP8)   // the tensor maximum of the cast that follows
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                amx = max_abs_bf16x2(max_abs_bf16x2(amx, pg[q]), pu[q]);
+                    }
+                }
+            }
+        }
+    } else {
         // phase 2: rowwise MXFP8 of the lane's own 32-column blocks (the same
         // lane wrote them, so no barrier is needed)
         if (slab && row < valid) {
