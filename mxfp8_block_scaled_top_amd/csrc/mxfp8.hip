@@ -25,19 +25,43 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(const u32x4* __restri
                                                            const uint8_t* __restrict__ scales,
                                                            int64_t nblocks,
                                                            u32x4* __restrict__ out) {
-    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks;
-         b += (int64_t)gridDim.x * blockDim.x) {
-        u32x4 c[2] = {codes[2 * b], codes[2 * b + 1]};
-        uint32_t S = scales[b];
+    // A wave covers 64 consecutive 32-value blocks; in step q, lane l handles
+    // 8 values: piece l&3 of block q*16 + l/4, so every load reads 512
+    // contiguous code bytes and every store writes 1 KiB of whole lines.
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (nblocks + 63) / 64;
+    const int64_t stride = (int64_t)gridDim.x * (blockDim.x / 64);
+    const u32x2* cw = (const u32x2*)codes;
+    for (int64_t w = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); w < nwaves;
+         w += stride) {
+        u32x2 c[4];
+        uint32_t S[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            uint32_t w0 = c[q >> 1][(q & 1) * 2], w1 = c[q >> 1][(q & 1) * 2 + 1];
-            u32x4 o;
-            o[0] = pack_bf16x2(mx_decode(w0 & 0xff, S), mx_decode((w0 >> 8) & 0xff, S));
-            o[1] = pack_bf16x2(mx_decode((w0 >> 16) & 0xff, S), mx_decode(w0 >> 24, S));
-            o[2] = pack_bf16x2(mx_decode(w1 & 0xff, S), mx_decode((w1 >> 8) & 0xff, S));
-            o[3] = pack_bf16x2(mx_decode((w1 >> 16) & 0xff, S), mx_decode(w1 >> 24, S));
-            out[4 * b + q] = o;
+            const int64_t blk = w * 64 + q * 16 + (lane >> 2);
+            c[q] = (u32x2){0u, 0u};
+            S[q] = 127u;
+            if (blk < nblocks) {
+                c[q] = cw[blk * 4 + (lane & 3)];
+                S[q] = scales[blk];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t blk = w * 64 + q * 16 + (lane >> 2);
+            if (blk < nblocks) {
+                // gfx950's scaled conversion, two codes per instruction: each
+                // code times 2^(S-127), rounded to nearest even bf16 (the same
+                // bits as mx_decode followed by that rounding, for every code
+                // and scale byte, overflow to infinity and underflow included)
+                const float scale = __builtin_ldexpf(1.f, (int)S[q] - 127);
+                u32x4 o;
+                o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[q][0], scale, false));
+                o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[q][0], scale, true));
+                o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[q][1], scale, false));
+                o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[q][1], scale, true));
+                out[blk * 4 + (lane & 3)] = o;
+            }
         }
     }
 }
