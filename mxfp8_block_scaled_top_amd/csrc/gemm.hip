@@ -1032,8 +1032,12 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         const int ln = lane_after_loop();
         const int c8 = (ln & 15) * 8;
         const int gcol = wn * 128 + c8;             // N is a multiple of 8: all or nothing
+        // (slices in reverse order: the compiler then keeps every accumulator
+        // in place through the epilogue instead of parking one fragment in
+        // scratch memory)
 #pragma unroll
-        for (int fi = 0; fi < 4; ++fi) {
+        for (int fr = 0; fr < 4; ++fr) {
+            const int fi = 3 - fr;
             stage_fragments(R, acc[fi][0], acc[fi][1], acc[fi][2], acc[fi][3], ln);
             wave_lds_sync();
 #pragma unroll
