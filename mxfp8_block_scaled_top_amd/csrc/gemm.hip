@@ -1074,10 +1074,12 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         EpiCtx c{g, tl, wm, wn, ntn, {pr[0], pr[1], pr[2], pr[3]}, ln};
         float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         uint32_t amx = 0;
-        swiglu_fwd_rows<DT>(c, R, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0, amx);
-        swiglu_fwd_rows<DT>(c, R, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1, amx);
-        swiglu_fwd_rows<DT>(c, R, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2, amx);
+        // (slices in reverse order, as in the plain-store epilogue: no
+        // accumulator fragment is parked in scratch memory)
         swiglu_fwd_rows<DT>(c, R, acc[3][0], acc[3][1], acc[3][2], acc[3][3], 3, amx);
+        swiglu_fwd_rows<DT>(c, R, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2, amx);
+        swiglu_fwd_rows<DT>(c, R, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1, amx);
+        swiglu_fwd_rows<DT>(c, R, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0, amx);
         if (kAmax) amax_to_part(amx, (uint32_t*)sched, g.amax_part);
         return;
     }
@@ -1087,10 +1089,11 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         float* R2 = R + 32 * 128;
         uint32_t amx = 0;
-        swiglu_bwd_rows<DT>(c, R, R2, red, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0, amx);
-        swiglu_bwd_rows<DT>(c, R, R2, red, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1, amx);
-        swiglu_bwd_rows<DT>(c, R, R2, red, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2, amx);
+        // (slices in reverse order: no accumulator fragment parked in scratch)
         swiglu_bwd_rows<DT>(c, R, R2, red, acc[3][0], acc[3][1], acc[3][2], acc[3][3], 3, amx);
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2, amx);
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1, amx);
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0, amx);
         if (kAmax) amax_to_part(amx, (uint32_t*)sched, g.amax_part);
         __syncthreads();                    // red holds both column halves' partials
         const int t = wave * 64 + ln;
