@@ -674,14 +674,31 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
             }
         }
     } else {
-        // phase 2: rowwise MXFP8 of the lane's own 32-column blocks (the same
-        // lane wrote them, so no barrier is needed)
+        // columnwise MXFP8 first (lane = column, its 32 rows; phase 1 staged
+        // zeros for the rows past the expert), while every staged value is
+        // still in place
+        wave_lds_sync();
+        if (slab && valid > 0) {
+#pragma unroll 1
+            for (int t = 0; t < 4; ++t) {
+                const int col = lane + 64 * t;              // 0..127 dg, 128..255 du
+                const int cc = col & 127;
+                const int64_t j = (col < 128 ? 0 : I) + jw + cc;
+                col_quant(col < 128 ? R : R2, cc,
+                          g.q_col + tl.pbase * 2 * I + j * tl.pad_e + frow0,
+                          g.q_col_s + tl.pbase / 32 * 2 * I + (frow0 / 32) * 2 * I + j);
+            }
+        }
+        wave_lds_sync();
+        // rowwise MXFP8 of the lane's own 32-column blocks: the block's 32
+        // code bytes replace its first 8 staged values (the lane has read all
+        // 32 of them)
         if (slab && row < valid) {
             const int64_t gr = tl.row0 + frow0 + row;
 #pragma unroll 1
             for (int q = 0; q < 4; ++q) {
                 const int cb = 64 * h + 32 * (q & 1);
-                const float* src = q < 2 ? R : R2;
+                float* src = q < 2 ? R : R2;
                 float x[32];
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
@@ -692,28 +709,33 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
                 }
                 u32x4 c0, c1;
                 uint32_t S = quant32(x, c0, c1);
+                *(float4*)(src + st_idx(row, cb)) = __builtin_bit_cast(float4, c0);
+                *(float4*)(src + st_idx(row, cb + 4)) = __builtin_bit_cast(float4, c1);
                 const int64_t j = (q < 2 ? 0 : I) + jw + cb;
-                u32x4* o = (u32x4*)(g.q_row + gr * 2 * I + j);
-                o[0] = c0;
-                o[1] = c1;
                 g.q_row_s[(j / 32) * g.rows + gr] = (uint8_t)S;
+            }
+        }
+        wave_lds_sync();
+        // the row codes in whole 128-byte lines (dg codes of the wave's 128 j,
+        // then du's): 8 lanes per line, 8 rows per instruction, streamed
+        if (slab) {
+            const int c8 = lane & 7;
+            const int scol = 32 * (c8 >> 1) + 4 * (c8 & 1);   // block c8/2, code half c8%2
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = (lane >> 3) + 8 * i;
+                if (r < valid) {
+                    const int64_t gr = tl.row0 + frow0 + r;
+                    const u32x4 cg = __builtin_bit_cast(u32x4, *(const float4*)(R + st_idx(r, scol)));
+                    const u32x4 cu = __builtin_bit_cast(u32x4, *(const float4*)(R2 + st_idx(r, scol)));
+                    __builtin_nontemporal_store(cg, (u32x4*)(g.q_row + gr * 2 * I + jw + 16 * c8));
+                    __builtin_nontemporal_store(cu, (u32x4*)(g.q_row + gr * 2 * I + I + jw + 16 * c8));
+                }
             }
         }
     }
     part += __shfl_xor(part, 1);
     if (h == 0) red[c.wn * kGemmBM + c.wm * 128 + fi * 32 + row] = part;
-    wave_lds_sync();
-    if (DT == DT_MX && slab && valid > 0) {
-#pragma unroll 1
-        for (int t = 0; t < 4; ++t) {
-            const int col = lane + 64 * t;                  // 0..127 dg, 128..255 du
-            const int cc = col & 127;
-            const int64_t j = (col < 128 ? 0 : I) + jw + cc;
-            col_quant(col < 128 ? R : R2, cc,
-                      g.q_col + tl.pbase * 2 * I + j * tl.pad_e + frow0,
-                      g.q_col_s + tl.pbase / 32 * 2 * I + (frow0 / 32) * 2 * I + j);
-        }
-    }
     wave_lds_sync();
 }
 
