@@ -23,7 +23,14 @@
 //     wave's LDS base + 16 l, so the lane picks the global chunk that fills
 //     its slot); 16-byte chunks of a 64-byte tile row are XOR-swizzled by
 //     (row >> 2) & 3 so fragment reads of 16 consecutive rows hit distinct
-//     banks.  Offsets past a row's valid K read zeros.
+//     banks.  Offsets past a row's valid K read zeros.  The fragments of
+//     step k+1 are read from LDS into a second register set right after the
+//     barrier that publishes them, under the last MFMAs of step k.
+//   * Epilogues: each wave stages its 128 x 128 result through its own LDS
+//     region, 32 rows at a time (last slice first), and syncs only on its
+//     own LDS accesses.  Outputs that a wave owns whole lines of (the plain
+//     stores, the saved A1, bf16 dA1, the backward's MXFP8 row codes) leave
+//     in whole 128-byte lines with streaming stores.
 //   * M/N-contiguous bf16 operands (the dgrad weights and both weight-gradient
 //     operands) are staged in LDS in their natural [k][m] order (16-byte
 //     chunks of a 512-byte row XOR-ed with 4*(k&3)) and turned into K-packed
