@@ -121,10 +121,15 @@ __device__ ColBlock locate_col_block(const int32_t* __restrict__ sizes, int ngro
 //               a quad reduction (DPP), and each lane encodes its 8 values and
 //               stores them as 8 bytes (512 contiguous bytes per wave and row).
 //   columnwise  a lane owns 8 whole 32-row column blocks: the maximum is a
-//               per-lane reduction and each column's 32 codes leave as two
-//               16-byte stores.  Block q of the walk goes to wave q % 4 of
-//               workgroup q / 4, so the four waves of a workgroup write the
-//               four neighbouring 32-byte pieces of a column's 128-byte line.
+//               per-lane reduction.  Block q of the walk goes to wave q % 4 of
+//               workgroup q / 4, so the four waves of a workgroup hold the
+//               four neighbouring 32-byte pieces of each column's 128 codes.
+//               When the four blocks share a group and all 512 columns
+//               exist, the codes meet in LDS and leave as 128-byte runs,
+//               eight threads to a column (whole lines when the group's
+//               padded size and start are multiples of 128); otherwise
+//               two neighbouring lanes store each column's 32 codes as one
+//               32-byte run.
 // Block maxima are taken on the bf16 bit patterns with the sign cleared
 // (ordered like the magnitudes), two at a time with packed 16-bit maxima.
 struct QuantTileArgs {
@@ -159,6 +164,18 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
     const int lane = threadIdx.x & 63;
     const ColBlock cb = locate_col_block(a.sizes, a.ngroups, a.rows,
                                          (int64_t)blockIdx.y * 4 + wv, lds);
+    // The workgroup's four blocks lie in one group and its 512 columns all
+    // exist: its column codes then leave through LDS as whole 128-byte lines
+    // (the four blocks' 32-byte pieces of a column are neighbours).
+    bool staged = false;
+    if constexpr (COLS) {
+        const int G = a.sizes ? a.ngroups : 1;
+        const int q0 = (int)blockIdx.y * 4;
+        int g0 = 0, g3 = 0;
+        while (g0 < G && lds[g0] <= q0) ++g0;
+        while (g3 < G && lds[g3] <= q0 + 3) ++g3;
+        staged = g3 < G && g0 == g3 && (int64_t)(blockIdx.x + 1) * 512 <= a.cols;
+    }
     // every field is the same across the wave
     const int valid = __builtin_amdgcn_readfirstlane(cb.valid);
     if (valid <= 0) return;
@@ -168,14 +185,17 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
     const int64_t pbase = __builtin_amdgcn_readfirstlane((int)cb.pbase);
     const int64_t cols = a.cols;
     const int64_t c0 = (int64_t)blockIdx.x * 512 + lane * 8;
-    if (c0 >= cols) return;   // whole 32-column blocks: cols is a multiple of 32 for rows
+    // lanes stay in pairs (the columnwise stores need both); rowwise, cols is
+    // a multiple of 32, so both lanes of a pair always hold columns
+    if ((c0 & ~(int64_t)15) >= cols) return;
+    const bool live = c0 < cols;
 
     const char* in = (const char*)a.src.p[m] + r0 * cols * 2;
     u32x4 v[kMxBlock];
 #pragma unroll
     for (int j = 0; j < kMxBlock; ++j) {
         v[j] = (u32x4){0u, 0u, 0u, 0u};
-        if (j < valid)
+        if (j < valid && live)
             v[j] = __builtin_nontemporal_load((const u32x4*)(in + (j * cols + c0) * 2));
     }
 
@@ -243,29 +263,77 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
         // group g stored as [cols, P_g] at cols * P_0..g-1; rows past the
         // group's end were loaded as zeros and encode to 0x00
         uint8_t* cc = (uint8_t*)a.ccodes.p[m] + pbase * cols + i0;
+        // staged: 256 column lines of 128 bytes (rows i0 - 32 wv .. + 127),
+        // half the workgroup's columns at a time.  Line li (lane li / 4,
+        // column t = li % 4 of the half) sits at slot li ^ bit 5 of li, its
+        // 16-byte pieces rotated by lane % 8, so neither the writes nor the
+        // reads meet on an LDS bank.
+        __shared__ u32x4 stage[256 * 8];
         uint32_t sc[2] = {0u, 0u};
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const uint32_t am = (t & 1) ? (mw[t >> 1] >> 16) : (mw[t >> 1] & 0xffffu);
-            const uint32_t S = FIXED ? Sfix : mx_scale_byte(__uint_as_float(am << 16));
-            u32x4 o[2];
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {   // rows 4q .. 4q+3
-                float f[4];
+            for (int tt = 0; tt < 4; ++tt) {
+                const int t = 4 * h + tt;
+                const uint32_t am = (t & 1) ? (mw[t >> 1] >> 16) : (mw[t >> 1] & 0xffffu);
+                const uint32_t S = FIXED ? Sfix : mx_scale_byte(__uint_as_float(am << 16));
+                u32x4 o[2];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t w = v[4 * q + r][t >> 1];
-                    f[r] = (t & 1) ? hi_bf16(w) : lo_bf16(w);
+                for (int q = 0; q < 8; ++q) {   // rows 4q .. 4q+3
+                    float f[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint32_t w = v[4 * q + r][t >> 1];
+                        f[r] = (t & 1) ? hi_bf16(w) : lo_bf16(w);
+                    }
+                    o[q >> 2][q & 3] = mx_encode4(f[0], f[1], f[2], f[3], S);
                 }
-                o[q >> 2][q & 3] = mx_encode4(f[0], f[1], f[2], f[3], S);
+                sc[t >> 2] |= S << (8 * (t & 3));
+                if (staged) {
+                    const int li = 4 * lane + tt;
+                    const int slot = li ^ ((li >> 5) & 1);
+                    stage[slot * 8 + ((2 * wv) ^ (lane & 7))] = o[0];
+                    stage[slot * 8 + ((2 * wv + 1) ^ (lane & 7))] = o[1];
+                    continue;
+                }
+                // lanes 2p and 2p + 1 trade halves so that each store writes
+                // the 32 codes of one column as 32 contiguous bytes over two
+                // lanes: first the even lane's column, then the odd lane's
+                const bool odd = lane & 1;
+                const u32x4 send = odd ? o[0] : o[1];
+                u32x4 recv;
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    recv[d] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send[d], 0xB1, 0xF, 0xF, true);
+                const int64_t ce = (c0 & ~(int64_t)15) + t;   // the even lane's column
+                *(u32x4*)(cc + ce * pad + (odd ? 16 : 0)) = odd ? recv : o[0];
+                if ((c0 | 8) < cols)
+                    *(u32x4*)(cc + (ce + 8) * pad + (odd ? 16 : 0)) = odd ? o[1] : recv;
             }
-            u32x4* dst = (u32x4*)(cc + (c0 + t) * pad);
-            dst[0] = o[0];
-            dst[1] = o[1];
-            sc[t >> 2] |= S << (8 * (t & 3));
+            if (staged) {
+                __syncthreads();
+                // eight neighbouring threads store one column's 128 codes:
+                // streamed past L2 when they fill one line, else plain stores
+                // (a run across two lines shares each with another workgroup)
+                uint8_t* cw = cc - 32 * wv;
+                const bool whole = (pad & 127) == 0 && ((uintptr_t)cw & 127) == 0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int ch = k * 256 + (int)threadIdx.x;
+                    const int li = ch >> 3, piece = ch & 7;
+                    const int slot = li ^ ((li >> 5) & 1);
+                    const u32x4 val = stage[slot * 8 + (piece ^ ((li >> 2) & 7))];
+                    const int64_t col = (int64_t)blockIdx.x * 512 + 8 * (li >> 2) + (li & 3) + 4 * h;
+                    u32x4* dst = (u32x4*)(cw + col * pad + 16 * piece);
+                    if (whole) __builtin_nontemporal_store(val, dst);
+                    else *dst = val;
+                }
+                __syncthreads();
+            }
         }
         uint8_t* cs = (uint8_t*)a.cscales.p[m] + pbase / kMxBlock * cols;
-        if (a.cscales_t) {   // [P_g/32][cols]: 8 neighbouring columns, 8 bytes
+        if (!live) {
+        } else if (a.cscales_t) {   // [P_g/32][cols]: 8 neighbouring columns, 8 bytes
             *(u32x2*)(cs + i0 / kMxBlock * cols + c0) = (u32x2){sc[0], sc[1]};
         } else {             // [cols][P_g/32]
 #pragma unroll
