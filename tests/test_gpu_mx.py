@@ -99,7 +99,13 @@ def test_quant_both_orientations(sizes, C):
     """Both orientations from one read equal the oracle's rowwise and grouped
     columnwise quantization (and so the two separate calls) byte for byte,
     including column tiles cut short (C not a multiple of 512) and groups with
-    no rows or a partial last block."""
+    no rows or a partial last block.
+
+    The cases reach each way the column codes are stored:
+    * LDS-staged 128-byte runs on aligned lines (2 x 2816 rows, 2048 columns);
+    * the same runs off the 128-byte grid (300 rows, padded to 320);
+    * paired 32-byte stores, for workgroups across a group boundary or in a
+      short column tile (608, 1408 and 96 columns)."""
     rng = np.random.default_rng(5)
     if sizes == "skewed":
         sh = synth.SHAPES["skewed"]
