@@ -299,3 +299,79 @@ def qdq_tensor_fast(x) -> torch.Tensor:
     sh = int(block_scale_exponent(np.array(amax))) - 127
     q = torch.ldexp(v, torch.tensor(float(-sh))).to(torch.float8_e4m3fn).to(torch.float32)
     return torch.ldexp(q, torch.tensor(float(sh)))
+
+
+# ---------------------------------------------------------------- fast codes
+# quantize_rows_fast / quantize_cols_grouped_fast return the codes and scale
+# bytes themselves (not only the values), in the layouts of quantize_rows and
+# quantize_cols_grouped, for whole expert weights and routed activations:
+# the same scale rule (block_scale_exponent), the exact power-of-two unscale in
+# fp32, and torch's CPU float8_e4m3fn cast as the rounding step; pinned byte for
+# byte to the reference functions.
+
+def quantize_rows_fast(x):
+    """Same (codes u8 [R, C], scales u8 [R, C/32]) as quantize_rows(x)."""
+    v = x.detach().to(torch.float32) if isinstance(x, torch.Tensor) else \
+        torch.from_numpy(np.asarray(x, dtype=np.float32))
+    R, C = v.shape
+    assert C % BLOCK == 0, "columns must be a multiple of 32"
+    b = v.reshape(R, C // BLOCK, BLOCK)
+    S = block_scale_exponent(b.abs().amax(dim=2).to(torch.float64).numpy()) if R and C else \
+        np.zeros((R, C // BLOCK), np.uint8)
+    sh = torch.from_numpy(S.astype(np.int32) - 127)[..., None].to(torch.float32)
+    codes = torch.ldexp(b, -sh).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.reshape(R, C).numpy(), S.reshape(R, C // BLOCK)
+
+
+def dequantize_rows_fast(codes, scales) -> torch.Tensor:
+    """Same values as dequantize_rows (fp32 tensor): decode(code) * 2^(S-127)."""
+    c = torch.as_tensor(np.ascontiguousarray(codes))
+    R, C = c.shape
+    vals = c.view(torch.float8_e4m3fn).to(torch.float32).reshape(R, C // BLOCK, BLOCK)
+    sh = torch.from_numpy(np.asarray(scales).astype(np.int32) - 127)[..., None].to(torch.float32)
+    return torch.ldexp(vals, sh).reshape(R, C)
+
+
+def quantize_cols_grouped_fast(x, sizes):
+    """Same flat (codes, scales) as quantize_cols_grouped(x, sizes)."""
+    v = x.detach().to(torch.float32) if isinstance(x, torch.Tensor) else \
+        torch.from_numpy(np.asarray(x, dtype=np.float32))
+    R, C = v.shape
+    sizes = np.asarray(sizes, dtype=np.int64)
+    assert sizes.sum() == R
+    codes_all, scales_all = [], []
+    r0 = 0
+    for n in sizes:
+        n = int(n)
+        if n == 0:
+            continue
+        pad = (-n) % BLOCK
+        g = v[r0:r0 + n].T                                  # [C, n]: the group transposed
+        if pad:
+            g = torch.cat([g, g.new_zeros((C, pad))], dim=1)
+        c, s = quantize_rows_fast(g.contiguous())
+        codes_all.append(c.reshape(-1))
+        scales_all.append(s.reshape(-1))
+        r0 += n
+    if not codes_all:
+        return np.zeros(0, np.uint8), np.zeros(0, np.uint8)
+    return np.concatenate(codes_all), np.concatenate(scales_all)
+
+
+def dequantize_cols_grouped_fast(codes, scales, sizes, C: int) -> torch.Tensor:
+    """Same values as dequantize_cols_grouped (fp32 tensor [R, C])."""
+    sizes = np.asarray(sizes, dtype=np.int64)
+    P = padded_sizes(sizes)
+    out = torch.zeros((int(sizes.sum()), C), dtype=torch.float32)
+    c0 = s0 = r0 = 0
+    for n, p in zip(sizes, P):
+        n, p = int(n), int(p)
+        if p == 0:
+            continue
+        cb = np.asarray(codes[c0:c0 + C * p]).reshape(C, p)
+        sb = np.asarray(scales[s0:s0 + C * p // BLOCK]).reshape(C, p // BLOCK)
+        out[r0:r0 + n] = dequantize_rows_fast(cb, sb)[:, :n].T
+        c0 += C * p
+        s0 += C * p // BLOCK
+        r0 += n
+    return out

@@ -8,7 +8,8 @@
 * central finite differences on a 2-expert, 8-token, H = I = 32 case;
 * invariants: empty experts give exact zero weight gradients and do not
   touch the output; doubling the probabilities doubles the output exactly
-  (BF16 and MXFP8); MXFP8 on operands already on the MXFP8 grid equals BF16.
+  (BF16 and MXFP8); MXFP8 on operands that it represents exactly along both
+  axes (block scales over many binades) equals BF16.
 """
 import numpy as np
 import pytest
@@ -155,21 +156,43 @@ def test_prob_scaling_is_exact(precision):
     assert torch.equal(b["yp"].float(), 2 * a["yp"].float())
 
 
-def _on_mx_grid(t, rng):
-    """Round a tensor to values that MXFP8 represents exactly along rows
-    (and, for 32x32 tiles with a common scale, along columns too)."""
-    q = mx.qdq_rows(t)
-    return q.to(torch.bfloat16)
-
-
-def test_mx_equals_bf16_on_representable_gate_up():
+def test_mx_equals_bf16_on_representable_operands():
+    """Operands that MXFP8 represents exactly along both axes, with block
+    scales spread over many binades: every MXFP8 operand preparation is the
+    identity, so the oracle's gate_up (A1) and its down dgrad (through the
+    fp32 probability gradient) equal BF16 mode bit for bit, and each recorded
+    operand holds the input values."""
+    from tests.mxgrid import grid_matrix, n_tiles
     rng = np.random.default_rng(61)
-    xp = _on_mx_grid(_rand((64, 64), rng), rng)
-    w1 = [_on_mx_grid(_rand((128, 64), rng, 0.1), rng)]
-    assert torch.equal(mx.qdq_rows(xp), xp.float())
-    a_bf = xp.float() @ w1[0].float().T
-    a_mx = mx.qdq_rows(xp) @ mx.qdq_rows(w1[0]).T
-    assert torch.equal(a_bf, a_mx)
+    split = [45, 0, 70, 13]
+    H, I, E = 64, 96, len(split)
+    nrt = sum(n_tiles(n) for n in split)
+    g = lambda n: rng.integers(-8, 9, n)             # noqa: E731
+    vx, vd = g(H // 32), g(H // 32)
+    xp = grid_matrix(rng, split, H, g(nrt), vx)
+    dyp = grid_matrix(rng, split, H, g(nrt), vd)
+    # products balanced along each contraction: W1's column tiles undo xp's,
+    # W2's row tiles undo dYp's
+    w1 = [grid_matrix(rng, [2 * I], H, g(n_tiles(2 * I)), -vx) for _ in range(E)]
+    w2 = [grid_matrix(rng, [H], I, -vd, g(I // 32)) for _ in range(E)]
+    pp = rng.uniform(0.2, 1.0, sum(split)).astype(np.float32)
+    out = {}
+    for prec in ("bf16", "mxfp8"):
+        f = mlp.grouped_mlp_fwd(xp, split, w1, w2, pp, prec, keep_operands=True)
+        b = mlp.grouped_mlp_bwd(dyp, xp, split, w1, w2, pp, f, prec, keep_operands=True)
+        out[prec] = (f, b)
+    fb, fm = out["bf16"][0], out["mxfp8"][0]
+    assert torch.equal(fb["a1"], fm["a1"])
+    assert torch.equal(out["bf16"][1]["dpp"], out["mxfp8"][1]["dpp"])
+    ops = dict(fm["operands"])
+    ops.update(out["mxfp8"][1]["operands"])
+    for key in [("gate_up", "a"), ("gate_up", "b"), ("down_dgrad", "a"), ("down_dgrad", "b"),
+                ("down_wgrad", "a"), ("gate_up_wgrad", "b")]:
+        for e, n in enumerate(split):
+            if n:
+                rec = ops[key + (e,)]
+                assert rec["axis"] != "none"
+                assert torch.equal(rec["value"], rec["pre"].float()), key + (e,)
 
 
 def test_mx_close_to_bf16():

@@ -318,3 +318,30 @@ def test_tensor_fast_equals_reference_all_bf16_patterns():
     v = v[v.float().abs().argsort()]
     for chunk in v.split(2048):
         assert torch.equal(mx.qdq_tensor(chunk[None, :]), mx.qdq_tensor_fast(chunk[None, :]))
+
+
+def test_fast_codes_equal_reference_codes():
+    """The code-returning fast quantizers give the reference bytes: every bf16
+    pattern, rows scaled over many binades, zero and outlier blocks, ragged
+    and empty groups."""
+    x = _bf16_all_finite_blocks(11)
+    for a, b in zip(mx.quantize_rows_fast(x), mx.quantize_rows(x)):
+        assert np.array_equal(a, b)
+    rng = np.random.default_rng(12)
+    v = rng.standard_normal((130, 96)).astype(np.float32)
+    v *= np.exp2(rng.integers(-30, 30, size=(130, 1))).astype(np.float32)
+    v[4] = 0.0
+    v[9, 3] = 65504.0
+    xb = torch.from_numpy(v).to(torch.bfloat16)
+    for a, b in zip(mx.quantize_rows_fast(xb), mx.quantize_rows(xb)):
+        assert np.array_equal(a, b)
+    sizes = [0, 1, 31, 32, 33, 0, 33]
+    for a, b in zip(mx.quantize_cols_grouped_fast(xb, sizes), mx.quantize_cols_grouped(xb, sizes)):
+        assert np.array_equal(a, b)
+    c, s = mx.quantize_rows(xb)
+    assert torch.equal(mx.dequantize_rows_fast(c, s),
+                       torch.from_numpy(mx.dequantize_rows(c, s).astype(np.float32)))
+    cc, cs = mx.quantize_cols_grouped(xb, sizes)
+    assert torch.equal(mx.dequantize_cols_grouped_fast(cc, cs, sizes, 96),
+                       torch.from_numpy(mx.dequantize_cols_grouped(cc, cs, sizes, 96)
+                                        .astype(np.float32)))
