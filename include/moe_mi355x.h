@@ -85,7 +85,10 @@ typedef enum moe_op {
     MOE_OP_MLP_FWD = 1,
     MOE_OP_MLP_BWD = 2,
     MOE_OP_ROUTER_FWD = 3,    /* T, E, k used */
-    MOE_OP_ROUTER_BWD = 4     /* T, H, E used (k must still be valid) */
+    MOE_OP_ROUTER_BWD = 4,    /* T, H, E used (k must still be valid) */
+    MOE_OP_LINEAR_FWD = 5,    /* grouped_linear_fwd: T = rows, H = in_features K,
+                                 I = out_features N, E, precision (k must be 1) */
+    MOE_OP_LINEAR_BWD = 6     /* grouped_linear_bwd: as MOE_OP_LINEAR_FWD */
 } moe_op;
 
 /* Limits of this version. */
@@ -376,6 +379,92 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
  * H, I, E, precision used).  Returns 0 for an invalid op.
  */
 size_t moe_workspace_bytes(int op, int64_t T, int H, int I, int E, int k, int precision);
+
+/*
+ * Regions of the grouped-MLP workspaces (inspection aid).  After
+ * grouped_mlp_fwd / grouped_mlp_bwd have run, these regions hold the MXFP8
+ * (or FP8) GEMM operands the calls made, until the next call that uses the
+ * same workspace.  The codes follow the layouts of mxfp8_quantize; the
+ * scales are the same bytes stored block-major, the order the GEMMs read:
+ *   rowwise [rows, C]          scales [C/32][rows]
+ *   per-expert weights         expert e's codes at e*(its size), scales
+ *                              block-major [C/32][R] at e*(its size)/32
+ *   grouped columnwise         codes as mxfp8_quantize axis=0 (groups =
+ *                              experts); scales [P_g/32][C] per group
+ * The region of MOE_WS_A2_* holds the codes the down GEMM read (rowwise
+ * MXFP8 of the ScaledSwiGLU output); *_W1_COL_* and *_W2_COL_* are used
+ * only when moe_saved carries no weight copies.
+ */
+typedef enum moe_ws_region {
+    /* MOE_OP_MLP_FWD, MOE_MXFP8 / MOE_FP8 */
+    MOE_WS_XP_CODES = 0,          /* [rows, H], blocks along H */
+    MOE_WS_XP_SCALES = 1,         /* [H/32][rows] */
+    MOE_WS_W1_CODES = 2,          /* E x [2I, H], blocks along H */
+    MOE_WS_W1_SCALES = 3,         /* E x [H/32][2I] */
+    MOE_WS_W2_CODES = 4,          /* E x [H, I], blocks along I */
+    MOE_WS_W2_SCALES = 5,         /* E x [I/32][H] */
+    MOE_WS_A2_CODES = 6,          /* [rows, I], blocks along I */
+    MOE_WS_A2_SCALES = 7,         /* [I/32][rows] */
+    /* MOE_OP_MLP_BWD, MOE_MXFP8 / MOE_FP8 */
+    MOE_WS_DYP_CODES = 8,         /* [rows, H], blocks along H */
+    MOE_WS_DYP_SCALES = 9,        /* [H/32][rows] */
+    MOE_WS_DYP_COL_CODES = 10,    /* grouped columnwise [H, P_e] per expert */
+    MOE_WS_DYP_COL_SCALES = 11,   /* [P_e/32][H] per expert */
+    MOE_WS_W2_COL_CODES = 12,     /* E x [I, H]: W2 blocked along H */
+    MOE_WS_W2_COL_SCALES = 13,    /* E x [H/32][I] */
+    MOE_WS_W1_COL_CODES = 14,     /* E x [H, 2I]: W1 blocked along 2I */
+    MOE_WS_W1_COL_SCALES = 15,    /* E x [2I/32][H] */
+    MOE_WS_DA1_CODES = 16,        /* [rows, 2I], blocks along 2I */
+    MOE_WS_DA1_SCALES = 17,       /* [2I/32][rows] */
+    MOE_WS_DA1_COL_CODES = 18,    /* grouped columnwise [2I, P_e] per expert */
+    MOE_WS_DA1_COL_SCALES = 19    /* [P_e/32][2I] per expert */
+} moe_ws_region;
+
+/* Byte offset and size of `region` inside the workspace of `op`
+ * (MOE_OP_MLP_FWD or MOE_OP_MLP_BWD) for these sizes.  Returns MOE_OK,
+ * MOE_ERR_ARG when the op/precision has no such region, or MOE_ERR_NULL. */
+int moe_workspace_region(int op, int region, int64_t rows, int H, int I, int E, int precision,
+                         size_t* offset, size_t* bytes);
+
+/*
+ * grouped_linear_fwd -- one linear map per expert over the expert's rows, all
+ * experts in one launch: y_e = x_e W_e^T (no bias), fp32 accumulation,
+ * rounded to bf16.
+ * [BioNeMo, "GroupedLinear": a grouped linear layer takes the tokens of all
+ *  local experts with split_sizes and applies each expert's own weight in one
+ *  grouped GEMM instead of one launch per expert.]
+ *
+ * precision    MOE_BF16 or MOE_MXFP8 (x and W quantized along K first).
+ * E            experts, 1..64.   N: out_features, K: in_features, both
+ *              multiples of 32, with rows * max(N, K) * 2 and N * K * 2 below
+ *              2^31 (otherwise MOE_ERR_SHAPE).
+ * rows         total rows (sum of split_sizes), 0 <= rows <= INT32_MAX.
+ * x            bf16 [rows, K], expert-grouped.   split_sizes: int32 [E] device.
+ * w            HOST array of E device pointers, each bf16 [N, K].
+ * y            bf16 [rows, N] out.
+ * workspace    moe_workspace_bytes(MOE_OP_LINEAR_FWD, rows, K, N, E, 1, precision).
+ */
+int grouped_linear_fwd(int precision, int E, int N, int K, int64_t rows, const uint16_t* x,
+                       const int32_t* split_sizes, const uint16_t* const* w, uint16_t* y,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * grouped_linear_bwd -- backward of grouped_linear_fwd: dx_e = dy_e W_e and
+ * dW_e = dy_e^T x_e (contraction over the expert's rows; exact zeros for an
+ * expert with no rows), fp32 accumulation, rounded to bf16.  MXFP8 mode
+ * quantizes dy along N and W along N for dx, and dy and x in 32-row blocks
+ * that restart at each expert's first row for dW.
+ * dy           bf16 [rows, N].   x: bf16 [rows, K] (used for dW).
+ * dx           bf16 [rows, K] out, or NULL (not computed).
+ * dw           HOST array of E device pointers, each bf16 [N, K] out, or
+ *              NULL (not computed).
+ * Other arguments as grouped_linear_fwd; workspace of
+ * moe_workspace_bytes(MOE_OP_LINEAR_BWD, rows, K, N, E, 1, precision) bytes.
+ */
+int grouped_linear_bwd(int precision, int E, int N, int K, int64_t rows, const uint16_t* dy,
+                       const uint16_t* x, const int32_t* split_sizes, const uint16_t* const* w,
+                       uint16_t* dx, uint16_t* const* dw, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
 
 
 /*

@@ -8,7 +8,9 @@ device is not a gfx950.
 
 The functions carry the names of the C entry points (include/moe_mi355x.h):
 moe_route, moe_route_bwd, moe_router_fwd, moe_router_bwd, moe_permute,
-moe_unpermute, mxfp8_quantize, mxfp8_quantize_both, mxfp8_dequantize, grouped_mlp_fwd, grouped_mlp_bwd, moe_workspace_bytes.
+moe_unpermute, mxfp8_quantize, mxfp8_quantize_both, mxfp8_dequantize, grouped_mlp_fwd,
+grouped_mlp_bwd, grouped_linear_fwd, grouped_linear_bwd, moe_workspace_bytes,
+moe_workspace_region.
 """
 from __future__ import annotations
 
@@ -23,6 +25,15 @@ LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(_PKG, "_lib", "libmo
 MOE_BF16, MOE_MXFP8, MOE_FP8 = 0, 1, 2
 MOE_ROUTE_RENORM, MOE_ROUTE_SOFTMAX_ALL = 0, 1
 MOE_OP_ROUTE, MOE_OP_MLP_FWD, MOE_OP_MLP_BWD, MOE_OP_ROUTER_FWD, MOE_OP_ROUTER_BWD = 0, 1, 2, 3, 4
+MOE_OP_LINEAR_FWD, MOE_OP_LINEAR_BWD = 5, 6
+# moe_workspace_region regions (include/moe_mi355x.h)
+WS_REGIONS = {
+    "xp_codes": 0, "xp_scales": 1, "w1_codes": 2, "w1_scales": 3, "w2_codes": 4, "w2_scales": 5,
+    "a2_codes": 6, "a2_scales": 7, "dyp_codes": 8, "dyp_scales": 9, "dyp_col_codes": 10,
+    "dyp_col_scales": 11, "w2_col_codes": 12, "w2_col_scales": 13, "w1_col_codes": 14,
+    "w1_col_scales": 15, "da1_codes": 16, "da1_scales": 17, "da1_col_codes": 18,
+    "da1_col_scales": 19,
+}
 MAX_EXPERTS = 64
 
 _lib = None
@@ -66,6 +77,10 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(_Saved), P, SZ, P]),
             "grouped_mlp_bwd": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P,
                                       ctypes.POINTER(_Saved), P, P, P, P, P, SZ, P]),
+            "grouped_linear_fwd": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, SZ, P]),
+            "grouped_linear_bwd": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P, P, SZ, P]),
+            "moe_workspace_region": (I32, [I32, I32, I64, I32, I32, I32, I32,
+                                           ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
             "moe_trace_enable": (I32, [I32]),
             "moe_trace_disable": (None, []),
             "moe_trace_count": (I32, []),
@@ -349,6 +364,57 @@ def grouped_mlp_bwd(dyp, xp, split_sizes, w_gate_up, w_down, prob_perm, saved,
                                  _ptr(dpp), _ptr(workspace), workspace.numel(), _stream(dev)),
            "grouped_mlp_bwd")
     return dxp, dw_gate_up, dw_down, dpp
+
+
+def workspace_region(op: int, name: str, rows: int, H: int, I: int, E: int,
+                     precision: int):
+    """(byte offset, bytes) of a named region of a grouped-MLP workspace."""
+    off, n = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().moe_workspace_region(op, WS_REGIONS[name], rows, H, I, E, precision,
+                                      ctypes.byref(off), ctypes.byref(n)),
+           f"moe_workspace_region({name})")
+    return off.value, n.value
+
+
+def grouped_linear_fwd(x, split_sizes, w, precision=MOE_BF16, workspace=None):
+    """y_e = x_e W_e^T for every expert.  x bf16 [rows, K]; w: list of E bf16
+    [N, K] device tensors.  Returns y bf16 [rows, N]."""
+    _dev(x, torch.bfloat16, "x")
+    rows, K = x.shape
+    E = len(w)
+    N = w[0].shape[0]
+    if workspace is None:
+        workspace = _workspace(moe_workspace_bytes(MOE_OP_LINEAR_FWD, rows, K, N, E, 1, precision),
+                               x.device)
+    y = torch.empty((rows, N), dtype=torch.bfloat16, device=x.device)
+    wp = _ptr_array(w)
+    _check(lib().grouped_linear_fwd(precision, E, N, K, rows, _ptr(x), _ptr(split_sizes),
+                                    ctypes.cast(wp, ctypes.c_void_p), _ptr(y), _ptr(workspace),
+                                    workspace.numel(), _stream(x.device)), "grouped_linear_fwd")
+    return y
+
+
+def grouped_linear_bwd(dy, x, split_sizes, w, precision=MOE_BF16, want_dx=True, want_dw=True,
+                       workspace=None):
+    """Returns (dx bf16 [rows, K] or None, list of E dW bf16 [N, K] or None)."""
+    _dev(dy, torch.bfloat16, "dy")
+    rows, N = dy.shape
+    E = len(w)
+    K = w[0].shape[1]
+    dev = dy.device
+    if workspace is None:
+        workspace = _workspace(moe_workspace_bytes(MOE_OP_LINEAR_BWD, rows, K, N, E, 1, precision),
+                               dev)
+    dx = torch.empty((rows, K), dtype=torch.bfloat16, device=dev) if want_dx else None
+    dw = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in range(E)] if want_dw else None
+    wp = _ptr_array(w)
+    dwp = _ptr_array(dw) if dw is not None else None
+    _check(lib().grouped_linear_bwd(precision, E, N, K, rows, _ptr(dy), _ptr(x), _ptr(split_sizes),
+                                    ctypes.cast(wp, ctypes.c_void_p), _ptr(dx),
+                                    ctypes.cast(dwp, ctypes.c_void_p) if dwp is not None else None,
+                                    _ptr(workspace), workspace.numel(), _stream(dev)),
+           "grouped_linear_bwd")
+    return dx, dw
 
 
 def trace_enable(capacity: int) -> None:

@@ -63,6 +63,8 @@ size_t moe_workspace_bytes(int op, int64_t T, int H, int I, int E, int k, int pr
         case MOE_OP_MLP_BWD: return mlp_bwd_workspace_bytes(T * k, H, I, E, precision);
         case MOE_OP_ROUTER_FWD: return route_workspace_bytes(T, E, k);
         case MOE_OP_ROUTER_BWD: return router_bwd_workspace_bytes(T, H, E);
+        case MOE_OP_LINEAR_FWD: return k == 1 ? linear_fwd_workspace_bytes(T, I, H, E, precision) : 0;
+        case MOE_OP_LINEAR_BWD: return k == 1 ? linear_bwd_workspace_bytes(T, I, H, E, precision) : 0;
         default: return 0;
     }
 }

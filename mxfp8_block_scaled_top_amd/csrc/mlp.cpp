@@ -185,6 +185,55 @@ int device_check() { return moe_device_supported() ? MOE_OK : MOE_ERR_UNSUPPORTE
 }  // namespace
 
 namespace moe {
+int mlp_workspace_region(int op, int region, int64_t rows, int H, int I, int E, int precision,
+                         size_t* offset, size_t* bytes) {
+    if (!offset || !bytes) return MOE_ERR_NULL;
+    if (precision != MOE_MXFP8 && precision != MOE_FP8) return MOE_ERR_ARG;
+    if (rows < 0 || E < 1 || E > kMaxExperts || H < 1 || I < 1) return MOE_ERR_SHAPE;
+    const size_t r = (size_t)rows, w1 = (size_t)E * 2 * I * H, w2 = (size_t)E * H * I;
+    const uint8_t* p = nullptr;
+    size_t n = 0;
+    if (op == MOE_OP_MLP_FWD) {
+        // carved from a non-null base (256) so that every region gets a pointer
+        FwdWs o = carve_fwd((void*)(uintptr_t)256, rows, H, I, E, precision);
+        switch (region) {
+            case MOE_WS_XP_CODES: p = o.xq; n = r * H; break;
+            case MOE_WS_XP_SCALES: p = o.xq_s; n = r * H / 32; break;
+            case MOE_WS_W1_CODES: p = o.w1q; n = w1; break;
+            case MOE_WS_W1_SCALES: p = o.w1q_s; n = w1 / 32; break;
+            case MOE_WS_W2_CODES: p = o.w2q; n = w2; break;
+            case MOE_WS_W2_SCALES: p = o.w2q_s; n = w2 / 32; break;
+            case MOE_WS_A2_CODES: p = o.a2q; n = r * I; break;
+            case MOE_WS_A2_SCALES: p = o.a2q_s; n = r * I / 32; break;
+            default: return MOE_ERR_ARG;
+        }
+    } else if (op == MOE_OP_MLP_BWD) {
+        BwdWs o = carve_bwd((void*)(uintptr_t)256, rows, H, I, E, precision);
+        const size_t ch = colwise_codes(rows, H, E), ci = colwise_codes(rows, 2 * (int64_t)I, E);
+        switch (region) {
+            case MOE_WS_DYP_CODES: p = o.dyq; n = r * H; break;
+            case MOE_WS_DYP_SCALES: p = o.dyq_s; n = r * H / 32; break;
+            case MOE_WS_DYP_COL_CODES: p = o.dyc; n = ch; break;
+            case MOE_WS_DYP_COL_SCALES: p = o.dyc_s; n = ch / 32; break;
+            case MOE_WS_W2_COL_CODES: p = o.w2c; n = w2; break;
+            case MOE_WS_W2_COL_SCALES: p = o.w2c_s; n = w2 / 32; break;
+            case MOE_WS_W1_COL_CODES: p = o.w1c; n = w1; break;
+            case MOE_WS_W1_COL_SCALES: p = o.w1c_s; n = w1 / 32; break;
+            case MOE_WS_DA1_CODES: p = o.da1q; n = r * 2 * I; break;
+            case MOE_WS_DA1_SCALES: p = o.da1q_s; n = r * 2 * I / 32; break;
+            case MOE_WS_DA1_COL_CODES: p = o.da1c; n = ci; break;
+            case MOE_WS_DA1_COL_SCALES: p = o.da1c_s; n = ci / 32; break;
+            default: return MOE_ERR_ARG;
+        }
+    } else {
+        return MOE_ERR_ARG;
+    }
+    if (!p) return MOE_ERR_ARG;
+    *offset = (size_t)((uintptr_t)p - 256);
+    *bytes = n;
+    return MOE_OK;
+}
+
 size_t mlp_fwd_workspace_bytes(int64_t rows, int H, int I, int E, int precision) {
     return carve_fwd(nullptr, rows, H, I, E, precision).bytes;
 }
@@ -199,6 +248,11 @@ size_t mlp_bwd_workspace_bytes(int64_t rows, int H, int I, int E, int precision)
     } while (0)
 
 extern "C" {
+
+int moe_workspace_region(int op, int region, int64_t rows, int H, int I, int E, int precision,
+                         size_t* offset, size_t* bytes) {
+    return mlp_workspace_region(op, region, rows, H, I, E, precision, offset, bytes);
+}
 
 int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint16_t* xp,
                     const int32_t* split_sizes, const uint16_t* const* w_gate_up,

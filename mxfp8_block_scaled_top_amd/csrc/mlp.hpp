@@ -73,6 +73,10 @@ int gemm_n_tiles(int epi, int N, int I);
 int64_t gemm_slots(int grp, int epi, int64_t rows, int E, int M, int N, int I);
 
 size_t mlp_fwd_workspace_bytes(int64_t rows, int H, int I, int E, int precision);
+int mlp_workspace_region(int op, int region, int64_t rows, int H, int I, int E, int precision,
+                         size_t* offset, size_t* bytes);
+size_t linear_fwd_workspace_bytes(int64_t rows, int N, int K, int E, int precision);
+size_t linear_bwd_workspace_bytes(int64_t rows, int N, int K, int E, int precision);
 size_t mlp_bwd_workspace_bytes(int64_t rows, int H, int I, int E, int precision);
 
 }  // namespace moe

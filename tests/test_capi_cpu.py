@@ -30,8 +30,10 @@ def _declared_functions():
 def test_header_declares_the_path():
     names = _declared_functions()
     for n in ["moe_route", "moe_route_bwd", "moe_permute", "moe_unpermute", "mxfp8_quantize",
-              "mxfp8_quantize_both", "mxfp8_dequantize", "moe_router_fwd", "moe_router_bwd", "grouped_mlp_fwd", "grouped_mlp_bwd", "moe_workspace_bytes",
-              "moe_status_string", "moe_device_supported", "mxfp8_colwise_bytes"]:
+              "mxfp8_quantize_both", "mxfp8_dequantize", "moe_router_fwd", "moe_router_bwd",
+              "grouped_mlp_fwd", "grouped_mlp_bwd", "grouped_linear_fwd", "grouped_linear_bwd",
+              "moe_workspace_bytes", "moe_workspace_region", "moe_status_string",
+              "moe_device_supported", "mxfp8_colwise_bytes"]:
         assert n in names, n
 
 
@@ -108,6 +110,47 @@ def test_host_validation_before_launch(L):
                              1 << 30, None) == ARG
     assert L.grouped_mlp_bwd(1, 2, 128, 256, 8, p, p, p, tab, tab, p, ctypes.byref(part), p, tab,
                              tab, p, p, 1 << 30, None) == ARG
+
+
+def test_grouped_linear_validation(L):
+    N, SHAPE, ALIGN, WS, ARG = 1, 2, 3, 4, 7
+    p = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4097)
+    tab = (ctypes.c_void_p * 2)(4096, 4096)
+    big = 1 << 30
+    assert L.grouped_linear_fwd(0, 2, 96, 48, 8, p, p, tab, p, p, big, None) == SHAPE   # K % 32
+    assert L.grouped_linear_fwd(2, 2, 96, 64, 8, p, p, tab, p, p, big, None) == ARG     # FP8
+    assert L.grouped_linear_fwd(0, 65, 96, 64, 8, p, p, tab, p, p, big, None) == SHAPE  # E > 64
+    assert L.grouped_linear_fwd(0, 2, 96, 64, 8, p, p, None, p, p, big, None) == N
+    assert L.grouped_linear_fwd(0, 2, 96, 64, 8, mis, p, tab, p, p, big, None) == ALIGN
+    assert L.grouped_linear_fwd(1, 2, 96, 64, 8, p, p, tab, p, p, 16, None) == WS
+    # 31-bit operand offsets: rows * max(N, K) * 2 must stay below 2^31
+    assert L.grouped_linear_fwd(0, 2, 1 << 15, 64, 1 << 15, p, p, tab, p, p, big, None) == SHAPE
+    assert L.grouped_linear_bwd(0, 2, 96, 64, 8, p, p, p, None, p, None, p, big, None) == N
+    assert L.grouped_linear_bwd(0, 2, 96, 64, 8, p, p, p, tab, p, tab, p, 16, None) == WS \
+        or moe.moe_workspace_bytes(moe.MOE_OP_LINEAR_BWD, 8, 64, 96, 2, 1, 0) <= 16
+    assert moe.moe_workspace_bytes(moe.MOE_OP_LINEAR_FWD, 8, 64, 96, 2, 2, 1) == 0   # k must be 1
+
+
+def test_workspace_regions(L):
+    """Regions lie inside the workspace, do not overlap, and have the sizes of
+    the operands they hold."""
+    rows, H, I, E = 16384, 4096, 14336, 8
+    for op, names in ((moe.MOE_OP_MLP_FWD, [n for n, v in moe.WS_REGIONS.items() if v < 8]),
+                      (moe.MOE_OP_MLP_BWD, [n for n, v in moe.WS_REGIONS.items() if v >= 8])):
+        total = moe.moe_workspace_bytes(op, rows // 2, H, I, E, 2, moe.MOE_MXFP8)
+        spans = sorted(moe.workspace_region(op, n, rows, H, I, E, moe.MOE_MXFP8) for n in names)
+        for (o1, n1), (o2, _) in zip(spans, spans[1:]):
+            assert o1 + n1 <= o2
+        assert spans[-1][0] + spans[-1][1] <= total
+    assert moe.workspace_region(moe.MOE_OP_MLP_FWD, "xp_codes", rows, H, I, E, 1)[1] == rows * H
+    assert moe.workspace_region(moe.MOE_OP_MLP_FWD, "w1_scales", rows, H, I, E, 1)[1] == \
+        E * 2 * I * H // 32
+    off, n = ctypes.c_size_t(), ctypes.c_size_t()
+    # BF16 has no MXFP8 regions; a forward region is not in the backward workspace
+    assert L.moe_workspace_region(1, 0, rows, H, I, E, 0, ctypes.byref(off), ctypes.byref(n)) == 7
+    assert L.moe_workspace_region(2, 0, rows, H, I, E, 1, ctypes.byref(off), ctypes.byref(n)) == 7
+    assert L.moe_workspace_region(1, 0, rows, H, I, E, 1, None, None) == 1
 
 
 def test_no_gpu_means_unsupported(L):

@@ -23,7 +23,7 @@ import torch
 
 import mxfp8_block_scaled_top_amd as moe
 from mxfp8_block_scaled_top_amd import synth
-from mxfp8_block_scaled_top_amd.layer import layer_step
+from mxfp8_block_scaled_top_amd.layer import LayerBuffers, layer_step
 from oracle import mlp as omlp
 from tests.helpers import need_gpu, np_, rel_frob, say
 
@@ -54,15 +54,17 @@ def _full_size(shape_name, precision):
     inp = synth.layer_inputs(sh)
     dev = {n: (v.cuda() if isinstance(v, torch.Tensor) else [w.cuda() for w in v])
            for n, v in inp.items()}
+    bufs = LayerBuffers(sh.T, sh.H, sh.I, sh.E, sh.k, CODE[precision], "cuda")
     got = layer_step(dev["logits"], dev["x"], dev["w1"], dev["w2"], dev["dy"], sh.k,
-                     CODE[precision])
+                     CODE[precision], bufs)
     torch.cuda.synchronize()
     say("  GPU step done; oracle on the chosen experts ...")
 
     r_split = np_(got["route"]["split_sizes"])
     experts = _pick_experts(r_split)
+    mx = precision == "mxfp8"
     ref = omlp.layer_step(inp["logits"], inp["x"], inp["w1"], inp["w2"], inp["dy"], sh.k,
-                          precision, experts=set(experts), fast_quant=True)
+                          precision, experts=set(experts), fast_quant=True, keep_operands=mx)
     r = ref["route"]
     say(f"  experts {experts} with {[int(r['split_sizes'][e]) for e in experts]} rows")
 
@@ -98,6 +100,16 @@ def _full_size(shape_name, precision):
         + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, bad
+    if mx:
+        # every in-layer MXFP8 operand of the chosen experts, byte for byte
+        # (ScaledSwiGLU outputs: code agreement), as in test_gpu_operands.py
+        from tests.test_gpu_operands import compare_layer_operands
+        agree = compare_layer_operands(bufs, ref["operands"], r["split_sizes"], sh.H, sh.I, sh.E,
+                                       experts=set(experts))
+        say("  operands byte-exact; computed-operand agreement: "
+            + " ".join(f"{a}={b:.5f}" for a, b in agree.items()))
+        for key, v in agree.items():
+            assert v >= 0.995, (key, v)
 
 
 @pytest.mark.parametrize("precision", ["bf16", "mxfp8"])

@@ -87,7 +87,7 @@ def _check_fp8_saved(got, ref, inp):
             assert np.all(scales[e * n // 32:(e + 1) * n // 32] == s), (name, e)
 
 
-def _layer_compare(inp, k, precision, tag):
+def _layer_compare(inp, k, precision, tag, fast_quant=False):
     say(f"layer {tag} prec={PREC[precision]} T={inp['x'].shape[0]} H={inp['x'].shape[1]} "
         f"I={inp['w2'][0].shape[1]} E={len(inp['w1'])} k={k}")
     dev = {n: (v.cuda() if isinstance(v, torch.Tensor) else [w.cuda() for w in v])
@@ -95,7 +95,7 @@ def _layer_compare(inp, k, precision, tag):
     got = layer_step(dev["logits"], dev["x"], dev["w1"], dev["w2"], dev["dy"], k, precision)
     torch.cuda.synchronize()
     ref = omlp.layer_step(inp["logits"], inp["x"], inp["w1"], inp["w2"], inp["dy"], k,
-                          PREC[precision])
+                          PREC[precision], fast_quant=fast_quant)
     r = ref["route"]
     assert np.array_equal(np_(got["route"]["split_sizes"]), r["split_sizes"])
     assert np.array_equal(np_(got["route"]["dest_row"]), r["dest_row"])
@@ -118,7 +118,8 @@ def _layer_compare(inp, k, precision, tag):
         _check_fp8_saved(got, ref, inp)
     if precision == moe.MOE_MXFP8:
         H = inp["x"].shape[1]
-        xc, xs = omx.quantize_cols_grouped(ref["xp"], r["split_sizes"])
+        qcg = omx.quantize_cols_grouped_fast if fast_quant else omx.quantize_cols_grouped
+        xc, xs = qcg(ref["xp"], r["split_sizes"])
         assert np.array_equal(np_(got["saved"]["xp_col_codes"])[: xc.size], xc)
         got_s = np_(got["saved"]["xp_col_scales"])
         assert np.array_equal(_block_major_to_public(got_s, r["split_sizes"], H)[: xs.size], xs)
@@ -128,7 +129,7 @@ def _layer_compare(inp, k, precision, tag):
         for name, (ws, n, C) in wc.items():
             codes, scales = np_(got["saved"][name + "_col_codes"]), np_(got["saved"][name + "_col_scales"])
             for e, W in enumerate(ws):
-                oc, os_ = omx.quantize_cols_grouped(W, [W.shape[0]])
+                oc, os_ = qcg(W, [W.shape[0]])
                 assert np.array_equal(codes[e * n:(e + 1) * n], oc), (name, e)
                 got_s = scales[e * n // 32:(e + 1) * n // 32]
                 assert np.array_equal(_block_major_to_public(got_s, [W.shape[0]], C), os_), (name, e)
@@ -163,6 +164,16 @@ def test_single_expert_dense(precision):
 def test_many_experts_topk8(precision):
     inp = _inputs(T=512, H=256, I=384, E=64, seed=3)
     _layer_compare(inp, 8, precision, "e64k8")
+
+
+@pytest.mark.parametrize("precision", ALL, ids=IDS)
+def test_midsize_all_experts(precision):
+    """Every GEMM's N-tile count a multiple of 8 (H = 2I/2 = 2048): the
+    expert-synchronous XCD tile order of every kernel, and the row-tile split
+    of the gate_up weight gradient, compared on all experts against the whole
+    oracle layer."""
+    inp = _inputs(T=2048, H=2048, I=2048, E=8, seed=5)
+    _layer_compare(inp, 2, precision, "midsize", fast_quant=True)
 
 
 @pytest.mark.parametrize("precision", [moe.MOE_MXFP8, moe.MOE_FP8], ids=["mxfp8", "fp8"])
