@@ -20,13 +20,17 @@ step_ms         median / min / max of the timed steps (events between steps);
 sclk_mhz        the shader clock the driver reports, sampled during the timed
                 steps (null where its sysfs file is not readable)
 cpu_baseline    the CPU oracle (tests only otherwise) timed on a bounded
-                sample of the same workload on this host's cores
+                sample of the same workload on this host's cores (the
+                first tokens, full sizes, all experts; no extrapolation)
 quantize        the standalone MXFP8 quantizer / dequantizer on the 8192 x 4096
                 quantize workload (HBM-bound; GB/s against the 8 TB/s peak)
 router          the router linear layer (logits = x W_r^T fused with the
                 routing; its backward) at the same shape, per launch
 loop_baseline   a per-expert torch loop (BF16, autograd) on the same inputs,
                 and the grouped path's speedup over it
+skewed          the fine-grained skewed layer (T=16384, H=2048, I=1408, E=64,
+                k=8, Zipf-biased routing) in the same precision, with its own
+                roofline line and loop baseline
 """
 from __future__ import annotations
 
@@ -53,8 +57,9 @@ def parse():
     ap.add_argument("--precision", default="all", choices=["mxfp8", "bf16", "fp8", "all"])
     ap.add_argument("--workload", default="mixtral", choices=["mixtral", "skewed", "tiny"])
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
-    ap.add_argument("--cpu-inter", type=int, default=768)
+    ap.add_argument("--cpu-tokens", type=int, default=1536)
+    ap.add_argument("--no-skewed", action="store_true",
+                    help="skip the fine-grained skewed layer line (mixtral workload only)")
     ap.add_argument("--no-router", action="store_true", help="skip the router linear layer line")
     ap.add_argument("--no-quant", action="store_true", help="skip the standalone quantizer line")
     ap.add_argument("--no-loop", action="store_true", help="skip the per-expert loop baseline")
@@ -214,7 +219,7 @@ def step_stats(events):
     return {"median": round(d[len(d) // 2], 4), "min": round(d[0], 4), "max": round(d[-1], 4)}
 
 
-def run_gpu(args, prec_name, inp_dev, shape):
+def run_gpu(args, prec_name, inp_dev, shape, workload=None):
     import torch
     import mxfp8_block_scaled_top_amd as moe
     from mxfp8_block_scaled_top_amd.layer import LayerBuffers, layer_step
@@ -269,7 +274,7 @@ def run_gpu(args, prec_name, inp_dev, shape):
         roof = {"bound": "hbm", "achieved": round(by / (dom_mean * 1e-3) / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"], roof["traffic_detail"] = measured_traffic(dom, args.workload)
+    roof["traffic"], roof["traffic_detail"] = measured_traffic(dom, workload or args.workload)
     roof["kernel"] = dom
     roof["mean_ms"] = round(dom_mean, 4)
     flops = 18.0 * H * I * T * k
@@ -397,17 +402,41 @@ def run_quant(args):
     return out
 
 
-def run_loop_baseline(args, inp_dev, shape):
-    """Per-expert loop: the structure of the Hugging Face
-    MoE block the pages compare against -- torch softmax + top-k, then for
-    each expert an index of its tokens, nn.Linear-style GEMMs (torch ->
-    hipBLASLt), SwiGLU, probability scale and index_add -- forward and
-    backward through torch autograd, in BF16.  A measurement baseline only;
-    the product path never runs it."""
+def loop_step(logits, x, w1, w2, dy, k, backward=True):
+    """One layer step as a per-expert loop: the structure of the Hugging Face
+    MoE block the pages compare against [BioNeMo, "MoE训练的瓶颈与TE的对应能力":
+    a Python loop over the experts, one launch per expert and GEMM] -- torch
+    softmax + top-k, then for each expert an index of its tokens,
+    nn.Linear-style GEMMs (torch -> hipBLASLt), SwiGLU, probability scale and
+    index_add; backward through torch autograd.  A measurement baseline only
+    (the product path never runs it).  Returns y and, with backward, the
+    gradients of x, logits, W1 and W2."""
     import torch
     import torch.nn.functional as F
 
-    T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
+    I = w2[0].shape[1]
+    probs, sel = torch.topk(logits, k, dim=1)
+    probs = torch.softmax(probs, dim=1)
+    y = torch.zeros_like(x)
+    for e in range(len(w1)):
+        tok, slot = torch.where(sel == e)
+        if tok.numel() == 0:
+            continue
+        h = F.linear(x[tok], w1[e])
+        a = F.silu(h[:, :I]) * h[:, I:]
+        ye = F.linear(a, w2[e]) * probs[tok, slot, None].to(x.dtype)
+        y = y.index_add(0, tok, ye)
+    if backward:
+        y.backward(dy)
+    return y
+
+
+def run_loop_baseline(args, inp_dev, shape):
+    """The per-expert loop (loop_step), BF16, forward and backward, on the
+    workload's inputs, timed over a few steps."""
+    import torch
+
+    k = shape.k
     w1 = [w.detach().clone().requires_grad_(True) for w in inp_dev["w1"]]
     w2 = [w.detach().clone().requires_grad_(True) for w in inp_dev["w2"]]
     logits = inp_dev["logits"].detach().clone().requires_grad_(True)
@@ -415,19 +444,7 @@ def run_loop_baseline(args, inp_dev, shape):
     dy = inp_dev["dy"]
 
     def step():
-        probs, sel = torch.topk(logits, k, dim=1)
-        probs = torch.softmax(probs, dim=1)
-        y = torch.zeros_like(x)
-        for e in range(E):
-            tok, slot = torch.where(sel == e)
-            if tok.numel() == 0:
-                continue
-            xe = x[tok]
-            h = F.linear(xe, w1[e])
-            a = F.silu(h[:, :I]) * h[:, I:]
-            ye = F.linear(a, w2[e]) * probs[tok, slot, None].to(x.dtype)
-            y = y.index_add(0, tok, ye)
-        y.backward(dy)
+        loop_step(logits, x, w1, w2, dy, k)
         for t in [x, logits, *w1, *w2]:
             t.grad = None
 
@@ -441,16 +458,16 @@ def run_loop_baseline(args, inp_dev, shape):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / n
     return {"kind": "per-expert loop, torch BF16 (autograd)", "steps": n, "ms_per_step": round(ms, 3),
-            "tokens_per_s": round(T / (ms * 1e-3), 1)}
+            "tokens_per_s": round(shape.T / (ms * 1e-3), 1)}
 
 
 def cpu_baseline(args, inp_host, shape, prec_name):
-    """The oracle on a bounded sample: the first `cpu_tokens` tokens and the
-    first `cpu_inter` intermediate columns (gate rows [0, Is), up rows
-    [I, I+Is) of W1, columns [0, Is) of W2) of every expert; the whole layer
-    step in the same precision.  Every part of the step except the activation
-    quantization scales with the intermediate width, so the full-layer rate is
-    taken as sample_tokens * (Is / I) / time."""
+    """The oracle's whole layer step (forward and backward, the workload's
+    precision, its pinned vectorized quantizers) on a bounded sample: the
+    first `cpu_tokens` tokens, at the full hidden and intermediate sizes and
+    all experts.  value = sampled tokens / time, with no extrapolation; the
+    BF16 master weights are quantized in full even for the sample, as in the
+    layer step."""
     import torch
     from oracle import mlp as omlp
 
@@ -464,21 +481,46 @@ def cpu_baseline(args, inp_host, shape, prec_name):
                 break
     except OSError:
         pass
-    Ts, Is = min(args.cpu_tokens, shape.T), min(args.cpu_inter, shape.I)
-    I = shape.I
-    w1 = [torch.cat([w[:Is], w[I:I + Is]]).contiguous() for w in inp_host["w1"]]
-    w2 = [w[:, :Is].contiguous() for w in inp_host["w2"]]
+    Ts = min(args.cpu_tokens, shape.T)
     t0 = time.perf_counter()
-    omlp.layer_step(inp_host["logits"][:Ts], inp_host["x"][:Ts], w1, w2, inp_host["dy"][:Ts],
-                    shape.k, prec_name)
+    omlp.layer_step(inp_host["logits"][:Ts], inp_host["x"][:Ts], inp_host["w1"], inp_host["w2"],
+                    inp_host["dy"][:Ts], shape.k, prec_name, fast_quant=True)
     t = time.perf_counter() - t0
-    return {"value": round(Ts * (Is / I) / t, 3), "unit": "tokens/s", "cores": cores,
+    return {"value": round(Ts / t, 2), "unit": "tokens/s", "cores": cores,
             "threads": torch.get_num_threads(), "cpu_model": cpu_model, "kind": "oracle",
-            "sample": (f"oracle layer step ({prec_name}, fwd+bwd) on the first {Ts} tokens and "
-                       f"the first {Is} of {I} intermediate columns of all {shape.E} experts "
-                       f"(H={shape.H}, k={shape.k}); took {t:.1f} s; full-layer rate "
-                       f"extrapolated by the intermediate fraction"),
+            "sample": (f"oracle layer step ({prec_name}, fwd+bwd, vectorized quantizers) on the "
+                       f"first {Ts} of {shape.T} tokens of the {shape.name} workload, full "
+                       f"H={shape.H}, I={shape.I}, all {shape.E} experts, k={shape.k}; took "
+                       f"{t:.1f} s; value = {Ts} / time"),
             "seconds": round(t, 2)}
+
+
+def run_skewed(args, prec_name):
+    """The fine-grained skewed layer (T=16384, H=2048, I=1408, E=64, k=8,
+    Zipf-biased routing: a fifth of the experts empty, the largest 8x the
+    mean) in the headline precision, with its own roofline line and the
+    per-expert loop baseline on the same inputs."""
+    import torch
+    from mxfp8_block_scaled_top_amd import synth
+
+    sh = synth.SHAPES["skewed"]
+    inp = synth.layer_inputs(sh)
+    dev = {n: (v.cuda() if isinstance(v, torch.Tensor) else [w.cuda() for w in v])
+           for n, v in inp.items()}
+    r = run_gpu(args, prec_name, dev, sh, workload="skewed")
+    out = {"workload": f"{sh.name} layer fwd+bwd, {prec_name}",
+           "config": {"T": sh.T, "H": sh.H, "I": sh.I, "E": sh.E, "k": sh.k},
+           "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
+           "ms_per_step": round(r["ms_per_step"], 4), "step_ms": r["step_ms"],
+           "sclk_mhz": r["sclk_mhz"], "tflops_per_layer": round(r["tflops"], 1),
+           "frac_of_mfma_peak": round(r["frac_of_peak"], 4), "roofline": r["roofline"],
+           "gemm_only": {"ms": round(r["gemm_ms"], 3), "tflops": round(r["gemm_tflops"], 1)},
+           "kernels": r["kernels"]}
+    if not args.no_loop:
+        lb = run_loop_baseline(args, dev, sh)
+        lb["grouped_speedup"] = round(lb["ms_per_step"] / r["ms_per_step"], 2)
+        out["loop_baseline"] = lb
+    return out
 
 
 def main():
@@ -559,6 +601,9 @@ def main():
         lb["grouped_speedup"] = {p: round(lb["ms_per_step"] / res[p]["ms_per_step"], 2) for p in precs}
         out["loop_baseline"] = lb
         log(args, f"per-expert loop: {lb['ms_per_step']} ms/step; grouped speedup {lb['grouped_speedup']}")
+    if args.workload == "mixtral" and not args.no_skewed:
+        out["skewed"] = run_skewed(args, head)
+        log(args, f"skewed: {out['skewed']['ms_per_step']} ms/step, {out['skewed']['value']} tokens/s")
     if not args.no_cpu:
         del dev
         torch.cuda.empty_cache()

@@ -130,6 +130,14 @@ int moe_route(const float* logits, int64_t T, int E, int k, uint32_t flags,
 /*
  * moe_route_bwd -- gradient of the router logits from the gradient of the
  * grouped-row probabilities (backward of the probabilities moe_route made).
+ * [BioNeMo, "MXFP8与融合MLP": the fused MLP's backward has a matching fused
+ *  operation, and ScaledSwiGLU takes the routing probabilities as its scales,
+ *  so they receive a gradient; AutoModel, "MoE 微调的痛点": the probabilities
+ *  come from the routing of each token to a few experts.]
+ * The probability gradient arrives per grouped row (dprob_perm, as
+ * grouped_mlp_bwd writes it) together with dest_row, instead of as a [T, k]
+ * table: the gather dprob[t][j] = dprob_perm[dest_row[t][j]] is done inside
+ * the kernel, so no permuted copy is materialized.
  *
  * topk_prob    fp32 [T, k]  probabilities from moe_route.
  * dprob_perm   fp32 [T*k]   gradient per grouped row (from grouped_mlp_bwd).
@@ -252,7 +260,15 @@ int mxfp8_quantize_both(const uint16_t* x, int64_t rows, int64_t cols,
                         uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
                         hipStream_t stream);
 
-/* Inverse of mxfp8_quantize: out bf16 [rows, cols] = RNE_bf16(decode(code) * 2^(S-127)). */
+/*
+ * mxfp8_dequantize -- inverse of mxfp8_quantize: out bf16 [rows, cols] =
+ * RNE_bf16(decode(code) * 2^(S-127)), the exact value of each code times its
+ * block's scale, rounded once to bf16.
+ * [BioNeMo, bottleneck section: the naive path turns the 8-bit values back
+ *  into a wider format in a separate step after the low-precision GEMM; the
+ *  fused MLP avoids it, and this call serves callers that need it.]
+ * Layouts, groups (axis 0) and errors as for mxfp8_quantize.
+ */
 int mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                      int axis, const int32_t* group_sizes, int ngroups, uint16_t* out,
                      hipStream_t stream);
@@ -422,7 +438,8 @@ typedef enum moe_ws_region {
 
 /* Byte offset and size of `region` inside the workspace of `op`
  * (MOE_OP_MLP_FWD or MOE_OP_MLP_BWD) for these sizes.  Returns MOE_OK,
- * MOE_ERR_ARG when the op/precision has no such region, or MOE_ERR_NULL. */
+ * MOE_ERR_ARG when the op/precision has no such region, MOE_ERR_SHAPE for
+ * sizes out of range, or MOE_ERR_NULL. */
 int moe_workspace_region(int op, int region, int64_t rows, int H, int I, int E, int precision,
                          size_t* offset, size_t* bytes);
 
