@@ -128,6 +128,28 @@ int moe_route(const float* logits, int64_t T, int E, int k, uint32_t flags,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_route_noalloc -- moe_route without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * that must not call hipMalloc, harnesses that forbid it).  Same arguments
+ * (less the workspace) and the same outputs, bit for bit.  Its scratch (the
+ * per-256-token-block expert counts and bases and the picks' ranks, 4 bytes
+ * each) lives in a static device array of MOE_ROUTE_NOALLOC_MAX_BYTES that
+ * every GPU the library runs on holds until the process ends; the call
+ * allocates nothing.  Sizes whose scratch exceeds that, i.e.
+ * 4*(T*k + 2*E*ceil(T/256)) rounded up to 256 bytes, return
+ * MOE_ERR_WORKSPACE before any launch (T*k up to about two million picks
+ * at E = 64).  Every call on one device shares the one array and leaves its
+ * contents behind (nothing in it needs clearing between calls): calls that
+ * overlap in time on one device, from several streams or host threads, race
+ * and must be serialized by the caller.
+ */
+#define MOE_ROUTE_NOALLOC_MAX_BYTES (8u << 20)
+int moe_route_noalloc(const float* logits, int64_t T, int E, int k, uint32_t flags,
+                      int32_t* topk_expert, float* topk_prob, int32_t* split_sizes,
+                      int32_t* expert_offsets, int32_t* dest_row, int32_t* src_token,
+                      hipStream_t stream);
+
+/*
  * moe_route_bwd -- gradient of the router logits from the gradient of the
  * grouped-row probabilities (backward of the probabilities moe_route made).
  * [BioNeMo, "MXFP8与融合MLP": the fused MLP's backward has a matching fused

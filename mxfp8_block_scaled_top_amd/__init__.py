@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
             "moe_workspace_bytes": (SZ, [I32, I64, I32, I32, I32, I32, I32]),
             "moe_route": (I32, [P, I64, I32, I32, U32, P, P, P, P, P, P, P, SZ, P]),
             "moe_route_bwd": (I32, [P, P, P, P, P, I64, I32, I32, U32, P, P]),
+            "moe_route_noalloc": (I32, [P, I64, I32, I32, U32, P, P, P, P, P, P, P]),
             "moe_permute": (I32, [P, I64, I32, I32, P, P, P, P, P]),
             "moe_unpermute": (I32, [P, I64, I32, I32, P, P, P, P]),
             "mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, P, P, P]),
@@ -150,6 +151,31 @@ def moe_route(logits: torch.Tensor, k: int, softmax_all: bool = False) -> dict:
                            _ptr(out["expert_offsets"]), _ptr(out["dest_row"]),
                            _ptr(out["src_token"]), _ptr(ws), ws.numel(), _stream(dev)),
            "moe_route")
+    return out
+
+
+def moe_route_noalloc(logits: torch.Tensor, k: int, softmax_all: bool = False,
+                      out: dict | None = None) -> dict:
+    """moe_route with the library's static scratch instead of a workspace
+    (the call allocates no device memory; pass `out` to reuse output
+    tensors).  Returns the same dict as moe_route."""
+    _dev(logits, torch.float32, "logits")
+    T, E = logits.shape
+    dev = logits.device
+    if out is None:
+        out = {
+            "topk_expert": torch.empty((T, k), dtype=torch.int32, device=dev),
+            "topk_prob": torch.empty((T, k), dtype=torch.float32, device=dev),
+            "split_sizes": torch.empty(E, dtype=torch.int32, device=dev),
+            "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "dest_row": torch.empty((T, k), dtype=torch.int32, device=dev),
+            "src_token": torch.empty(T * k, dtype=torch.int32, device=dev),
+        }
+    _check(lib().moe_route_noalloc(_ptr(logits), T, E, k, int(softmax_all),
+                                   _ptr(out["topk_expert"]), _ptr(out["topk_prob"]),
+                                   _ptr(out["split_sizes"]), _ptr(out["expert_offsets"]),
+                                   _ptr(out["dest_row"]), _ptr(out["src_token"]), _stream(dev)),
+           "moe_route_noalloc")
     return out
 
 

@@ -85,6 +85,24 @@ int moe_route(const float* logits, int64_t T, int E, int k, uint32_t flags, int3
                                    stream));
 }
 
+int moe_route_noalloc(const float* logits, int64_t T, int E, int k, uint32_t flags,
+                      int32_t* topk_expert, float* topk_prob, int32_t* split_sizes,
+                      int32_t* expert_offsets, int32_t* dest_row, int32_t* src_token,
+                      hipStream_t stream) {
+    if (!split_sizes || !expert_offsets) return MOE_ERR_NULL;
+    if (T > 0 && (!logits || !topk_expert || !topk_prob || !dest_row || !src_token))
+        return MOE_ERR_NULL;
+    if (T < 0 || E < 1 || E > kMaxExperts || k < 1 || k > E || T * k > INT32_MAX)
+        return MOE_ERR_SHAPE;
+    if (flags > MOE_ROUTE_SOFTMAX_ALL) return MOE_ERR_ARG;
+    if (route_workspace_bytes(T, E, k) > kRouteScratchBytes) return MOE_ERR_WORKSPACE;
+    if (!device_ok()) return MOE_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    if (route_scratch(&ws) != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(launch_route(logits, (int)T, E, k, flags, topk_expert, topk_prob,
+                                   split_sizes, expert_offsets, dest_row, src_token, ws, stream));
+}
+
 int moe_router_fwd(const uint16_t* x, const uint16_t* w_router, int64_t T, int H, int E, int k,
                    uint32_t flags, float* logits, int32_t* topk_expert, float* topk_prob,
                    int32_t* split_sizes, int32_t* expert_offsets, int32_t* dest_row,

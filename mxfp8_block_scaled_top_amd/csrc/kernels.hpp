@@ -19,6 +19,12 @@ struct MatTable {
 
 // ---- routing / permutation
 size_t route_workspace_bytes(int64_t T, int E, int k);
+// The no-allocation routing scratch: a static device array of this many bytes
+// per device; route_scratch() returns its device address on the current
+// device (taken once per device).
+constexpr size_t kRouteScratchBytes = (size_t)8 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t route_scratch(void** ptr);
 hipError_t launch_route(const float* logits, int T, int E, int k, uint32_t flags,
                         int32_t* topk_expert, float* topk_prob, int32_t* split_sizes,
                         int32_t* expert_offsets, int32_t* dest_row, int32_t* src_token,

@@ -16,6 +16,8 @@
 //   2. route_scan:    one wave.  Per expert, exclusive scan of the block counts
 //                     (the blocks' base rows), split_sizes and offsets.
 //   3. route_scatter: one thread per pick: dest_row and src_token.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "trace.hpp"
@@ -190,6 +192,35 @@ __global__ void route_bwd_kernel(const float* __restrict__ topk_prob,
         float p = topk_prob[base + j];
         out[topk_expert[base + j]] = p * (dprob_perm[dest_row[base + j]] - dot);
     }
+}
+
+// Scratch of the no-allocation routing entry point: one static device array,
+// which every GPU the library runs on holds (each at its own address) until
+// the process ends.  Host code never passes `scratch` itself to a kernel (on
+// the host it names a host-side stand-in): route_scratch() fetches the array's
+// device address once per device, with that device current, and the kernels
+// take that address like the caller's workspace of moe_route.
+static __device__ __align__(256) uint8_t scratch[kRouteScratchBytes];
+
+namespace {
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+}  // namespace
+
+hipError_t route_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    *ptr = g_scratch_ptr[dev];
+    return *ptr ? hipSuccess : hipErrorInvalidSymbol;
 }
 
 size_t route_workspace_bytes(int64_t T, int E, int k) {
