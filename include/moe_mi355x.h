@@ -301,23 +301,35 @@ void mxfp8_colwise_bytes(int64_t rows, int64_t cols, int ngroups, size_t* code_b
                          size_t* scale_bytes);
 
 /*
- * Tensors the forward saves for the backward.  Caller-owned device buffers.
+ * Tensors the forward saves for the backward.  Caller-owned device buffers;
+ * moe_saved_bytes() gives the size of each member.
  *   a1          bf16 [rows, 2I]: gate_up output before the activation (both modes).
  *   a2          BF16 mode: bf16 [rows, I], the ScaledSwiGLU output.
- *   a2_col_*    MXFP8 mode: grouped columnwise MXFP8 of the ScaledSwiGLU
- *               output (groups = experts), mxfp8_colwise_bytes(rows, I, E).
- *   xp_col_*    MXFP8 mode: grouped columnwise MXFP8 of xp, (rows, H, E).
- * The *_col_codes follow the grouped columnwise layout of mxfp8_quantize; the
- * *_col_scales hold the same bytes block-major per group ([P_g/32][cols]
- * at offset cols*sum(P_j/32, j<g)), the order the backward GEMMs read.
+ *   a2_col_*    MXFP8 (FP8) mode: grouped columnwise MXFP8 of the ScaledSwiGLU
+ *               output (groups = experts).
+ *   xp_col_*    MXFP8 (FP8) mode: grouped columnwise MXFP8 of xp.
  *
- * Optional, MXFP8 mode (all four or none; otherwise MOE_ERR_ARG): the
+ * 8-bit GEMM operand layout ("row-pair layout").  The 8-bit operands that the
+ * library keeps for its GEMMs store an R x K byte matrix (K the contraction
+ * axis) so that rows 2p and 2p+1 share 128-byte lines, one line per 64
+ * K-bytes: byte (r, k) sits at
+ *     (r / 2) * PS(K) + (k / 64) * 128 + (r % 2) * 64 + (k % 64),
+ *     PS(K) = 128 * ceil(K / 64),
+ * so that one K step of two neighbouring rows is one whole cache line.  The
+ * *_col_codes hold, per expert e (group g), the transposed group [cols, n_g]
+ * in this layout with K = Q_g = 64*ceil(n_g/64) (padding codes unspecified),
+ * at byte offset cols*(Q_0+..+Q_{g-1}).  Their scales are those of
+ * mxfp8_quantize axis=0 stored block-major per group ([P_g/32][cols] at
+ * offset cols*(P_0+..+P_{g-1})/32, P_g = 32*ceil(n_g/32)), the order the
+ * backward GEMMs read.
+ *
+ * Optional, MXFP8 (FP8) mode (all four or none; otherwise MOE_ERR_ARG): the
  * columnwise MXFP8 of the weights, which the backward's data-gradient GEMMs
  * contract along the other axis than the forward's.
- *   w_gate_up_col_*  E*2I*H code bytes: expert e's W1 quantized along 2I,
- *                    codes [H, 2I] at e*2I*H, scales block-major [2I/32][H]
+ *   w_gate_up_col_*  expert e's W1 quantized along 2I: codes [H, 2I] in the
+ *                    row-pair layout at e*2I*H, scales block-major [2I/32][H]
  *                    (E*2I*H/32 bytes, expert e at e*2I*H/32).
- *   w_down_col_*     E*H*I code bytes: W2_e quantized along H, codes [I, H] at
+ *   w_down_col_*     W2_e quantized along H: codes [I, H] (row-pair layout) at
  *                    e*H*I, scales [H/32][I] at e*H*I/32.
  * When given, grouped_mlp_fwd writes them in the same pass that quantizes the
  * weights rowwise (each weight is read once), and grouped_mlp_bwd uses them
@@ -337,6 +349,12 @@ typedef struct moe_saved {
     uint8_t* w_down_col_codes;
     uint8_t* w_down_col_scales;
 } moe_saved;
+
+/* Bytes of member `member` of moe_saved (0 = a1, 1 = a2, ..., 9 =
+ * w_down_col_scales, in declaration order) for grouped_mlp_fwd/bwd with these
+ * sizes and precision; 0 for a member the precision does not use or invalid
+ * arguments.  Host-side, no launch. */
+size_t moe_saved_bytes(int precision, int member, int64_t rows, int H, int I, int E);
 
 /*
  * grouped_mlp_fwd -- all experts' gate_up -> ScaledSwiGLU -> down in one call.
@@ -422,13 +440,16 @@ size_t moe_workspace_bytes(int op, int64_t T, int H, int I, int E, int k, int pr
  * Regions of the grouped-MLP workspaces (inspection aid).  After
  * grouped_mlp_fwd / grouped_mlp_bwd have run, these regions hold the MXFP8
  * (or FP8) GEMM operands the calls made, until the next call that uses the
- * same workspace.  The codes follow the layouts of mxfp8_quantize; the
- * scales are the same bytes stored block-major, the order the GEMMs read:
- *   rowwise [rows, C]          scales [C/32][rows]
- *   per-expert weights         expert e's codes at e*(its size), scales
- *                              block-major [C/32][R] at e*(its size)/32
- *   grouped columnwise         codes as mxfp8_quantize axis=0 (groups =
- *                              experts); scales [P_g/32][C] per group
+ * same workspace.  The codes are in the row-pair layout described with
+ * moe_saved; the scales are the bytes of mxfp8_quantize stored block-major,
+ * the order the GEMMs read:
+ *   rowwise [rows, C]          expert e's row i at row P_0+..+P_{e-1}+i of a
+ *                              [RP, C] row-pair matrix, RP = 32*(ceil(rows/32)
+ *                              + E) (P_g = 32*ceil(n_g/32)); scales [C/32][RP]
+ *   per-expert weights         expert e's [R, C] row-pair matrix at e*R*C,
+ *                              scales block-major [C/32][R] at e*R*C/32
+ *   grouped columnwise         as the *_col_codes of moe_saved; scales
+ *                              [P_g/32][C] per group
  * The region of MOE_WS_A2_* holds the codes the down GEMM read (rowwise
  * MXFP8 of the ScaledSwiGLU output); *_W1_COL_* and *_W2_COL_* are used
  * only when moe_saved carries no weight copies.

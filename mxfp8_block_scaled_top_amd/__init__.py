@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(_Saved), P, P, P, P, P, SZ, P]),
             "grouped_linear_fwd": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, SZ, P]),
             "grouped_linear_bwd": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P, P, SZ, P]),
+            "moe_saved_bytes": (SZ, [I32, I32, I64, I32, I32, I32]),
             "moe_workspace_region": (I32, [I32, I32, I64, I32, I32, I32, I32,
                                            ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
             "moe_trace_enable": (I32, [I32]),
@@ -315,25 +316,20 @@ def _ptr_array(ts):
 
 def alloc_saved(rows: int, H: int, I: int, E: int, precision: int, device,
                 weight_cols: bool = True) -> dict:
-    """Caller-owned tensors the forward saves for the backward.  weight_cols
-    (MXFP8): also the buffers for the weights' columnwise MXFP8, so that the
-    forward quantizes each weight once for both passes."""
+    """Caller-owned tensors the forward saves for the backward, sized by
+    moe_saved_bytes.  weight_cols (MXFP8/FP8): also the buffers for the
+    weights' columnwise copies, so that the forward quantizes each weight once
+    for both passes."""
+    L = lib()
     s = {"a1": torch.empty((rows, 2 * I), dtype=torch.bfloat16, device=device)}
     if precision == MOE_BF16:
         s["a2"] = torch.empty((rows, I), dtype=torch.bfloat16, device=device)
-    else:
-        cb, sb = colwise_bytes(rows, I, E)
-        s["a2_col_codes"] = torch.empty(cb, dtype=torch.uint8, device=device)
-        s["a2_col_scales"] = torch.empty(sb, dtype=torch.uint8, device=device)
-        cb, sb = colwise_bytes(rows, H, E)
-        s["xp_col_codes"] = torch.empty(cb, dtype=torch.uint8, device=device)
-        s["xp_col_scales"] = torch.empty(sb, dtype=torch.uint8, device=device)
-        if weight_cols:
-            n1, n2 = E * 2 * I * H, E * H * I
-            s["w_gate_up_col_codes"] = torch.empty(n1, dtype=torch.uint8, device=device)
-            s["w_gate_up_col_scales"] = torch.empty(n1 // 32, dtype=torch.uint8, device=device)
-            s["w_down_col_codes"] = torch.empty(n2, dtype=torch.uint8, device=device)
-            s["w_down_col_scales"] = torch.empty(n2 // 32, dtype=torch.uint8, device=device)
+        return s
+    for i, (name, _) in enumerate(_Saved._fields_):
+        if name in ("a1", "a2") or (name.startswith("w_") and not weight_cols):
+            continue
+        n = int(L.moe_saved_bytes(precision, i, rows, H, I, E))
+        s[name] = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
     return s
 
 

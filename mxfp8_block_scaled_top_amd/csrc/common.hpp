@@ -110,6 +110,17 @@ __device__ __forceinline__ float mx_decode(uint32_t code, uint32_t S) {
     return (code & 0x80u) ? -v : v;
 }
 
+// Row-pair layout of the 8-bit GEMM operands: rows 2p and 2p+1 of a matrix
+// with K bytes per row share 128-byte lines, one line per 64 K-bytes, so that
+// one K step (64 bytes) of a tile's row pair is one whole line:
+//   byte (r, k) at (r >> 1) * p2_stride(K) + (k >> 6) * 128 + (r & 1) * 64 + (k & 63)
+// The matrix occupies ceil(R / 2) * p2_stride(K) bytes; bytes of K-steps past
+// K (when K is not a multiple of 64) are padding that no kernel reads.
+__host__ __device__ inline int64_t p2_stride(int64_t K) { return ((K + 63) / 64) * 128; }
+__host__ __device__ inline int64_t p2_off(int64_t r, int64_t k, int64_t ps) {
+    return (r >> 1) * ps + (k >> 6) * 128 + (r & 1) * 64 + (k & 63);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -91,6 +91,8 @@ struct Tile {
     int rows_e;      // M_e (= K extent for G_K)
     int64_t pbase;   // sum of the padded (32) sizes of earlier experts
     int pad_e;       // padded size of this expert
+    int64_t pbase64; // the same sums with sizes padded to 64 (row-pair grouped layouts)
+    int pad64_e;
     int n_tile;
 };
 
@@ -121,6 +123,7 @@ __device__ bool decode_tile(const GemmArgs& g, int ntn, int mtm, int t, int* sch
         sched[64 + lane] = wave_incl_scan(n);
         sched[128 + lane] = n;
         sched[192 + lane] = wave_incl_scan((n + 31) / 32);
+        sched[256 + lane] = wave_incl_scan((n + 63) / 64);
     }
     __syncthreads();
     int e;
@@ -192,13 +195,19 @@ __device__ bool decode_tile(const GemmArgs& g, int ntn, int mtm, int t, int* sch
     tl.rows_e = __builtin_amdgcn_readfirstlane(sched[128 + e]);
     tl.pbase = (int64_t)__builtin_amdgcn_readfirstlane(e ? sched[192 + e - 1] : 0) * 32;
     tl.pad_e = ((tl.rows_e + 31) / 32) * 32;
+    tl.pbase64 = (int64_t)__builtin_amdgcn_readfirstlane(e ? sched[256 + e - 1] : 0) * 64;
+    tl.pad64_e = ((tl.rows_e + 63) / 64) * 64;
     return true;
 }
 
 // ---------------------------------------------------------------- operand loads
-// K-contiguous operand: rows of `stride` bytes from `base`; tile row r maps to
-// operand row kop_row(r) (clamped into [0, rows_valid)); K bytes at or past
-// kbytes read zero.  Offsets from `base` stay below 2^31 (checked by the host).
+// K-contiguous operand from `base`: tile row r maps to operand row kop_row(r)
+// (clamped into [0, rows_valid)); K bytes at or past kbytes read zero.  bf16
+// operands are row-major with rows of `stride` bytes; 8-bit operands are in
+// the row-pair layout (common.hpp) with `stride` bytes per row pair, so the
+// 16 lanes that fill two neighbouring tile rows fetch one whole 128-byte line.
+// The bases are taken per tile (and per expert), so offsets from them stay
+// below 2^31.
 struct KOp {
     const uint8_t* base;
     int64_t stride;
@@ -267,16 +276,24 @@ __device__ __forceinline__ void pipe_barrier() {
 // cover tile rows (wave*4 + j)*16 .. +15; slot i of instruction j is tile row
 // (wave*4 + j)*16 + i/4 and physical chunk i%4, whose logical chunk is
 // (i%4) ^ ((row>>2)&3) = (i%4) ^ ((i>>4)&3).
+template <bool P2>
 __device__ __forceinline__ void dma_kop(const KOp& op, const i32x4& rs, int k0b, uint8_t* lds) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int kc16 = (((lane & 3) ^ ((lane >> 4) & 3)) << 4) + k0b;
+    const int lc16 = ((lane & 3) ^ ((lane >> 4) & 3)) << 4;    // logical 16-byte chunk
+    const int kc16 = lc16 + k0b;
     const uint32_t l0 = lds_u32(lds + wave * 4 * 1024);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         int r = (wave * 4 + j) * 16 + (lane >> 2);
-        uint32_t o = kc16 < op.kbytes
-                         ? (uint32_t)((int64_t)kop_row(op, r) * op.stride) + (uint32_t)kc16
-                         : kOob;
+        const int gr = kop_row(op, r);
+        uint32_t o = kOob;
+        if (kc16 < op.kbytes) {
+            if (P2)   // K step k0b / 64 of row pair gr / 2: line k0b / 64, half gr & 1
+                o = (uint32_t)(gr >> 1) * (uint32_t)op.stride + (uint32_t)(2 * k0b) +
+                    (uint32_t)((gr & 1) * 64 + lc16);
+            else
+                o = (uint32_t)((int64_t)gr * op.stride) + (uint32_t)kc16;
+        }
         dma16(rs, o, l0 + j * 1024);
     }
 }
@@ -293,16 +310,18 @@ struct MNOp {
 // into its natural order: instruction j of the wave covers K rows
 // (wave*4 + j)*2 .. +1; slot i is K row (wave*4+j)*2 + i/32, physical chunk
 // i%32, logical chunk (i%32) ^ ((k&3)<<2).  Rows past k_valid and columns
-// past mn_valid read zeros.
-__device__ __forceinline__ void dma_mnop(const MNOp& op, const i32x4& rs, int k0, uint8_t* lds) {
+// past mn_valid read zeros.  The buffer resource is rebuilt at the step's
+// first K row, so offsets stay below 32 rows whatever the K extent.
+__device__ __forceinline__ void dma_mnop(const MNOp& op, int k0, uint8_t* lds) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const i32x4 rs = make_rsrc(op.base + (int64_t)k0 * op.stride);
     const uint32_t l0 = lds_u32(lds + wave * 4 * 1024);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         int k = (wave * 4 + j) * 2 + (lane >> 5);
         int c = (lane & 31) ^ ((k & 3) << 2);
         bool ok = k0 + k < op.k_valid && c * 8 < op.mn_valid;
-        uint32_t o = ok ? (uint32_t)((int64_t)(k0 + k) * op.stride) + (uint32_t)(c * 16) : kOob;
+        uint32_t o = ok ? (uint32_t)(k * op.stride) + (uint32_t)(c * 16) : kOob;
         dma16(rs, o, l0 + j * 1024);
     }
 }
@@ -522,12 +541,15 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
                         for (int q = 0; q < 4; ++q) amx = max_abs_bf16x2(amx, pk[q]);
                 }
             } else {
+                // rowwise codes in the row-pair layout, the row at its
+                // expert-padded position
                 u32x4 c0, c1;
                 uint32_t S = quant32(a2, c0, c1);
-                u32x4* o = (u32x4*)(g.q_row + gr * I + j0);
+                const int64_t rp = tl.pbase + frow0 + row;
+                u32x4* o = (u32x4*)(g.q_row + p2_off(rp, j0, p2_stride(I)));
                 o[0] = c0;
                 o[1] = c1;
-                g.q_row_s[(j0 / 32) * g.rows + gr] = (uint8_t)S;
+                g.q_row_s[(j0 / 32) * g.rows_pad + rp] = (uint8_t)S;
             }
         } else {
 #pragma unroll
@@ -541,7 +563,7 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
     if (DT == DT_MX && valid > 0) {
         const int q = lane >> 5, jj = lane & 31;
         const int64_t j = tl.n_tile * (kGemmBN / 2) + (2 * c.wn + q) * 32 + jj;
-        col_quant(R, 64 * q + jj, g.q_col + tl.pbase * I + j * tl.pad_e + frow0,
+        col_quant(R, 64 * q + jj, g.q_col + tl.pbase64 * I + p2_off(j, frow0, 2 * tl.pad64_e),
                   g.q_col_s + tl.pbase / 32 * I + (frow0 / 32) * I + j);
     }
     wave_lds_sync();
@@ -692,7 +714,7 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
                 const int cc = col & 127;
                 const int64_t j = (col < 128 ? 0 : I) + jw + cc;
                 col_quant(col < 128 ? R : R2, cc,
-                          g.q_col + tl.pbase * 2 * I + j * tl.pad_e + frow0,
+                          g.q_col + tl.pbase64 * 2 * I + p2_off(j, frow0, 2 * tl.pad64_e),
                           g.q_col_s + tl.pbase / 32 * 2 * I + (frow0 / 32) * 2 * I + j);
             }
         }
@@ -701,7 +723,7 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
         // code bytes replace its first 8 staged values (the lane has read all
         // 32 of them)
         if (slab && row < valid) {
-            const int64_t gr = tl.row0 + frow0 + row;
+            const int64_t rp = tl.pbase + frow0 + row;       // expert-padded row
 #pragma unroll 1
             for (int q = 0; q < 4; ++q) {
                 const int cb = 64 * h + 32 * (q & 1);
@@ -719,24 +741,29 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
                 *(float4*)(src + st_idx(row, cb)) = __builtin_bit_cast(float4, c0);
                 *(float4*)(src + st_idx(row, cb + 4)) = __builtin_bit_cast(float4, c1);
                 const int64_t j = (q < 2 ? 0 : I) + jw + cb;
-                g.q_row_s[(j / 32) * g.rows + gr] = (uint8_t)S;
+                g.q_row_s[(j / 32) * g.rows_pad + rp] = (uint8_t)S;
             }
         }
         wave_lds_sync();
-        // the row codes in whole 128-byte lines (dg codes of the wave's 128 j,
-        // then du's): 8 lanes per line, 8 rows per instruction, streamed
+        // the row codes in whole 128-byte lines of the row-pair layout (dg
+        // codes of the wave's 128 j, then du's): line (pair p, chunk ch)
+        // holds 64 codes of row 2p, then of row 2p+1; 8 lanes per line (the
+        // row's parity c8/4, 16 codes each), 8 lines per instruction, streamed
         if (slab) {
-            const int c8 = lane & 7;
-            const int scol = 32 * (c8 >> 1) + 4 * (c8 & 1);   // block c8/2, code half c8%2
+            const int c8 = lane & 7, half = c8 >> 2, piece = c8 & 3;
+            const int64_t ps = p2_stride(2 * I);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = (lane >> 3) + 8 * i;
+                const int slot = (lane >> 3) + 8 * i;        // (pair, chunk) of 16 x 2
+                const int r = 2 * (slot >> 1) + half, ch = slot & 1;
                 if (r < valid) {
-                    const int64_t gr = tl.row0 + frow0 + r;
+                    const int bo = 64 * ch + 16 * piece;      // code byte in the wave's 128
+                    const int scol = 32 * (bo >> 5) + 4 * ((bo >> 4) & 1);
+                    const int64_t rp = tl.pbase + frow0 + r;
                     const u32x4 cg = __builtin_bit_cast(u32x4, *(const float4*)(R + st_idx(r, scol)));
                     const u32x4 cu = __builtin_bit_cast(u32x4, *(const float4*)(R2 + st_idx(r, scol)));
-                    __builtin_nontemporal_store(cg, (u32x4*)(g.q_row + gr * 2 * I + jw + 16 * c8));
-                    __builtin_nontemporal_store(cu, (u32x4*)(g.q_row + gr * 2 * I + I + jw + 16 * c8));
+                    __builtin_nontemporal_store(cg, (u32x4*)(g.q_row + p2_off(rp, jw + bo, ps)));
+                    __builtin_nontemporal_store(cu, (u32x4*)(g.q_row + p2_off(rp, I + jw + bo, ps)));
                 }
             }
         }
@@ -782,7 +809,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     __shared__ __attribute__((aligned(16))) uint8_t lds3[kStageB];
     __shared__ __attribute__((aligned(16))) uint8_t ssc[kStages][2][2][kGemmBM];   // MXFP8 scales
     __shared__ float red[2 * kGemmBM];                  // probability-gradient row partials
-    __shared__ int sched[256];
+    __shared__ int sched[320];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // uniform
@@ -810,16 +837,26 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     uint32_t soff_a = 0, soff_b = 0, sld_a = 0, sld_b = 0;
     const int r4 = (lane & 63) * 4;    // first of the 4 tile rows whose scales this lane loads
     int nblk = 0;
+    constexpr bool kP2 = DT != DT_BF16;    // 8-bit operands: row-pair layout
     if (GRP == G_M) {
         kext = g.K;
-        ka.base = (const uint8_t*)g.a + (tl.row0 + tl.m0) * g.lda * kElemB;
-        ka.stride = g.lda * kElemB;
+        if (kP2) {
+            // the expert's rows start at its padded row base (a multiple of
+            // 32), so the tile's first row starts a row pair
+            const int64_t rp = tl.pbase + tl.m0;
+            ka.stride = p2_stride(g.K);
+            ka.base = (const uint8_t*)g.a + (rp >> 1) * ka.stride;
+            ka.rows_valid = tl.rows_e - tl.m0;
+        } else {
+            ka.base = (const uint8_t*)g.a + (tl.row0 + tl.m0) * g.lda * kElemB;
+            ka.stride = g.lda * kElemB;
+            ka.rows_valid = (int)(g.rows - (tl.row0 + tl.m0));
+        }
         ka.row_first = 0;
-        ka.rows_valid = (int)(g.rows - (tl.row0 + tl.m0));
         ka.kbytes = g.K * kElemB;
         if (LB == L_KMAJ) {
             kb.base = (const uint8_t*)g.b.p[tl.e];
-            kb.stride = g.ldb * kElemB;
+            kb.stride = kP2 ? p2_stride(g.K) : g.ldb * kElemB;
             kb.row_first = tl.n0;
             kb.rows_valid = EPI == EPI_SWIGLU_FWD ? 2 * g.I : g.N;
             kb.kbytes = g.K * kElemB;
@@ -834,8 +871,8 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         if (DT != DT_BF16) {
             nblk = g.K / 32;
             sbase_a = g.a_scale;
-            soff_a = r4 < ka.rows_valid ? (uint32_t)(tl.row0 + tl.m0 + r4) : kOob;
-            sld_a = (uint32_t)g.rows;
+            soff_a = r4 < ka.rows_valid ? (uint32_t)(tl.pbase + tl.m0 + r4) : kOob;
+            sld_a = (uint32_t)g.rows_pad;
             sbase_b = (const uint8_t*)g.b_scale.p[tl.e];
             soff_b = (kb.pair_I > 0 || kb.row_first + r4 < kb.rows_valid)
                          ? (uint32_t)kop_row(kb, r4) : kOob;
@@ -853,15 +890,19 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
             mb.k_valid = tl.rows_e;
             mb.mn_valid = g.N - tl.n0;
         } else {
-            ka.base = (const uint8_t*)g.a + tl.pbase * g.M;
-            ka.stride = tl.pad_e;
-            ka.row_first = tl.m0;
-            ka.rows_valid = g.M;
+            // grouped columnwise operands in the row-pair layout: the group of
+            // expert e at C * pbase64_e, its rows (the columns of the
+            // activation) 2p, 2p+1 sharing lines of its 64-padded K extent
+            const int64_t ps = (int64_t)tl.pad64_e * 2;
+            ka.base = (const uint8_t*)g.a + tl.pbase64 * g.M + (tl.m0 >> 1) * ps;
+            ka.stride = ps;
+            ka.row_first = 0;
+            ka.rows_valid = g.M - tl.m0;
             ka.kbytes = tl.pad_e;
-            kb.base = (const uint8_t*)g.b.p[0] + tl.pbase * g.N;
-            kb.stride = tl.pad_e;
-            kb.row_first = tl.n0;
-            kb.rows_valid = g.N;
+            kb.base = (const uint8_t*)g.b.p[0] + tl.pbase64 * g.N + (tl.n0 >> 1) * ps;
+            kb.stride = ps;
+            kb.row_first = 0;
+            kb.rows_valid = g.N - tl.n0;
             kb.kbytes = tl.pad_e;
             nblk = tl.pad_e / 32;
             sbase_a = g.a_scale + tl.pbase / 32 * g.M;
@@ -889,8 +930,9 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     // read zeros into stages that are never consumed.
     constexpr int kBatch = 8 + (DT != DT_BF16 ? 1 : 0);
     constexpr int kWait2 = 2 * kBatch;                           // vmcnt(2 batches)
-    const i32x4 rs_a = make_rsrc(LA == L_KMAJ ? (const void*)ka.base : (const void*)ma.base);
-    const i32x4 rs_b = make_rsrc(LB == L_KMAJ ? (const void*)kb.base : (const void*)mb.base);
+    // (M/N-contiguous operands build their buffer resource per K step)
+    const i32x4 rs_a = make_rsrc(LA == L_KMAJ ? (const void*)ka.base : nullptr);
+    const i32x4 rs_b = make_rsrc(LB == L_KMAJ ? (const void*)kb.base : nullptr);
     const i32x4 rs_sa = make_rsrc(sbase_a), rs_sb = make_rsrc(sbase_b);
 
     auto stage_ptr = [&](auto S) -> uint8_t* {
@@ -901,10 +943,10 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     auto issue = [&](auto S, int kt) {
         constexpr int st = decltype(S)::value % kStages;
         uint8_t* base = stage_ptr(S);
-        if (LA == L_KMAJ) dma_kop(ka, rs_a, kt * kRowB, base);
-        else dma_mnop(ma, rs_a, kt * 32, base);
-        if (LB == L_KMAJ) dma_kop(kb, rs_b, kt * kRowB, base + kTileB);
-        else dma_mnop(mb, rs_b, kt * 32, base + kTileB);
+        if (LA == L_KMAJ) dma_kop<kP2>(ka, rs_a, kt * kRowB, base);
+        else dma_mnop(ma, kt * 32, base);
+        if (LB == L_KMAJ) dma_kop<kP2>(kb, rs_b, kt * kRowB, base + kTileB);
+        else dma_mnop(mb, kt * 32, base + kTileB);
         if (DT != DT_BF16)
             dma_scales(rs_sa, rs_sb, soff_a, soff_b, sld_a, sld_b, kt, nblk, ssc[st]);
     };
@@ -1157,6 +1199,13 @@ int64_t gemm_slots(int grp, int epi, int64_t rows, int E, int M, int N, int I) {
     else
         tiles = (int64_t)E * ((M + kGemmBM - 1) / kGemmBM) * ntn;
     return (tiles + 7) / 8 * 8;
+}
+
+int64_t padded_rows(int64_t rows, int E) { return ((rows + 31) / 32 + (E > 1 ? E : 1)) * 32; }
+
+size_t grouped_p2_bytes(int64_t rows, int64_t C, int E) {
+    // C columns of sum_e 64 ceil(M_e / 64) <= 64 (ceil(rows / 64) + E) K bytes
+    return (size_t)C * 64 * (size_t)((rows + 63) / 64 + (E > 1 ? E : 1));
 }
 
 template <int DT, int LA, int LB, int GRP, int EPI, int USE>

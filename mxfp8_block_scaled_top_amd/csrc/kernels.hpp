@@ -53,11 +53,18 @@ int64_t colwise_block_bound(int64_t rows, int ngroups);
 // GEMM reads with one coalesced load per K step; false = the public layout.
 // Rowwise (rcodes given), grouped columnwise (ccodes given) or both, from one
 // read of each matrix.
+// p2_rows_pad > 0: the GEMM operand layouts (row-pair layout, common.hpp):
+// row codes at expert-padded rows (groups from their 32-padded row bases),
+// block-major row scales [cols/32][p2_rows_pad] (rscales_t required); grouped
+// columnwise codes in the row-pair layout of [cols, 64-padded group rows] per
+// group at cols * (sum of the earlier groups' 64-padded sizes), scales as in
+// the public layout (cscales_t: block-major).  0: the public layouts.
 hipError_t launch_quant(const MatTable& src, int nmat, const int32_t* sizes, int ngroups,
                         int64_t rows, int64_t cols, const MatTable* rcodes,
                         const MatTable* rscales, bool rscales_t, const MatTable* ccodes,
                         const MatTable* cscales, bool cscales_t, hipStream_t s,
-                        const char* name, const float* fixed_amax = nullptr);
+                        const char* name, const float* fixed_amax = nullptr,
+                        int64_t p2_rows_pad = 0);
 // Per-tensor FP8: fixed_amax (device, one float per matrix) replaces the block
 // maxima, so every block of matrix m gets the scale of amax[m].
 // amax[m] = max |x| over matrix m's n values (n a multiple of 8); ws holds
@@ -71,11 +78,16 @@ hipError_t launch_amax_final(const uint32_t* part, int nparts, float* amax, hipS
                              const char* name);
 hipError_t launch_quant_rows(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, int64_t rows, int64_t cols, hipStream_t s,
-                             const char* name = "mx_quant_rows", bool scales_t = false);
+                             const char* name = "mx_quant_rows", bool scales_t = false,
+                             int64_t p2_rows_pad = 0);
 hipError_t launch_quant_cols(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, const int32_t* sizes, int ngroups, int64_t rows,
                              int64_t cols, hipStream_t s, const char* name = "mx_quant_cols",
-                             bool scales_t = false);
+                             bool scales_t = false, int64_t p2_rows_pad = 0);
+// Bytes of an R x K 8-bit matrix in the row-pair layout.
+inline size_t p2_bytes(int64_t R, int64_t K) {
+    return (size_t)((R + 1) / 2) * (size_t)(((K + 63) / 64) * 128);
+}
 hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                int64_t cols, bf16_t* out, hipStream_t s);
 hipError_t launch_dequant_cols(const uint8_t* codes, const uint8_t* scales, const int32_t* sizes,

@@ -52,10 +52,11 @@ struct LinFwdWs {
 LinFwdWs carve_lin_fwd(void* base, int64_t rows, int N, int K, int E, int precision) {
     Carve c(base);
     LinFwdWs w{};
-    if (precision == MOE_MXFP8) {
-        w.xq = c.take((size_t)rows * K);
-        w.xq_s = c.take((size_t)rows * K / 32);
-        w.wq = c.take((size_t)E * N * K);
+    if (precision == MOE_MXFP8) {   // 8-bit operands in the row-pair layout
+        const int64_t rp = padded_rows(rows, E);
+        w.xq = c.take(p2_bytes(rp, K));
+        w.xq_s = c.take((size_t)rp * K / 32);
+        w.wq = c.take((size_t)E * p2_bytes(N, K));
         w.wq_s = c.take((size_t)E * N * K / 32);
     }
     c.take(256);
@@ -74,15 +75,16 @@ struct LinBwdWs {
 LinBwdWs carve_lin_bwd(void* base, int64_t rows, int N, int K, int E, int precision) {
     Carve c(base);
     LinBwdWs w{};
-    if (precision == MOE_MXFP8) {
-        w.dyq = c.take((size_t)rows * N);
-        w.dyq_s = c.take((size_t)rows * N / 32);
+    if (precision == MOE_MXFP8) {   // 8-bit operands in the row-pair layout
+        const int64_t rp = padded_rows(rows, E);
+        w.dyq = c.take(p2_bytes(rp, N));
+        w.dyq_s = c.take((size_t)rp * N / 32);
         const size_t cn = colwise_codes(rows, N, E), ck = colwise_codes(rows, K, E);
-        w.dyc = c.take(cn);
+        w.dyc = c.take(grouped_p2_bytes(rows, N, E));
         w.dyc_s = c.take(cn / 32);
-        w.wc = c.take((size_t)E * N * K);
+        w.wc = c.take((size_t)E * p2_bytes(K, N));
         w.wc_s = c.take((size_t)E * N * K / 32);
-        w.xc = c.take(ck);
+        w.xc = c.take(grouped_p2_bytes(rows, K, E));
         w.xc_s = c.take(ck / 32);
     }
     c.take(256);
@@ -143,6 +145,7 @@ int grouped_linear_fwd(int precision, int E, int N, int K, int64_t rows, const u
     g.split = split_sizes;
     g.E = E;
     g.rows = rows;
+    g.rows_pad = padded_rows(rows, E);
     g.N = N;
     g.K = K;
     g.c = y;
@@ -161,14 +164,16 @@ int grouped_linear_fwd(int precision, int E, int N, int K, int64_t rows, const u
     src.p[0] = x;
     cd.p[0] = ws.xq;
     sc.p[0] = ws.xq_s;
-    MOE_TRY(launch_quant_rows(src, cd, sc, 1, rows, K, stream, "linear_mx_quant_x", true));
+    // x along K at the experts' padded rows (the group walk places them)
+    MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, K, &cd, &sc, true, nullptr, nullptr, false,
+                         stream, "linear_mx_quant_x", nullptr, g.rows_pad));
     MatTable wt{}, wq{}, wsc{};
     for (int e = 0; e < E; ++e) {
         wt.p[e] = w[e];
-        wq.p[e] = ws.wq + (size_t)e * N * K;
+        wq.p[e] = ws.wq + (size_t)e * p2_bytes(N, K);
         wsc.p[e] = ws.wq_s + (size_t)e * N * K / 32;
     }
-    MOE_TRY(launch_quant_rows(wt, wq, wsc, E, N, K, stream, "linear_mx_quant_w", true));
+    MOE_TRY(launch_quant_rows(wt, wq, wsc, E, N, K, stream, "linear_mx_quant_w", true, N));
     g.a = ws.xq;
     g.a_scale = ws.xq_s;
     g.lda_s = K / 32;
@@ -206,6 +211,7 @@ int grouped_linear_bwd(int precision, int E, int N, int K, int64_t rows, const u
     dg.split = split_sizes;
     dg.E = E;
     dg.rows = rows;
+    dg.rows_pad = padded_rows(rows, E);
     dg.N = K;
     dg.K = N;
     dg.c = dx;
@@ -215,6 +221,7 @@ int grouped_linear_bwd(int precision, int E, int N, int K, int64_t rows, const u
     wg.split = split_sizes;
     wg.E = E;
     wg.rows = rows;
+    wg.rows_pad = dg.rows_pad;
     wg.M = N;
     wg.N = K;
     wg.c_tab = dwt;
@@ -249,18 +256,18 @@ int grouped_linear_bwd(int precision, int E, int N, int K, int64_t rows, const u
         cs.p[0] = ws.dyc_s;
         MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, N, dx ? &rc : nullptr,
                              dx ? &rs : nullptr, true, dw ? &cc : nullptr, dw ? &cs : nullptr,
-                             true, stream, "linear_mx_quant_dy"));
+                             true, stream, "linear_mx_quant_dy", nullptr, dg.rows_pad));
     }
     if (dx && rows > 0) {
         MatTable wt{}, wc{}, wcs{};
         for (int e = 0; e < E; ++e) {
             wt.p[e] = w[e];
-            wc.p[e] = ws.wc + (size_t)e * N * K;
+            wc.p[e] = ws.wc + (size_t)e * p2_bytes(K, N);
             wcs.p[e] = ws.wc_s + (size_t)e * N * K / 32;
         }
         // W_e [N, K] in 32-row blocks along N, stored [K, N]
         MOE_TRY(launch_quant_cols(wt, wc, wcs, E, nullptr, 1, N, K, stream, "linear_mx_quant_w",
-                                  true));
+                                  true, N));
         dg.a = ws.dyq;
         dg.a_scale = ws.dyq_s;
         dg.lda_s = N / 32;
@@ -278,7 +285,7 @@ int grouped_linear_bwd(int precision, int E, int N, int K, int64_t rows, const u
             cc.p[0] = ws.xc;
             cs.p[0] = ws.xc_s;
             MOE_TRY(launch_quant_cols(src, cc, cs, 1, split_sizes, E, rows, K, stream,
-                                      "linear_mx_quant_x", true));
+                                      "linear_mx_quant_x", true, dg.rows_pad));
         }
         wg.a = ws.dyc;
         wg.a_scale = ws.dyc_s;

@@ -57,18 +57,21 @@ struct FwdWs {
     size_t bytes;
 };
 
+// 8-bit operands are stored in the row-pair layout (common.hpp); activation
+// rows at their expert-padded positions (padded_rows(rows, E) of them).
 FwdWs carve_fwd(void* base, int64_t rows, int H, int I, int E, int precision) {
     Carve c(base);
     FwdWs w{};
     if (precision != MOE_BF16) {
-        w.xq = c.take((size_t)rows * H);
-        w.xq_s = c.take((size_t)rows * H / 32);
-        w.w1q = c.take((size_t)E * 2 * I * H);
+        const int64_t rp = padded_rows(rows, E);
+        w.xq = c.take(p2_bytes(rp, H));
+        w.xq_s = c.take((size_t)rp * H / 32);
+        w.w1q = c.take((size_t)E * p2_bytes(2 * (int64_t)I, H));
         w.w1q_s = c.take((size_t)E * 2 * I * H / 32);
-        w.w2q = c.take((size_t)E * H * I);
+        w.w2q = c.take((size_t)E * p2_bytes(H, I));
         w.w2q_s = c.take((size_t)E * H * I / 32);
-        w.a2q = c.take((size_t)rows * I);
-        w.a2q_s = c.take((size_t)rows * I / 32);
+        w.a2q = c.take(p2_bytes(rp, I));
+        w.a2q_s = c.take((size_t)rp * I / 32);
     }
     if (precision == MOE_FP8) {
         w.a2bf = c.take((size_t)rows * I * 2);
@@ -106,20 +109,19 @@ BwdWs carve_bwd(void* base, int64_t rows, int H, int I, int E, int precision) {
     if (precision == MOE_BF16) {
         w.da1 = c.take((size_t)rows * 2 * I * 2);
     } else {
-        w.dyq = c.take((size_t)rows * H);
-        w.dyq_s = c.take((size_t)rows * H / 32);
-        size_t ch = colwise_codes(rows, H, E);
-        w.dyc = c.take(ch);
-        w.dyc_s = c.take(ch / 32);
-        w.w2c = c.take((size_t)E * H * I);
+        const int64_t rp = padded_rows(rows, E);
+        w.dyq = c.take(p2_bytes(rp, H));
+        w.dyq_s = c.take((size_t)rp * H / 32);
+        w.dyc = c.take(grouped_p2_bytes(rows, H, E));
+        w.dyc_s = c.take(colwise_codes(rows, H, E) / 32);
+        w.w2c = c.take((size_t)E * p2_bytes(I, H));
         w.w2c_s = c.take((size_t)E * H * I / 32);
-        w.w1c = c.take((size_t)E * 2 * I * H);
+        w.w1c = c.take((size_t)E * p2_bytes(H, 2 * (int64_t)I));
         w.w1c_s = c.take((size_t)E * 2 * I * H / 32);
-        w.da1q = c.take((size_t)rows * 2 * I);
-        w.da1q_s = c.take((size_t)rows * 2 * I / 32);
-        size_t ci = colwise_codes(rows, 2 * (int64_t)I, E);
-        w.da1c = c.take(ci);
-        w.da1c_s = c.take(ci / 32);
+        w.da1q = c.take(p2_bytes(rp, 2 * (int64_t)I));
+        w.da1q_s = c.take((size_t)rp * 2 * I / 32);
+        w.da1c = c.take(grouped_p2_bytes(rows, 2 * (int64_t)I, E));
+        w.da1c_s = c.take(colwise_codes(rows, 2 * (int64_t)I, E) / 32);
     }
     if (precision == MOE_FP8) {
         w.da1 = c.take((size_t)rows * 2 * I * 2);
@@ -190,38 +192,39 @@ int mlp_workspace_region(int op, int region, int64_t rows, int H, int I, int E, 
     if (!offset || !bytes) return MOE_ERR_NULL;
     if (precision != MOE_MXFP8 && precision != MOE_FP8) return MOE_ERR_ARG;
     if (rows < 0 || E < 1 || E > kMaxExperts || H < 1 || I < 1) return MOE_ERR_SHAPE;
-    const size_t r = (size_t)rows, w1 = (size_t)E * 2 * I * H, w2 = (size_t)E * H * I;
+    const int64_t rp = padded_rows(rows, E);
+    const size_t w1 = (size_t)E * 2 * I * H, w2 = (size_t)E * H * I;
     const uint8_t* p = nullptr;
     size_t n = 0;
     if (op == MOE_OP_MLP_FWD) {
         // carved from a non-null base (256) so that every region gets a pointer
         FwdWs o = carve_fwd((void*)(uintptr_t)256, rows, H, I, E, precision);
         switch (region) {
-            case MOE_WS_XP_CODES: p = o.xq; n = r * H; break;
-            case MOE_WS_XP_SCALES: p = o.xq_s; n = r * H / 32; break;
-            case MOE_WS_W1_CODES: p = o.w1q; n = w1; break;
+            case MOE_WS_XP_CODES: p = o.xq; n = p2_bytes(rp, H); break;
+            case MOE_WS_XP_SCALES: p = o.xq_s; n = (size_t)rp * H / 32; break;
+            case MOE_WS_W1_CODES: p = o.w1q; n = (size_t)E * p2_bytes(2 * (int64_t)I, H); break;
             case MOE_WS_W1_SCALES: p = o.w1q_s; n = w1 / 32; break;
-            case MOE_WS_W2_CODES: p = o.w2q; n = w2; break;
+            case MOE_WS_W2_CODES: p = o.w2q; n = (size_t)E * p2_bytes(H, I); break;
             case MOE_WS_W2_SCALES: p = o.w2q_s; n = w2 / 32; break;
-            case MOE_WS_A2_CODES: p = o.a2q; n = r * I; break;
-            case MOE_WS_A2_SCALES: p = o.a2q_s; n = r * I / 32; break;
+            case MOE_WS_A2_CODES: p = o.a2q; n = p2_bytes(rp, I); break;
+            case MOE_WS_A2_SCALES: p = o.a2q_s; n = (size_t)rp * I / 32; break;
             default: return MOE_ERR_ARG;
         }
     } else if (op == MOE_OP_MLP_BWD) {
         BwdWs o = carve_bwd((void*)(uintptr_t)256, rows, H, I, E, precision);
         const size_t ch = colwise_codes(rows, H, E), ci = colwise_codes(rows, 2 * (int64_t)I, E);
         switch (region) {
-            case MOE_WS_DYP_CODES: p = o.dyq; n = r * H; break;
-            case MOE_WS_DYP_SCALES: p = o.dyq_s; n = r * H / 32; break;
-            case MOE_WS_DYP_COL_CODES: p = o.dyc; n = ch; break;
+            case MOE_WS_DYP_CODES: p = o.dyq; n = p2_bytes(rp, H); break;
+            case MOE_WS_DYP_SCALES: p = o.dyq_s; n = (size_t)rp * H / 32; break;
+            case MOE_WS_DYP_COL_CODES: p = o.dyc; n = grouped_p2_bytes(rows, H, E); break;
             case MOE_WS_DYP_COL_SCALES: p = o.dyc_s; n = ch / 32; break;
-            case MOE_WS_W2_COL_CODES: p = o.w2c; n = w2; break;
+            case MOE_WS_W2_COL_CODES: p = o.w2c; n = (size_t)E * p2_bytes(I, H); break;
             case MOE_WS_W2_COL_SCALES: p = o.w2c_s; n = w2 / 32; break;
-            case MOE_WS_W1_COL_CODES: p = o.w1c; n = w1; break;
+            case MOE_WS_W1_COL_CODES: p = o.w1c; n = (size_t)E * p2_bytes(H, 2 * (int64_t)I); break;
             case MOE_WS_W1_COL_SCALES: p = o.w1c_s; n = w1 / 32; break;
-            case MOE_WS_DA1_CODES: p = o.da1q; n = r * 2 * I; break;
-            case MOE_WS_DA1_SCALES: p = o.da1q_s; n = r * 2 * I / 32; break;
-            case MOE_WS_DA1_COL_CODES: p = o.da1c; n = ci; break;
+            case MOE_WS_DA1_CODES: p = o.da1q; n = p2_bytes(rp, 2 * (int64_t)I); break;
+            case MOE_WS_DA1_SCALES: p = o.da1q_s; n = (size_t)rp * 2 * I / 32; break;
+            case MOE_WS_DA1_COL_CODES: p = o.da1c; n = grouped_p2_bytes(rows, 2 * (int64_t)I, E); break;
             case MOE_WS_DA1_COL_SCALES: p = o.da1c_s; n = ci / 32; break;
             default: return MOE_ERR_ARG;
         }
@@ -232,6 +235,25 @@ int mlp_workspace_region(int op, int region, int64_t rows, int H, int I, int E, 
     *offset = (size_t)((uintptr_t)p - 256);
     *bytes = n;
     return MOE_OK;
+}
+
+size_t mlp_saved_bytes(int precision, int member, int64_t rows, int H, int I, int E) {
+    if (rows < 0 || E < 1 || E > kMaxExperts || H < 1 || I < 1) return 0;
+    const bool q8 = precision == MOE_MXFP8 || precision == MOE_FP8;
+    if (!q8 && precision != MOE_BF16) return 0;
+    switch (member) {
+        case 0: return (size_t)rows * 2 * I * 2;                         // a1
+        case 1: return q8 ? 0 : (size_t)rows * I * 2;                    // a2
+        case 2: return q8 ? grouped_p2_bytes(rows, I, E) : 0;            // a2_col_codes
+        case 3: return q8 ? colwise_codes(rows, I, E) / 32 : 0;          // a2_col_scales
+        case 4: return q8 ? grouped_p2_bytes(rows, H, E) : 0;            // xp_col_codes
+        case 5: return q8 ? colwise_codes(rows, H, E) / 32 : 0;          // xp_col_scales
+        case 6: return q8 ? (size_t)E * p2_bytes(H, 2 * (int64_t)I) : 0; // w_gate_up_col_codes
+        case 7: return q8 ? (size_t)E * 2 * I * H / 32 : 0;              // w_gate_up_col_scales
+        case 8: return q8 ? (size_t)E * p2_bytes(I, H) : 0;              // w_down_col_codes
+        case 9: return q8 ? (size_t)E * H * I / 32 : 0;                  // w_down_col_scales
+        default: return 0;
+    }
 }
 
 size_t mlp_fwd_workspace_bytes(int64_t rows, int H, int I, int E, int precision) {
@@ -252,6 +274,10 @@ extern "C" {
 int moe_workspace_region(int op, int region, int64_t rows, int H, int I, int E, int precision,
                          size_t* offset, size_t* bytes) {
     return mlp_workspace_region(op, region, rows, H, I, E, precision, offset, bytes);
+}
+
+size_t moe_saved_bytes(int precision, int member, int64_t rows, int H, int I, int E) {
+    return mlp_saved_bytes(precision, member, rows, H, I, E);
 }
 
 int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint16_t* xp,
@@ -286,6 +312,7 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     g.split = split_sizes;
     g.E = E;
     g.rows = rows;
+    g.rows_pad = padded_rows(rows, E);
     g.prob = prob_perm;
     g.I = I;
     if (precision == MOE_BF16) {
@@ -324,8 +351,9 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     ccd.p[0] = saved->xp_col_codes;
     csc.p[0] = saved->xp_col_scales;
     if (fp8) MOE_TRY(launch_amax(src, 1, rows * H, w.amax_ws, w.amax, stream, "fp8_amax_xp"));
+    const int64_t rpad = padded_rows(rows, E);
     MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, H, &cd, &sc, true, &ccd, &csc, true, stream,
-                         fp8 ? "fp8_quant_xp" : "mx_quant_xp", fp8 ? w.amax : nullptr));
+                         fp8 ? "fp8_quant_xp" : "mx_quant_xp", fp8 ? w.amax : nullptr, rpad));
     // weights: rowwise (along H for W1, along I for W2) for these GEMMs; with
     // the saved columnwise buffers, also the backward's copies from the same read
     MatTable w1t{}, w1c{}, w1s{}, w2t{}, w2c{}, w2s{};
@@ -348,15 +376,16 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     if (saved->w_gate_up_col_codes) {
         WeightCols wc = weight_cols(saved, E, H, I);
         MOE_TRY(launch_quant(w1t, E, nullptr, 1, 2 * (int64_t)I, H, &w1c, &w1s, true, &wc.w1c,
-                             &wc.w1s, true, stream, fp8 ? "fp8_quant_w1" : "mx_quant_w1", aw1));
+                             &wc.w1s, true, stream, fp8 ? "fp8_quant_w1" : "mx_quant_w1", aw1,
+                             2 * (int64_t)I));
         MOE_TRY(launch_quant(w2t, E, nullptr, 1, H, I, &w2c, &w2s, true, &wc.w2c, &wc.w2s, true,
-                             stream, fp8 ? "fp8_quant_w2" : "mx_quant_w2", aw2));
+                             stream, fp8 ? "fp8_quant_w2" : "mx_quant_w2", aw2, H));
     } else {
         MOE_TRY(launch_quant(w1t, E, nullptr, 1, 2 * (int64_t)I, H, &w1c, &w1s, true, nullptr,
                              nullptr, false, stream, fp8 ? "fp8_quant_rows_w1" : "mx_quant_rows_w1",
-                             aw1));
+                             aw1, 2 * (int64_t)I));
         MOE_TRY(launch_quant(w2t, E, nullptr, 1, H, I, &w2c, &w2s, true, nullptr, nullptr, false,
-                             stream, fp8 ? "fp8_quant_rows_w2" : "mx_quant_rows_w2", aw2));
+                             stream, fp8 ? "fp8_quant_rows_w2" : "mx_quant_rows_w2", aw2, H));
     }
 
     g.a = w.xq;
@@ -392,12 +421,13 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
         // the maximum from the GEMM epilogue's per-workgroup partials
         MOE_TRY(launch_amax_final(w.a2_part, w.a2_nparts, aa2, stream, "fp8_amax_a2"));
         MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, I, &cd, &sc, true, &ccd, &csc, true,
-                             stream, "fp8_quant_a2", aa2));
+                             stream, "fp8_quant_a2", aa2, rpad));
     }
     GemmArgs d{};
     d.split = split_sizes;
     d.E = E;
     d.rows = rows;
+    d.rows_pad = padded_rows(rows, E);
     d.I = I;
     d.a = w.a2q;
     d.lda = I;
@@ -462,6 +492,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         g.split = split_sizes;
         g.E = E;
         g.rows = rows;
+        g.rows_pad = padded_rows(rows, E);
         g.prob = prob_perm;
         g.I = I;
         if (rows > 0) {
@@ -484,6 +515,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         wg.split = split_sizes;
         wg.E = E;
         wg.rows = rows;
+        wg.rows_pad = padded_rows(rows, E);
         wg.a = dyp;
         wg.lda = H;
         wg.b.p[0] = saved->a2;
@@ -500,6 +532,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
             dg.split = split_sizes;
             dg.E = E;
             dg.rows = rows;
+            dg.rows_pad = padded_rows(rows, E);
             dg.a = w.da1;
             dg.lda = 2 * I;
             for (int e = 0; e < E; ++e) dg.b.p[e] = w_gate_up[e];
@@ -516,6 +549,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         wg1.split = split_sizes;
         wg1.E = E;
         wg1.rows = rows;
+        wg1.rows_pad = padded_rows(rows, E);
         wg1.a = w.da1;
         wg1.lda = 2 * I;
         wg1.b.p[0] = xp;
@@ -532,6 +566,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     // ---- MXFP8 and FP8 (per-tensor scales from each tensor's amax)
     const bool fp8 = precision == MOE_FP8;
     const int dt8 = fp8 ? DT_FP8 : DT_MX;
+    const int64_t rpad = padded_rows(rows, E);
     MatTable src{}, cd{}, sc{};
     if (rows > 0) {
         // rowwise for the down dgrad, grouped columnwise for the down wgrad
@@ -544,7 +579,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         if (fp8) MOE_TRY(launch_amax(src, 1, rows * H, w.amax_ws, w.amax, stream, "fp8_amax_dyp"));
         MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, H, &cd, &sc, true, &ccd, &csc, true,
                              stream, fp8 ? "fp8_quant_dyp" : "mx_quant_dyp",
-                             fp8 ? w.amax : nullptr));
+                             fp8 ? w.amax : nullptr, rpad));
     }
     MatTable w1t{}, w1c{}, w1s{}, w2t{}, w2c{}, w2s{};
     for (int e = 0; e < E; ++e) {
@@ -575,15 +610,17 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
             }
             MOE_TRY(launch_quant(w2t, E, nullptr, 1, H, I, nullptr, nullptr, false, &w2c, &w2s,
                                  true, stream, fp8 ? "fp8_quant_cols_w2" : "mx_quant_cols_w2",
-                                 aw2));
+                                 aw2, H));
             MOE_TRY(launch_quant(w1t, E, nullptr, 1, 2 * (int64_t)I, H, nullptr, nullptr, false,
                                  &w1c, &w1s, true, stream,
-                                 fp8 ? "fp8_quant_cols_w1" : "mx_quant_cols_w1", aw1));
+                                 fp8 ? "fp8_quant_cols_w1" : "mx_quant_cols_w1", aw1,
+                                 2 * (int64_t)I));
         }
         GemmArgs g{};
         g.split = split_sizes;
         g.E = E;
         g.rows = rows;
+        g.rows_pad = padded_rows(rows, E);
         g.prob = prob_perm;
         g.I = I;
         g.a = w.dyq;
@@ -622,7 +659,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
             // the maximum from the GEMM epilogue's per-workgroup partials
             MOE_TRY(launch_amax_final(w.da1_part, w.da1_nparts, ad, stream, "fp8_amax_da1"));
             MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, 2 * (int64_t)I, &cd, &sc, true,
-                                 &ccd, &csc, true, stream, "fp8_quant_da1", ad));
+                                 &ccd, &csc, true, stream, "fp8_quant_da1", ad, rpad));
         }
     }
     // down wgrad: dW2 [H, I] = dYp^T A2 over grouped columnwise operands
@@ -630,6 +667,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     wg.split = split_sizes;
     wg.E = E;
     wg.rows = rows;
+    wg.rows_pad = padded_rows(rows, E);
     wg.a = w.dyc;
     wg.a_scale = w.dyc_s;
     wg.b.p[0] = saved->a2_col_codes;
@@ -645,6 +683,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         dg.split = split_sizes;
         dg.E = E;
         dg.rows = rows;
+        dg.rows_pad = padded_rows(rows, E);
         dg.a = w.da1q;
         dg.lda = 2 * I;
         dg.a_scale = w.da1q_s;
@@ -664,6 +703,7 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     wg1.split = split_sizes;
     wg1.E = E;
     wg1.rows = rows;
+    wg1.rows_pad = padded_rows(rows, E);
     wg1.a = w.da1c;
     wg1.a_scale = w.da1c_s;
     wg1.b.p[0] = saved->xp_col_codes;

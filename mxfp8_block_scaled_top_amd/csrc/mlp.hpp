@@ -33,7 +33,10 @@ constexpr int kGemmBM = 256, kGemmBN = 256, kGemmThreads = 256;
 //      and C_e (= c_tab.p[e], [M, N]) = A_rows^T B_rows, contracting over them
 //      (bf16: both L_MNMAJ); MXFP8: both operands are the grouped columnwise
 //      layouts, [M, P_e] and [N, P_e] at the group's offset (L_KMAJ).
-// Strides are in elements for bf16 operands and in bytes for MXFP8 codes.
+// 8-bit operands (MXFP8, FP8) are in the row-pair layout (common.hpp): the
+// G_M A operand in the expert-padded row order (rows_pad), the weights per
+// expert, the grouped columnwise operands per group at C * (sum of the
+// 64-padded sizes of earlier groups).  bf16 strides are in elements.
 struct GemmArgs {
     const void* a;
     int64_t lda;
@@ -46,6 +49,9 @@ struct GemmArgs {
     const int32_t* split;
     int E;
     int64_t rows;       // total grouped rows
+    int64_t rows_pad;   // 8-bit row operands (G_M A operand, epilogue row codes): rows
+                        // in the expert-padded order (expert e from its 32-padded row
+                        // base), the row stride of their block-major scales
     int M, N, K;        // G_M: N and K; G_K: M and N (K ragged)
     void* c;            // G_M output base (bf16)
     int64_t ldc;
@@ -71,10 +77,15 @@ hipError_t launch_dprob_reduce(const float* part, int64_t rows, int ntiles, floa
 int gemm_n_tiles(int epi, int N, int I);
 // Workgroups (tile slots, a multiple of 8) of one grouped GEMM launch.
 int64_t gemm_slots(int grp, int epi, int64_t rows, int E, int M, int N, int I);
+// Rows of the expert-padded order (an upper bound of sum_e 32 ceil(M_e / 32))
+// and bytes of a grouped columnwise row-pair buffer of C columns.
+int64_t padded_rows(int64_t rows, int E);
+size_t grouped_p2_bytes(int64_t rows, int64_t C, int E);
 
 size_t mlp_fwd_workspace_bytes(int64_t rows, int H, int I, int E, int precision);
 int mlp_workspace_region(int op, int region, int64_t rows, int H, int I, int E, int precision,
                          size_t* offset, size_t* bytes);
+size_t mlp_saved_bytes(int precision, int member, int64_t rows, int H, int I, int E);
 size_t linear_fwd_workspace_bytes(int64_t rows, int N, int K, int E, int precision);
 size_t linear_bwd_workspace_bytes(int64_t rows, int N, int K, int E, int precision);
 size_t mlp_bwd_workspace_bytes(int64_t rows, int H, int I, int E, int precision);

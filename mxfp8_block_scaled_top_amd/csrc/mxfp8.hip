@@ -75,11 +75,13 @@ struct ColBlock {
     int64_t pad_rows;  // P_g of the block's group
     int64_t pbase;     // P_0 + .. + P_{g-1}
     int64_t i0;        // row of the block inside its (padded) group
+    int64_t pad64;     // the group's size padded to 64, and the sum of those of
+    int64_t pbase64;   // the earlier groups (row-pair grouped layout)
 };
 
 __device__ ColBlock locate_col_block(const int32_t* __restrict__ sizes, int ngroups,
                                      int64_t rows, int64_t q, int* lds) {
-    // lds: 3 * 64 ints; filled by the first wave.
+    // lds: 4 * 64 ints; filled by the first wave.
     const int tid = threadIdx.x;
     if (tid < 64) {
         int n = 0;
@@ -91,9 +93,10 @@ __device__ ColBlock locate_col_block(const int32_t* __restrict__ sizes, int ngro
         lds[tid] = inb;          // inclusive block prefix
         lds[64 + tid] = inr;     // inclusive row prefix
         lds[128 + tid] = n;
+        lds[192 + tid] = wave_incl_scan((n + 63) / 64);   // inclusive 64-row-chunk prefix
     }
     __syncthreads();
-    ColBlock cb{0, 0, 0, 0, 0};
+    ColBlock cb{0, 0, 0, 0, 0, 0, 0};
     int G = sizes ? ngroups : 1;
     int g = 0;
     while (g < G && lds[g] <= q) ++g;   // first group whose inclusive prefix passes q
@@ -106,6 +109,8 @@ __device__ ColBlock locate_col_block(const int32_t* __restrict__ sizes, int ngro
     cb.valid = (int)min((int64_t)kMxBlock, (int64_t)n - cb.i0);
     cb.pad_rows = (int64_t)((n + kMxBlock - 1) / kMxBlock) * kMxBlock;
     cb.pbase = (int64_t)bex * kMxBlock;
+    cb.pad64 = (int64_t)((n + 63) / 64) * 64;
+    cb.pbase64 = (int64_t)(g ? lds[192 + g - 1] : 0) * 64;
     return cb;
 }
 
@@ -142,6 +147,11 @@ struct QuantTileArgs {
     int ngroups;
     int64_t rows, cols;
     int rscales_t, cscales_t;
+    int p2;                     // GEMM operand layouts: row codes in the row-pair
+                                // layout at expert-padded rows (scales [cols/32]
+                                // [rows_pad]); grouped columnwise codes in the
+                                // row-pair layout of each group's 64-padded rows
+    int64_t rows_pad;
     const float* amax;          // per-tensor mode: amax of matrix m (one scale for all
                                 // its blocks, still written to every scale slot)
 };
@@ -158,7 +168,7 @@ __device__ __forceinline__ uint32_t abs2(uint32_t w) { return w & 0x7fff7fffu; }
 
 template <bool ROWS, bool COLS, bool FIXED>
 __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
-    __shared__ int lds[192];
+    __shared__ int lds[256];
     const int m = blockIdx.z;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
@@ -183,6 +193,8 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
     const int64_t i0 = __builtin_amdgcn_readfirstlane((int)cb.i0);
     const int64_t pad = __builtin_amdgcn_readfirstlane((int)cb.pad_rows);
     const int64_t pbase = __builtin_amdgcn_readfirstlane((int)cb.pbase);
+    const int64_t pad64 = __builtin_amdgcn_readfirstlane((int)cb.pad64);
+    const int64_t pbase64 = __builtin_amdgcn_readfirstlane((int)cb.pbase64);
     const int64_t cols = a.cols;
     const int64_t c0 = (int64_t)blockIdx.x * 512 + lane * 8;
     // lanes stay in pairs (the columnwise stores need both); rowwise, cols is
@@ -203,7 +215,13 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
     if constexpr (FIXED) Sfix = mx_scale_byte(a.amax[m]);
 
     if constexpr (ROWS) {
+        // public layout: row r0 + j at (r0 + j) * cols; row-pair layout: row
+        // pbase + i0 + j (its expert-padded position), 8 bytes per lane
+        // within one 64-byte half line
+        const int64_t ps = p2_stride(cols);
+        const int64_t rq = pbase + i0;
         uint8_t* rc = (uint8_t*)a.rcodes.p[m] + r0 * cols + c0;
+        uint8_t* rcp = (uint8_t*)a.rcodes.p[m] + (rq >> 1) * ps + (c0 >> 6) * 128 + (c0 & 63);
         const int64_t kb = c0 >> 5;
         const int s = lane & 3;
         uint32_t sp[2] = {0u, 0u};   // block-major: scale bytes of rows 8s .. 8s+7
@@ -225,8 +243,11 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
                                   hi_bf16(v[j][1]), S);
                 o[1] = mx_encode4(lo_bf16(v[j][2]), hi_bf16(v[j][2]), lo_bf16(v[j][3]),
                                   hi_bf16(v[j][3]), S);
-                // whole 512-byte runs per instruction: streamed past L2
-                __builtin_nontemporal_store(o, (u32x2*)(rc + j * cols));
+                if (a.p2) {   // rq is even: row j is half j & 1 of pair (rq + j) / 2
+                    *(u32x2*)(rcp + (j >> 1) * ps + (j & 1) * 64) = o;
+                } else {      // whole 512-byte runs per instruction: streamed past L2
+                    __builtin_nontemporal_store(o, (u32x2*)(rc + j * cols));
+                }
                 if (a.rscales_t) {
                     if ((j >> 3) == s) sp[(j >> 2) & 1] |= S << (8 * (j & 3));
                 } else if (s == 0) {
@@ -237,7 +258,8 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
         if (a.rscales_t) {
             // [cols/32][rows]: this block's 32 rows of column block kb are
             // contiguous; lane s of the quad stores rows 8s .. 8s+7
-            uint8_t* rs = (uint8_t*)a.rscales.p[m] + kb * a.rows + r0 + 8 * s;
+            uint8_t* rs = (uint8_t*)a.rscales.p[m] +
+                          (a.p2 ? kb * a.rows_pad + rq : kb * a.rows + r0) + 8 * s;
             const int nv = min(8, valid - 8 * s);
             if (nv == 8 && ((uintptr_t)rs & 7u) == 0) {
                 *(u32x2*)rs = (u32x2){sp[0], sp[1]};
@@ -260,9 +282,17 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
         for (int j = 0; j < kMxBlock; ++j)
 #pragma unroll
             for (int w = 0; w < 4; ++w) mw[w] = pk_max_u16(mw[w], abs2(v[j][w]));
-        // group g stored as [cols, P_g] at cols * P_0..g-1; rows past the
-        // group's end were loaded as zeros and encode to 0x00
+        // group g stored as [cols, P_g] at cols * P_0..g-1 (public layout) or
+        // in the row-pair layout of [cols, 64-padded rows] at cols * the sum
+        // of the earlier groups' 64-padded sizes; rows past the group's end
+        // were loaded as zeros and encode to 0x00.  colrun(c, i) is where
+        // column c's codes of group rows i .. i + 31 start (32 contiguous bytes).
         uint8_t* cc = (uint8_t*)a.ccodes.p[m] + pbase * cols + i0;
+        uint8_t* ccp = (uint8_t*)a.ccodes.p[m] + pbase64 * cols;
+        const int64_t cps = 2 * pad64;
+        auto colrun = [&](int64_t c, int64_t i) -> uint8_t* {
+            return a.p2 ? ccp + p2_off(c, i, cps) : cc + c * pad + (i - i0);
+        };
         // staged: 256 column lines of 128 bytes (rows i0 - 32 wv .. + 127),
         // half the workgroup's columns at a time.  Line li (lane li / 4,
         // column t = li % 4 of the half) sits at slot li ^ bit 5 of li, its
@@ -306,17 +336,22 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
                 for (int d = 0; d < 4; ++d)
                     recv[d] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send[d], 0xB1, 0xF, 0xF, true);
                 const int64_t ce = (c0 & ~(int64_t)15) + t;   // the even lane's column
-                *(u32x4*)(cc + ce * pad + (odd ? 16 : 0)) = odd ? recv : o[0];
+                *(u32x4*)(colrun(ce, i0) + (odd ? 16 : 0)) = odd ? recv : o[0];
                 if ((c0 | 8) < cols)
-                    *(u32x4*)(cc + (ce + 8) * pad + (odd ? 16 : 0)) = odd ? o[1] : recv;
+                    *(u32x4*)(colrun(ce + 8, i0) + (odd ? 16 : 0)) = odd ? o[1] : recv;
             }
             if (staged) {
                 __syncthreads();
-                // eight neighbouring threads store one column's 128 codes:
-                // streamed past L2 when they fill one line, else plain stores
-                // (a run across two lines shares each with another workgroup)
+                // eight neighbouring threads store one column's 128 codes
+                // (piece p: rows i0b + 16p .. + 15): streamed past L2 when the
+                // instruction fills whole lines, else plain stores (a run
+                // across two lines shares each with another workgroup).  In
+                // the row-pair layout the pieces of columns 2c and 2c+1 from
+                // a 64-row boundary fill two lines.
+                const int64_t i0b = i0 - 32 * wv;
                 uint8_t* cw = cc - 32 * wv;
-                const bool whole = (pad & 127) == 0 && ((uintptr_t)cw & 127) == 0;
+                const bool whole = a.p2 ? (i0b & 63) == 0
+                                        : (pad & 127) == 0 && ((uintptr_t)cw & 127) == 0;
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const int ch = k * 256 + (int)threadIdx.x;
@@ -324,7 +359,8 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
                     const int slot = li ^ ((li >> 5) & 1);
                     const u32x4 val = stage[slot * 8 + (piece ^ ((li >> 2) & 7))];
                     const int64_t col = (int64_t)blockIdx.x * 512 + 8 * (li >> 2) + (li & 3) + 4 * h;
-                    u32x4* dst = (u32x4*)(cw + col * pad + 16 * piece);
+                    u32x4* dst = (u32x4*)(a.p2 ? ccp + p2_off(col, i0b + 16 * piece, cps)
+                                               : cw + col * pad + 16 * piece);
                     if (whole) __builtin_nontemporal_store(val, dst);
                     else *dst = val;
                 }
@@ -350,7 +386,7 @@ __global__ __launch_bounds__(256) void dequant_cols_kernel(const uint8_t* __rest
                                                            int ngroups, int64_t rows,
                                                            int64_t cols,
                                                            bf16_t* __restrict__ out) {
-    __shared__ int lds[192];
+    __shared__ int lds[256];
     ColBlock cb = locate_col_block(sizes, ngroups, rows, blockIdx.y, lds);
     if (cb.valid <= 0) return;
     const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
@@ -468,7 +504,7 @@ hipError_t launch_quant(const MatTable& src, int nmat, const int32_t* sizes, int
                         int64_t rows, int64_t cols, const MatTable* rcodes,
                         const MatTable* rscales, bool rscales_t, const MatTable* ccodes,
                         const MatTable* cscales, bool cscales_t, hipStream_t s,
-                        const char* name, const float* fixed_amax) {
+                        const char* name, const float* fixed_amax, int64_t p2_rows_pad) {
     if (rows == 0 || cols == 0 || nmat == 0 || (!rcodes && !ccodes)) return hipSuccess;
     QuantTileArgs a{};
     a.src = src;
@@ -481,6 +517,8 @@ hipError_t launch_quant(const MatTable& src, int nmat, const int32_t* sizes, int
     a.rscales_t = rscales_t ? 1 : 0;
     a.cscales_t = cscales_t ? 1 : 0;
     a.amax = fixed_amax;
+    a.p2 = p2_rows_pad > 0 ? 1 : 0;
+    a.rows_pad = p2_rows_pad;
     const int64_t nblk = colwise_block_bound(rows, a.ngroups);
     dim3 grid((unsigned)((cols + 511) / 512), (unsigned)((nblk + 3) / 4), (unsigned)nmat);
     TraceScope ts(name, s);
@@ -498,16 +536,17 @@ hipError_t launch_quant(const MatTable& src, int nmat, const int32_t* sizes, int
 
 hipError_t launch_quant_rows(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, int64_t rows, int64_t cols, hipStream_t s,
-                             const char* name, bool scales_t) {
+                             const char* name, bool scales_t, int64_t p2_rows_pad) {
     return launch_quant(src, nmat, nullptr, 1, rows, cols, &codes, &scales, scales_t, nullptr,
-                        nullptr, false, s, name);
+                        nullptr, false, s, name, nullptr, p2_rows_pad);
 }
 
 hipError_t launch_quant_cols(const MatTable& src, const MatTable& codes, const MatTable& scales,
                              int nmat, const int32_t* sizes, int ngroups, int64_t rows,
-                             int64_t cols, hipStream_t s, const char* name, bool scales_t) {
+                             int64_t cols, hipStream_t s, const char* name, bool scales_t,
+                             int64_t p2_rows_pad) {
     return launch_quant(src, nmat, sizes, ngroups, rows, cols, nullptr, nullptr, false, &codes,
-                        &scales, scales_t, s, name);
+                        &scales, scales_t, s, name, nullptr, p2_rows_pad);
 }
 
 hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,

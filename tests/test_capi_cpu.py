@@ -143,7 +143,8 @@ def test_workspace_regions(L):
         for (o1, n1), (o2, _) in zip(spans, spans[1:]):
             assert o1 + n1 <= o2
         assert spans[-1][0] + spans[-1][1] <= total
-    assert moe.workspace_region(moe.MOE_OP_MLP_FWD, "xp_codes", rows, H, I, E, 1)[1] == rows * H
+    rp = (rows // 32 + E) * 32          # expert-padded rows
+    assert moe.workspace_region(moe.MOE_OP_MLP_FWD, "xp_codes", rows, H, I, E, 1)[1] == rp * H
     assert moe.workspace_region(moe.MOE_OP_MLP_FWD, "w1_scales", rows, H, I, E, 1)[1] == \
         E * 2 * I * H // 32
     off, n = ctypes.c_size_t(), ctypes.c_size_t()
@@ -151,6 +152,18 @@ def test_workspace_regions(L):
     assert L.moe_workspace_region(1, 0, rows, H, I, E, 0, ctypes.byref(off), ctypes.byref(n)) == 7
     assert L.moe_workspace_region(2, 0, rows, H, I, E, 1, ctypes.byref(off), ctypes.byref(n)) == 7
     assert L.moe_workspace_region(1, 0, rows, H, I, E, 1, None, None) == 1
+
+
+def test_saved_bytes(L):
+    rows, H, I, E = 1000, 256, 384, 4
+    f = lambda p, m: int(L.moe_saved_bytes(p, m, rows, H, I, E))   # noqa: E731
+    assert f(0, 0) == rows * 2 * I * 2 and f(0, 1) == rows * I * 2 and f(0, 2) == 0
+    assert f(1, 1) == 0
+    q = 64 * (-(-rows // 64) + E)         # 64-padded group rows, upper bound
+    assert f(1, 2) == I * q and f(1, 4) == H * q
+    assert f(1, 3) == I * 32 * (-(-(rows + 31 * E) // 32)) // 32
+    assert f(1, 6) == E * 2 * I * H and f(1, 9) == E * H * I // 32
+    assert f(1, 10) == 0 and f(7, 0) == 0
 
 
 def test_no_gpu_means_unsupported(L):

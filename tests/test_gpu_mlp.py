@@ -14,6 +14,7 @@ from mxfp8_block_scaled_top_amd.layer import LayerBuffers, layer_step
 from oracle import mlp as omlp
 from oracle import mx as omx
 from oracle import route as oroute
+from tests import layouts as L
 from tests.helpers import need_gpu, np_, rel_frob, say
 
 pytestmark = pytest.mark.gpu
@@ -72,18 +73,20 @@ def _check_fp8_saved(got, ref, inp):
     are the oracle's per-tensor codes transposed, every scale slot the
     tensor's scale byte."""
     r = ref["route"]
-    xc, xs = omx.quantize_tensor(ref["xp"])
-    want = _grouped_layout(xc, r["split_sizes"])
-    assert np.array_equal(np_(got["saved"]["xp_col_codes"])[: want.size], want), "xp codes"
-    assert np.all(np_(got["saved"]["xp_col_scales"])[: want.size // 32] == xs), "xp scale"
     H = inp["x"].shape[1]
     I = inp["w2"][0].shape[1]
-    for name, ws, n in (("w_gate_up", inp["w1"], 2 * I * H), ("w_down", inp["w2"], H * I)):
+    xc, xs = omx.quantize_tensor(ref["xp"])
+    want = _grouped_layout(xc, r["split_sizes"])
+    got_c = L.p2_group_cols(np_(got["saved"]["xp_col_codes"]), r["split_sizes"], H)
+    assert np.array_equal(got_c, want), "xp codes"
+    assert np.all(np_(got["saved"]["xp_col_scales"])[: want.size // 32] == xs), "xp scale"
+    for name, ws, R, C in (("w_gate_up", inp["w1"], H, 2 * I), ("w_down", inp["w2"], I, H)):
         codes = np_(got["saved"][name + "_col_codes"])
         scales = np_(got["saved"][name + "_col_scales"])
+        n = R * C
         for e, W in enumerate(ws):
             c, s = omx.quantize_tensor(W)
-            assert np.array_equal(codes[e * n:(e + 1) * n], c.T.reshape(-1)), (name, e)
+            assert np.array_equal(L.p2_to_matrix(codes[e * n:(e + 1) * n], R, C), c.T), (name, e)
             assert np.all(scales[e * n // 32:(e + 1) * n // 32] == s), (name, e)
 
 
@@ -120,7 +123,8 @@ def _layer_compare(inp, k, precision, tag, fast_quant=False):
         H = inp["x"].shape[1]
         qcg = omx.quantize_cols_grouped_fast if fast_quant else omx.quantize_cols_grouped
         xc, xs = qcg(ref["xp"], r["split_sizes"])
-        assert np.array_equal(np_(got["saved"]["xp_col_codes"])[: xc.size], xc)
+        got_c = L.p2_group_cols(np_(got["saved"]["xp_col_codes"]), r["split_sizes"], H)
+        assert np.array_equal(got_c, xc)
         got_s = np_(got["saved"]["xp_col_scales"])
         assert np.array_equal(_block_major_to_public(got_s, r["split_sizes"], H)[: xs.size], xs)
         # the weights' columnwise copies the forward saved for the backward
@@ -130,7 +134,8 @@ def _layer_compare(inp, k, precision, tag, fast_quant=False):
             codes, scales = np_(got["saved"][name + "_col_codes"]), np_(got["saved"][name + "_col_scales"])
             for e, W in enumerate(ws):
                 oc, os_ = qcg(W, [W.shape[0]])
-                assert np.array_equal(codes[e * n:(e + 1) * n], oc), (name, e)
+                got_w = L.p2_to_matrix(codes[e * n:(e + 1) * n], C, W.shape[0]).reshape(-1)
+                assert np.array_equal(got_w, oc), (name, e)
                 got_s = scales[e * n // 32:(e + 1) * n // 32]
                 assert np.array_equal(_block_major_to_public(got_s, [W.shape[0]], C), os_), (name, e)
     return got, ref

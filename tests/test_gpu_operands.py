@@ -36,6 +36,7 @@ import torch
 import mxfp8_block_scaled_top_amd as moe
 from mxfp8_block_scaled_top_amd.layer import LayerBuffers, layer_step
 from oracle import mlp as omlp
+from tests import layouts as L
 from tests.helpers import need_gpu, np_, say
 from tests.mxgrid import grid_matrix, n_tiles
 
@@ -66,38 +67,37 @@ def _region(ws, op, name, rows, H, I, E, prec=moe.MOE_MXFP8):
     return np_(ws[off:off + n])
 
 
-def _rows_public(scales, R, C):
-    """Block-major rowwise scales [C/32][R] -> [R, C/32]."""
-    return scales.reshape(C // 32, R).T
-
-
 def _groups(split):
-    """(expert, first row, rows, padded base) of every expert."""
-    out, r0, p0 = [], 0, 0
+    """(expert, first row, rows) of every expert."""
+    out, r0 = [], 0
     for e, n in enumerate(split):
-        n = int(n)
-        out.append((e, r0, n, p0))
-        r0 += n
-        p0 += (n + 31) // 32 * 32
+        out.append((e, r0, int(n)))
+        r0 += int(n)
     return out
 
 
-def _check_rows(codes, scales, rec, r0, n, C, R_all, what):
-    assert np.array_equal(codes.reshape(-1, C)[r0:r0 + n], rec["codes"]), what + " codes"
-    assert np.array_equal(_rows_public(scales, R_all, C)[r0:r0 + n], rec["scales"]), what + " scales"
+def _check_rows(codes, scales, rec, split, e, C, what):
+    """Rowwise activation operand (expert-padded rows, row-pair layout)."""
+    r0 = int(np.sum(split[:e]))
+    n = int(split[e])
+    assert np.array_equal(L.p2_expert_rows(codes, split, C)[r0:r0 + n], rec["codes"]), what + " codes"
+    assert np.array_equal(L.expert_rows_scales(scales, split, C)[r0:r0 + n], rec["scales"]), \
+        what + " scales"
 
 
 def _check_weight(codes, scales, rec, e, R, C, what):
-    """Per-expert matrices [R, C] (codes) with block-major scales [C/32][R]."""
+    """Per-expert [R, C] row-pair matrices with block-major scales [C/32][R]."""
     n = R * C
-    assert np.array_equal(codes[e * n:(e + 1) * n].reshape(R, C), rec["codes"]), what + " codes"
+    assert np.array_equal(L.p2_to_matrix(codes[e * n:(e + 1) * n], R, C), rec["codes"]), \
+        what + " codes"
     s = scales[e * n // 32:(e + 1) * n // 32].reshape(C // 32, R).T
     assert np.array_equal(s, rec["scales"]), what + " scales"
 
 
-def _check_group_cols(codes, scales, rec, p0, n, C, what):
-    P = (n + 31) // 32 * 32
-    assert np.array_equal(codes[C * p0:C * (p0 + P)], rec["codes"]), what + " codes"
+def _check_group_cols(codes, scales, rec, split, e, C, what):
+    assert np.array_equal(L.p2_group_cols_one(codes, split, C, e), rec["codes"]), what + " codes"
+    p0 = sum((int(n) + 31) // 32 * 32 for n in split[:e])
+    P = (int(split[e]) + 31) // 32 * 32
     s = scales[C * p0 // 32:C * (p0 + P) // 32].reshape(P // 32, C).T.reshape(-1)
     assert np.array_equal(s, rec["scales"]), what + " scales"
 
@@ -129,13 +129,18 @@ def compare_layer_operands(got_bufs, ops, split, H, I, E, weights=True, experts=
     w1c, w1cs = np_(sv["w_gate_up_col_codes"]), np_(sv["w_gate_up_col_scales"])
     w2c, w2cs = np_(sv["w_down_col_codes"]), np_(sv["w_down_col_scales"])
     agree = {}
-    for e, r0, n, p0 in _groups(split):
+    split = [int(n) for n in split]
+    a2rows = L.p2_expert_rows(a2q, split, I) if computed else None
+    a2rs = L.expert_rows_scales(a2s, split, I) if computed else None
+    da1rows = L.p2_expert_rows(da1q, split, 2 * I) if computed else None
+    da1rs = L.expert_rows_scales(da1s, split, 2 * I) if computed else None
+    for e, r0, n in _groups(split):
         if n == 0 or (experts is not None and e not in experts):
             continue
-        _check_rows(xq, xs, ops[("gate_up", "a", e)], r0, n, H, rows, f"xp rows e{e}")
-        _check_rows(dq, ds, ops[("down_dgrad", "a", e)], r0, n, H, rows, f"dyp rows e{e}")
-        _check_group_cols(dc, dcs, ops[("down_wgrad", "a", e)], p0, n, H, f"dyp cols e{e}")
-        _check_group_cols(xc, xcs, ops[("gate_up_wgrad", "b", e)], p0, n, H, f"xp cols e{e}")
+        _check_rows(xq, xs, ops[("gate_up", "a", e)], split, e, H, f"xp rows e{e}")
+        _check_rows(dq, ds, ops[("down_dgrad", "a", e)], split, e, H, f"dyp rows e{e}")
+        _check_group_cols(dc, dcs, ops[("down_wgrad", "a", e)], split, e, H, f"dyp cols e{e}")
+        _check_group_cols(xc, xcs, ops[("gate_up_wgrad", "b", e)], split, e, H, f"xp cols e{e}")
         if weights:
             _check_weight(w1q, w1s, ops[("gate_up", "b", e)], e, 2 * I, H, f"W1 rows e{e}")
             _check_weight(w2q, w2s, ops[("down", "b", e)], e, H, I, f"W2 rows e{e}")
@@ -143,18 +148,14 @@ def compare_layer_operands(got_bufs, ops, split, H, I, E, weights=True, experts=
             _check_weight(w2c, w2cs, ops[("down_dgrad", "b", e)], e, I, H, f"W2 cols e{e}")
         if computed:
             ra = ops[("down", "a", e)]
-            agree.setdefault("a2_codes", []).append(
-                _agree(a2q.reshape(-1, I)[r0:r0 + n], ra["codes"]))
-            agree.setdefault("a2_scales", []).append(
-                _agree(_rows_public(a2s, rows, I)[r0:r0 + n], ra["scales"]))
+            agree.setdefault("a2_codes", []).append(_agree(a2rows[r0:r0 + n], ra["codes"]))
+            agree.setdefault("a2_scales", []).append(_agree(a2rs[r0:r0 + n], ra["scales"]))
             rd = ops[("gate_up_dgrad", "a", e)]
-            agree.setdefault("da1_codes", []).append(
-                _agree(da1q.reshape(-1, 2 * I)[r0:r0 + n], rd["codes"]))
-            agree.setdefault("da1_scales", []).append(
-                _agree(_rows_public(da1s, rows, 2 * I)[r0:r0 + n], rd["scales"]))
+            agree.setdefault("da1_codes", []).append(_agree(da1rows[r0:r0 + n], rd["codes"]))
+            agree.setdefault("da1_scales", []).append(_agree(da1rs[r0:r0 + n], rd["scales"]))
             rc = ops[("down_wgrad", "b", e)]
-            P = (n + 31) // 32 * 32
-            agree.setdefault("a2_col_codes", []).append(_agree(a2c[I * p0:I * (p0 + P)], rc["codes"]))
+            agree.setdefault("a2_col_codes", []).append(
+                _agree(L.p2_group_cols_one(a2c, split, I, e), rc["codes"]))
     return {k: min(v) for k, v in agree.items()}
 
 
