@@ -383,9 +383,12 @@ size_t moe_saved_bytes(int precision, int member, int64_t rows, int H, int I, in
  * precision    MOE_BF16, MOE_MXFP8 or MOE_FP8.
  * E            experts, 1..64.   H, I: hidden and intermediate sizes,
  *              multiples of 128.
- * rows         T*k, 0 <= rows <= INT32_MAX, with rows * max(H, 2I) * 2 and
- *              2I * H * 2 below 2^31 (the kernels address each operand with
- *              31-bit byte offsets); otherwise MOE_ERR_SHAPE.
+ * rows         T*k, 0 <= rows <= INT32_MAX, with 2I * H * 2 (one expert's
+ *              bf16 weight) and max(H, 2I)/32 * 32*(ceil(rows/32) + E) (the
+ *              block-major scales of the widest 8-bit activation operand)
+ *              below 2^31: rows up to about 2.4 million at the Mixtral shape
+ *              (the kernels take every other offset from per-tile or per-step
+ *              bases); otherwise MOE_ERR_SHAPE.
  * xp           bf16 [rows, H], expert-grouped (moe_permute).
  * split_sizes  int32 [E] device, sum = rows.
  * w_gate_up    HOST array of E device pointers, each bf16 [2I, H] (rows
@@ -496,8 +499,8 @@ int moe_workspace_region(int op, int region, int64_t rows, int H, int I, int E, 
  *
  * precision    MOE_BF16 or MOE_MXFP8 (x and W quantized along K first).
  * E            experts, 1..64.   N: out_features, K: in_features, both
- *              multiples of 32, with rows * max(N, K) * 2 and N * K * 2 below
- *              2^31 (otherwise MOE_ERR_SHAPE).
+ *              multiples of 32, with N * K * 2 and max(N, K)/32 *
+ *              32*(ceil(rows/32) + E) below 2^31 (otherwise MOE_ERR_SHAPE).
  * rows         total rows (sum of split_sizes), 0 <= rows <= INT32_MAX.
  * x            bf16 [rows, K], expert-grouped.   split_sizes: int32 [E] device.
  * w            HOST array of E device pointers, each bf16 [N, K].

@@ -99,10 +99,12 @@ int check_linear(int precision, int E, int N, int K, int64_t rows) {
     if (E < 1 || E > kMaxExperts) return MOE_ERR_SHAPE;
     if (N < 32 || K < 32 || (N % 32) || (K % 32)) return MOE_ERR_SHAPE;
     if (rows < 0 || rows > INT32_MAX) return MOE_ERR_SHAPE;
-    // the GEMM kernels address each operand with 31-bit byte offsets
+    // offsets that span a whole tensor stay below 2^31: inside one bf16
+    // weight, and inside the block-major scales of the 8-bit row operands
     const int64_t kMaxSpan = (int64_t)1 << 31;
     const int64_t widest = N > K ? N : K;
-    if (rows * widest * 2 >= kMaxSpan || (int64_t)N * K * 2 >= kMaxSpan) return MOE_ERR_SHAPE;
+    if ((int64_t)N * K * 2 >= kMaxSpan) return MOE_ERR_SHAPE;
+    if (widest / 32 * padded_rows(rows, E) >= kMaxSpan) return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 

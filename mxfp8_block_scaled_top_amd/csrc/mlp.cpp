@@ -173,12 +173,15 @@ int check_common(int precision, int E, int H, int I, int64_t rows) {
     if (E < 1 || E > kMaxExperts) return MOE_ERR_SHAPE;
     if (H < 128 || I < 128 || (H % 128) || (I % 128)) return MOE_ERR_SHAPE;
     if (rows < 0 || rows > INT32_MAX) return MOE_ERR_SHAPE;
-    // the GEMM kernels address every operand with 32-bit byte offsets below
-    // 2^31 from its base: bf16 activations [rows, max(H, 2I)] and one expert's
-    // bf16 weight [2I, H]
+    // The GEMM kernels take their operands' buffer bases per tile (activations)
+    // or per K step (M/N-contiguous operands), so only two offsets still span a
+    // whole tensor and must stay below 2^31: inside one expert's bf16 weight
+    // [2I, H], and inside the block-major scales of the widest 8-bit
+    // activation operand, [max(H, 2I)/32][padded rows].
     const int64_t kMaxSpan = (int64_t)1 << 31;
     const int64_t widest = H > 2 * (int64_t)I ? H : 2 * (int64_t)I;
-    if (rows * widest * 2 >= kMaxSpan || 2 * (int64_t)I * H * 2 >= kMaxSpan) return MOE_ERR_SHAPE;
+    if (2 * (int64_t)I * H * 2 >= kMaxSpan) return MOE_ERR_SHAPE;
+    if (widest / 32 * padded_rows(rows, E) >= kMaxSpan) return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 

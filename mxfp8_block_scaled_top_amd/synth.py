@@ -20,6 +20,7 @@ Mixtral-8x7B training layer; no dataset or trained weight is used):
 * ``mixtral``   T=8192, H=4096, I=14336, E=8,  k=2  (BF16 or MXFP8)
 * ``skewed``    T=16384, H=2048, I=1408, E=64, k=8 with a Zipf(1.2) expert
                 bias on the router logits (ragged split sizes, empty experts)
+* ``mixtral_long`` the Mixtral shape with T=32768 (a long batch)
 """
 from __future__ import annotations
 
@@ -64,6 +65,10 @@ SHAPES = {
     "mixtral_mx": MoEShape("mixtral_mx", T=8192, H=4096, I=14336, E=8, k=2, precision="mxfp8"),
     "skewed": MoEShape("skewed", T=16384, H=2048, I=1408, E=64, k=8, zipf_s=1.2,
                        precision="mxfp8"),
+    # a long batch at the Mixtral shape: 65,536 routed rows (rows x 2I x 2
+    # bytes of one activation tensor is above 2^31)
+    "mixtral_long": MoEShape("mixtral_long", T=32768, H=4096, I=14336, E=8, k=2,
+                             precision="mxfp8"),
 }
 
 

@@ -124,8 +124,10 @@ def test_grouped_linear_validation(L):
     assert L.grouped_linear_fwd(0, 2, 96, 64, 8, p, p, None, p, p, big, None) == N
     assert L.grouped_linear_fwd(0, 2, 96, 64, 8, mis, p, tab, p, p, big, None) == ALIGN
     assert L.grouped_linear_fwd(1, 2, 96, 64, 8, p, p, tab, p, p, 16, None) == WS
-    # 31-bit operand offsets: rows * max(N, K) * 2 must stay below 2^31
-    assert L.grouped_linear_fwd(0, 2, 1 << 15, 64, 1 << 15, p, p, tab, p, p, big, None) == SHAPE
+    # offsets spanning a whole tensor stay below 2^31: one bf16 weight, and the
+    # block-major scales of the widest row operand (max(N, K)/32 * padded rows)
+    assert L.grouped_linear_fwd(0, 2, 1 << 15, 1 << 15, 8, p, p, tab, p, p, big, None) == SHAPE
+    assert L.grouped_linear_fwd(0, 2, 1 << 14, 64, 1 << 22, p, p, tab, p, p, big, None) == SHAPE
     assert L.grouped_linear_bwd(0, 2, 96, 64, 8, p, p, p, None, p, None, p, big, None) == N
     assert L.grouped_linear_bwd(0, 2, 96, 64, 8, p, p, p, tab, p, tab, p, 16, None) == WS \
         or moe.moe_workspace_bytes(moe.MOE_OP_LINEAR_BWD, 8, 64, 96, 2, 1, 0) <= 16
@@ -152,6 +154,21 @@ def test_workspace_regions(L):
     assert L.moe_workspace_region(1, 0, rows, H, I, E, 0, ctypes.byref(off), ctypes.byref(n)) == 7
     assert L.moe_workspace_region(2, 0, rows, H, I, E, 1, ctypes.byref(off), ctypes.byref(n)) == 7
     assert L.moe_workspace_region(1, 0, rows, H, I, E, 1, None, None) == 1
+
+
+def test_batch_limit_is_the_scale_span(L):
+    """rows * max(H, 2I) * 2 >= 2^31 is accepted at the Mixtral shape (the
+    tensors are addressed from per-tile bases); the scale span still bounds
+    the batch (about 2.4 million rows)."""
+    SHAPE, WS = 2, 4
+    p = ctypes.c_void_p(4096)
+    saved = moe._Saved(4096, 4096, 4096, 4096, 4096, 4096)
+    tab = (ctypes.c_void_p * 8)(*([4096] * 8))
+    # 65536 rows (T = 32768, k = 2): past the workspace check means the shape passed
+    assert L.grouped_mlp_fwd(1, 8, 4096, 14336, 65536, p, p, tab, tab, p, p,
+                             ctypes.byref(saved), p, 16, None) == WS
+    assert L.grouped_mlp_fwd(1, 8, 4096, 14336, 3 << 20, p, p, tab, tab, p, p,
+                             ctypes.byref(saved), p, 16, None) == SHAPE
 
 
 def test_saved_bytes(L):

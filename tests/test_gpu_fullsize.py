@@ -38,17 +38,19 @@ def _gpu():
     need_gpu()
 
 
-def _pick_experts(split):
+def _pick_experts(split, largest_only=False):
     split = np.asarray(split)
     live = np.nonzero(split)[0]
-    chosen = {int(live[np.argmax(split[live])]), int(live[np.argmin(split[live])])}
+    chosen = {int(live[np.argmax(split[live])])}
+    if not largest_only:
+        chosen.add(int(live[np.argmin(split[live])]))
     empty = np.nonzero(split == 0)[0]
     if len(empty):
         chosen.add(int(empty[0]))
     return sorted(chosen)
 
 
-def _full_size(shape_name, precision):
+def _full_size(shape_name, precision, largest_only=False):
     sh = synth.SHAPES[shape_name]
     say(f"full-size {shape_name} {precision}: T={sh.T} H={sh.H} I={sh.I} E={sh.E} k={sh.k}")
     inp = synth.layer_inputs(sh)
@@ -61,7 +63,7 @@ def _full_size(shape_name, precision):
     say("  GPU step done; oracle on the chosen experts ...")
 
     r_split = np_(got["route"]["split_sizes"])
-    experts = _pick_experts(r_split)
+    experts = _pick_experts(r_split, largest_only)
     mx = precision == "mxfp8"
     ref = omlp.layer_step(inp["logits"], inp["x"], inp["w1"], inp["w2"], inp["dy"], sh.k,
                           precision, experts=set(experts), fast_quant=True, keep_operands=mx)
@@ -119,6 +121,13 @@ def test_mixtral_layer_full_size(precision):
 
 def test_skewed_layer_full_size_mxfp8():
     _full_size("skewed", "mxfp8")
+
+
+def test_mixtral_long_batch_mxfp8():
+    """T = 32768 at the Mixtral shape: 65,536 routed rows, so one activation
+    tensor (rows x 2I bf16) spans more than 2^31 bytes; the largest expert
+    (over 8,000 rows) against the oracle, operands byte for byte."""
+    _full_size("mixtral_long", "mxfp8", largest_only=True)
 
 
 def test_mixtral_layer_full_size_fp8():
