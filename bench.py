@@ -73,58 +73,10 @@ def log(args, *a):
 
 
 def kernel_work(name: str, T: int, H: int, I: int, E: int, k: int):
-    """(algorithmic FLOPs, algorithmic HBM bytes) of one launch of a kernel."""
-    A = T * k
-    mx = 1 + 1 / 32      # bytes per element of an MXFP8 tensor (codes + scales)
-    table = {
-        "gemm_mx_gateup_fwd_swiglu": (2 * A * 2 * I * H, 0),
-        "gemm_bf16_gateup_fwd_swiglu": (2 * A * 2 * I * H, 0),
-        "gemm_mx_down_fwd": (2 * A * H * I, 0),
-        "gemm_bf16_down_fwd": (2 * A * H * I, 0),
-        "gemm_mx_down_dgrad_swiglu_bwd": (2 * A * I * H, 0),
-        "gemm_bf16_down_dgrad_swiglu_bwd": (2 * A * I * H, 0),
-        "gemm_mx_down_wgrad": (2 * H * I * A, 0),
-        "gemm_bf16_down_wgrad": (2 * H * I * A, 0),
-        "gemm_mx_gateup_dgrad": (2 * A * 2 * I * H, 0),
-        "gemm_bf16_gateup_dgrad": (2 * A * 2 * I * H, 0),
-        "gemm_mx_gateup_wgrad": (2 * 2 * I * H * A, 0),
-        "gemm_fp8_gateup_fwd_swiglu": (2 * A * 2 * I * H, 0),
-        "gemm_fp8_down_fwd": (2 * A * H * I, 0),
-        "gemm_fp8_down_dgrad_swiglu_bwd": (2 * A * I * H, 0),
-        "gemm_fp8_down_wgrad": (2 * H * I * A, 0),
-        "gemm_fp8_gateup_dgrad": (2 * A * 2 * I * H, 0),
-        "gemm_fp8_gateup_wgrad": (2 * 2 * I * H * A, 0),
-        "gemm_bf16_gateup_wgrad": (2 * 2 * I * H * A, 0),
-        "route_topk": (0, T * E * 4 + A * 12),
-        "route_scan": (0, 0),
-        "route_scatter": (0, A * 16),
-        "route_bwd": (0, A * 16 + T * E * 4),
-        "permute": (0, T * H * 2 + A * H * 2 + A * 8),
-        "unpermute": (0, A * H * 2 + T * H * 2),
-        # both orientations from one read: 2 B in, twice 1 + 1/32 B out
-        "mx_quant_xp": (0, A * H * (2 + 2 * mx)),
-        "mx_quant_dyp": (0, A * H * (2 + 2 * mx)),
-        "mx_quant_w1": (0, E * 2 * I * H * (2 + 2 * mx)),
-        "mx_quant_w2": (0, E * H * I * (2 + 2 * mx)),
-        # per-tensor FP8: amax passes read the bf16 tensor; casts as the MXFP8 ones
-        "fp8_amax_xp": (0, A * H * 2), "fp8_amax_dyp": (0, A * H * 2),
-        "fp8_amax_w1": (0, E * 2 * I * H * 2), "fp8_amax_w2": (0, E * H * I * 2),
-        "fp8_amax_a2": (0, A * I * 2), "fp8_amax_da1": (0, A * 2 * I * 2),
-        "fp8_quant_xp": (0, A * H * (2 + 2 * mx)), "fp8_quant_dyp": (0, A * H * (2 + 2 * mx)),
-        "fp8_quant_w1": (0, E * 2 * I * H * (2 + 2 * mx)),
-        "fp8_quant_w2": (0, E * H * I * (2 + 2 * mx)),
-        "fp8_quant_a2": (0, A * I * (2 + 2 * mx)), "fp8_quant_da1": (0, A * 2 * I * (2 + 2 * mx)),
-        "mx_quant_rows_xp": (0, A * H * (2 + mx)),
-        "mx_quant_cols_xp": (0, A * H * (2 + mx)),
-        "mx_quant_rows_dyp": (0, A * H * (2 + mx)),
-        "mx_quant_cols_dyp": (0, A * H * (2 + mx)),
-        "mx_quant_rows_w1": (0, E * 2 * I * H * (2 + mx)),
-        "mx_quant_cols_w1": (0, E * 2 * I * H * (2 + mx)),
-        "mx_quant_rows_w2": (0, E * H * I * (2 + mx)),
-        "mx_quant_cols_w2": (0, E * H * I * (2 + mx)),
-        "dprob_reduce": (0, A * ((I + 255) // 256) * 4 + A * 4),
-    }
-    return table.get(name, (0, 0))
+    """(algorithmic FLOPs, algorithmic HBM bytes) of one launch of a kernel
+    (the table lives with the profile summarizer, which uses it too)."""
+    from mxfp8_block_scaled_top_amd import profsum
+    return profsum.kernel_work(name, T, H, I, E, k)
 
 
 def measured_traffic(kernel: str, workload: str):
