@@ -224,6 +224,9 @@ int moe_router_bwd(const float* dlogits, const uint16_t* x, const uint16_t* w_ro
  * topk_prob    fp32 [T, k]    may be NULL (then prob_perm is not written).
  * xp           bf16 [T*k, H]  out: xp[dest_row[t][j]] = x[t].
  * prob_perm    fp32 [T*k]     out (may be NULL): prob_perm[dest_row[t][j]] = topk_prob[t][j].
+ * x and xp may both be NULL: then only prob_perm is written (topk_prob and
+ * prob_perm required), for a consumer that gathers the token rows itself
+ * (grouped_mlp_fwd_gather / grouped_mlp_bwd_gather).
  */
 int moe_permute(const uint16_t* x, int64_t T, int H, int k, const int32_t* dest_row,
                 const float* topk_prob, uint16_t* xp, float* prob_perm, hipStream_t stream);
@@ -406,6 +409,32 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
                     hipStream_t stream);
 
 /*
+ * grouped_mlp_fwd_gather -- grouped_mlp_fwd with the dispatch fused into the
+ * quantization of its input: grouped row r is token row src_token[r] of x,
+ * read by the MXFP8 (FP8) quantizer straight from x, so the bf16 grouped
+ * copy xp is never written or read.
+ * [BioNeMo, "GroupedLinear": the fused path removes the intermediate data
+ *  movement between the permutation and the quantized grouped GEMM;
+ *  AutoModel, "专家并行": tokens are sent to the experts that compute them.]
+ *
+ * Results, saved tensors and workspace contents are bit for bit those of
+ * grouped_mlp_fwd on xp[r] = x[src_token[r]] (FP8: the tensor maximum is
+ * taken over the gathered rows).
+ * precision    MOE_MXFP8 or MOE_FP8 (MOE_BF16: MOE_ERR_ARG; its GEMMs read
+ *              xp itself, from moe_permute).
+ * x            bf16 [T, H] token rows.
+ * src_token    int32 [rows] device, from moe_route; every entry a valid row
+ *              of x (not checked).
+ * Other arguments and the workspace size: as grouped_mlp_fwd.  prob_perm
+ * comes from moe_permute with x = xp = NULL.
+ */
+int grouped_mlp_fwd_gather(int precision, int E, int H, int I, int64_t rows, const uint16_t* x,
+                           const int32_t* src_token, const int32_t* split_sizes,
+                           const uint16_t* const* w_gate_up, const uint16_t* const* w_down,
+                           const float* prob_perm, uint16_t* yp, const moe_saved* saved,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * grouped_mlp_bwd -- backward of grouped_mlp_fwd.
  * [BioNeMo, "MXFP8与融合MLP": the fused forward has a matching fused backward.]
  *
@@ -419,7 +448,9 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
  * dA1 after its bf16 materialization.
  *
  * dyp          bf16 [rows, H] (moe_permute of the upstream gradient).
- * xp, split_sizes, w_gate_up, w_down, prob_perm, saved: as in the forward.
+ * xp           as in the forward; read by BF16 mode only (the 8-bit modes
+ *              take its columnwise copy from saved) and may be NULL there.
+ * split_sizes, w_gate_up, w_down, prob_perm, saved: as in the forward.
  * dxp          bf16 [rows, H] out.
  * dw_gate_up   HOST array of E device pointers, each bf16 [2I, H] out.
  * dw_down      HOST array of E device pointers, each bf16 [H, I] out.
@@ -432,6 +463,25 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
                     const float* prob_perm, const moe_saved* saved, uint16_t* dxp,
                     uint16_t* const* dw_gate_up, uint16_t* const* dw_down, float* dprob_perm,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * grouped_mlp_bwd_gather -- grouped_mlp_bwd with the dispatch of the upstream
+ * gradient fused into its quantization: grouped row r of dY is token row
+ * src_token[r] of dy.  [The same passages as grouped_mlp_fwd_gather.]
+ *
+ * Results are bit for bit those of grouped_mlp_bwd on dyp[r] = dy[src_token[r]].
+ * precision    MOE_MXFP8 or MOE_FP8 (MOE_BF16: MOE_ERR_ARG).
+ * dy           bf16 [T, H] upstream gradient per token.
+ * src_token    int32 [rows] device, from moe_route (not checked).
+ * Other arguments and the workspace size: as grouped_mlp_bwd (no xp).
+ */
+int grouped_mlp_bwd_gather(int precision, int E, int H, int I, int64_t rows, const uint16_t* dy,
+                           const int32_t* src_token, const int32_t* split_sizes,
+                           const uint16_t* const* w_gate_up, const uint16_t* const* w_down,
+                           const float* prob_perm, const moe_saved* saved, uint16_t* dxp,
+                           uint16_t* const* dw_gate_up, uint16_t* const* dw_down,
+                           float* dprob_perm, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /*
  * Workspace bytes for op (MOE_OP_ROUTE: T, E, k used; MLP ops: rows = T*k,

@@ -78,6 +78,10 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(_Saved), P, SZ, P]),
             "grouped_mlp_bwd": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P,
                                       ctypes.POINTER(_Saved), P, P, P, P, P, SZ, P]),
+            "grouped_mlp_fwd_gather": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P, P,
+                                             ctypes.POINTER(_Saved), P, SZ, P]),
+            "grouped_mlp_bwd_gather": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P,
+                                             ctypes.POINTER(_Saved), P, P, P, P, P, SZ, P]),
             "grouped_linear_fwd": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, SZ, P]),
             "grouped_linear_bwd": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P, P, SZ, P]),
             "moe_saved_bytes": (SZ, [I32, I32, I64, I32, I32, I32]),
@@ -248,6 +252,16 @@ def moe_permute(x: torch.Tensor, dest_row: torch.Tensor, topk_prob=None):
     return xp, pp
 
 
+def moe_permute_prob(dest_row: torch.Tensor, topk_prob: torch.Tensor) -> torch.Tensor:
+    """prob_perm [T*k] fp32 alone (moe_permute with x = xp = NULL), for the
+    gathering grouped-MLP calls."""
+    T, k = dest_row.shape
+    pp = torch.empty(T * k, dtype=torch.float32, device=dest_row.device)
+    _check(lib().moe_permute(None, T, 8, k, _ptr(dest_row), _ptr(topk_prob), None, _ptr(pp),
+                             _stream(dest_row.device)), "moe_permute")
+    return pp
+
+
 def moe_unpermute(yp: torch.Tensor, dest_row: torch.Tensor, topk_prob=None) -> torch.Tensor:
     _dev(yp, torch.bfloat16, "yp")
     T, k = dest_row.shape
@@ -337,11 +351,24 @@ def _saved_struct(s: dict) -> _Saved:
     return _Saved(*[_ptr(s.get(n)) for n, _ in _Saved._fields_])
 
 
+def grouped_mlp_fwd_gather(x, src_token, split_sizes, w_gate_up, w_down, prob_perm,
+                           precision=MOE_MXFP8, saved=None, workspace=None):
+    """grouped_mlp_fwd on the grouped rows x[src_token] without materializing
+    them (8-bit precisions).  Returns (yp, saved)."""
+    return grouped_mlp_fwd(x, split_sizes, w_gate_up, w_down, prob_perm, precision, saved,
+                           workspace, src_token=src_token)
+
+
 def grouped_mlp_fwd(xp, split_sizes, w_gate_up, w_down, prob_perm, precision=MOE_BF16,
-                    saved=None, workspace=None):
-    """Returns (yp, saved).  w_gate_up / w_down: lists of E device tensors."""
+                    saved=None, workspace=None, src_token=None):
+    """Returns (yp, saved).  w_gate_up / w_down: lists of E device tensors.
+    With src_token, xp is the token matrix x and grouped row r is
+    x[src_token[r]] (grouped_mlp_fwd_gather)."""
     _dev(xp, torch.bfloat16, "xp")
     rows, H = xp.shape
+    if src_token is not None:
+        _dev(src_token, torch.int32, "src_token")
+        rows = src_token.numel()
     E = len(w_gate_up)
     I = w_down[0].shape[1]
     if saved is None:
@@ -352,18 +379,38 @@ def grouped_mlp_fwd(xp, split_sizes, w_gate_up, w_down, prob_perm, precision=MOE
     yp = torch.empty((rows, H), dtype=torch.bfloat16, device=xp.device)
     w1, w2 = _ptr_array(w_gate_up), _ptr_array(w_down)
     st = _saved_struct(saved)
-    _check(lib().grouped_mlp_fwd(precision, E, H, I, rows, _ptr(xp), _ptr(split_sizes),
-                                 ctypes.cast(w1, ctypes.c_void_p), ctypes.cast(w2, ctypes.c_void_p),
-                                 _ptr(prob_perm), _ptr(yp), ctypes.byref(st), _ptr(workspace),
-                                 workspace.numel(), _stream(xp.device)), "grouped_mlp_fwd")
+    W = (ctypes.cast(w1, ctypes.c_void_p), ctypes.cast(w2, ctypes.c_void_p))
+    if src_token is None:
+        _check(lib().grouped_mlp_fwd(precision, E, H, I, rows, _ptr(xp), _ptr(split_sizes), *W,
+                                     _ptr(prob_perm), _ptr(yp), ctypes.byref(st), _ptr(workspace),
+                                     workspace.numel(), _stream(xp.device)), "grouped_mlp_fwd")
+    else:
+        _check(lib().grouped_mlp_fwd_gather(precision, E, H, I, rows, _ptr(xp), _ptr(src_token),
+                                            _ptr(split_sizes), *W, _ptr(prob_perm), _ptr(yp),
+                                            ctypes.byref(st), _ptr(workspace), workspace.numel(),
+                                            _stream(xp.device)), "grouped_mlp_fwd_gather")
     return yp, saved
 
 
+def grouped_mlp_bwd_gather(dy, src_token, split_sizes, w_gate_up, w_down, prob_perm, saved,
+                           precision=MOE_MXFP8, workspace=None, dw_gate_up=None, dw_down=None):
+    """grouped_mlp_bwd on the grouped rows dy[src_token] without materializing
+    them (8-bit precisions).  Returns (dxp, dw_gate_up, dw_down, dprob_perm)."""
+    return grouped_mlp_bwd(dy, None, split_sizes, w_gate_up, w_down, prob_perm, saved, precision,
+                           workspace, dw_gate_up, dw_down, src_token=src_token)
+
+
 def grouped_mlp_bwd(dyp, xp, split_sizes, w_gate_up, w_down, prob_perm, saved,
-                    precision=MOE_BF16, workspace=None, dw_gate_up=None, dw_down=None):
-    """Returns (dxp, dw_gate_up list, dw_down list, dprob_perm)."""
+                    precision=MOE_BF16, workspace=None, dw_gate_up=None, dw_down=None,
+                    src_token=None):
+    """Returns (dxp, dw_gate_up list, dw_down list, dprob_perm).  With
+    src_token, dyp is the per-token gradient dy and grouped row r is
+    dy[src_token[r]] (grouped_mlp_bwd_gather; xp unused)."""
     _dev(dyp, torch.bfloat16, "dyp")
     rows, H = dyp.shape
+    if src_token is not None:
+        _dev(src_token, torch.int32, "src_token")
+        rows = src_token.numel()
     E = len(w_gate_up)
     I = w_down[0].shape[1]
     dev = dyp.device
@@ -379,12 +426,19 @@ def grouped_mlp_bwd(dyp, xp, split_sizes, w_gate_up, w_down, prob_perm, saved,
     w1, w2 = _ptr_array(w_gate_up), _ptr_array(w_down)
     d1, d2 = _ptr_array(dw_gate_up), _ptr_array(dw_down)
     st = _saved_struct(saved)
-    _check(lib().grouped_mlp_bwd(precision, E, H, I, rows, _ptr(dyp), _ptr(xp), _ptr(split_sizes),
-                                 ctypes.cast(w1, ctypes.c_void_p), ctypes.cast(w2, ctypes.c_void_p),
-                                 _ptr(prob_perm), ctypes.byref(st), _ptr(dxp),
-                                 ctypes.cast(d1, ctypes.c_void_p), ctypes.cast(d2, ctypes.c_void_p),
-                                 _ptr(dpp), _ptr(workspace), workspace.numel(), _stream(dev)),
-           "grouped_mlp_bwd")
+    W = (ctypes.cast(w1, ctypes.c_void_p), ctypes.cast(w2, ctypes.c_void_p))
+    D = (ctypes.cast(d1, ctypes.c_void_p), ctypes.cast(d2, ctypes.c_void_p))
+    if src_token is None:
+        _check(lib().grouped_mlp_bwd(precision, E, H, I, rows, _ptr(dyp), _ptr(xp),
+                                     _ptr(split_sizes), *W, _ptr(prob_perm), ctypes.byref(st),
+                                     _ptr(dxp), *D, _ptr(dpp), _ptr(workspace), workspace.numel(),
+                                     _stream(dev)), "grouped_mlp_bwd")
+    else:
+        _check(lib().grouped_mlp_bwd_gather(precision, E, H, I, rows, _ptr(dyp), _ptr(src_token),
+                                            _ptr(split_sizes), *W, _ptr(prob_perm),
+                                            ctypes.byref(st), _ptr(dxp), *D, _ptr(dpp),
+                                            _ptr(workspace), workspace.numel(), _stream(dev)),
+               "grouped_mlp_bwd_gather")
     return dxp, dw_gate_up, dw_down, dpp
 
 

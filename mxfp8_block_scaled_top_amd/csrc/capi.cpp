@@ -162,7 +162,11 @@ int moe_permute(const uint16_t* x, int64_t T, int H, int k, const int32_t* dest_
                 const float* topk_prob, uint16_t* xp, float* prob_perm, hipStream_t stream) {
     if (T < 0 || H < 8 || (H % 8) || k < 1 || k > kMaxTopK || T * k > INT32_MAX)
         return MOE_ERR_SHAPE;
-    if (T > 0 && (!x || !dest_row || !xp)) return MOE_ERR_NULL;
+    // x and xp both NULL: only the probabilities move (the rows are gathered
+    // by the consumer, grouped_mlp_*_gather)
+    if ((x == nullptr) != (xp == nullptr)) return MOE_ERR_NULL;
+    if (T > 0 && !dest_row) return MOE_ERR_NULL;
+    if (T > 0 && !x && (!topk_prob || !prob_perm)) return MOE_ERR_NULL;
     if (T > 0 && topk_prob && !prob_perm) return MOE_ERR_NULL;
     if (!aligned16(x) || !aligned16(xp)) return MOE_ERR_ALIGN;
     if (!device_ok()) return MOE_ERR_UNSUPPORTED;

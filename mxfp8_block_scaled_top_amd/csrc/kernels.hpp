@@ -64,14 +64,20 @@ hipError_t launch_quant(const MatTable& src, int nmat, const int32_t* sizes, int
                         const MatTable* rscales, bool rscales_t, const MatTable* ccodes,
                         const MatTable* cscales, bool cscales_t, hipStream_t s,
                         const char* name, const float* fixed_amax = nullptr,
-                        int64_t p2_rows_pad = 0);
+                        int64_t p2_rows_pad = 0, const int32_t* gather = nullptr);
 // Per-tensor FP8: fixed_amax (device, one float per matrix) replaces the block
 // maxima, so every block of matrix m gets the scale of amax[m].
+// gather (one matrix only): row r of the quantized matrix is row gather[r] of
+// src, so a permutation of token rows and their quantization are one pass.
 // amax[m] = max |x| over matrix m's n values (n a multiple of 8); ws holds
 // amax_workspace_bytes(nmat) bytes.
 size_t amax_workspace_bytes(int nmat);
 hipError_t launch_amax(const MatTable& src, int nmat, int64_t n, void* ws, float* amax,
                        hipStream_t s, const char* name);
+// amax over the rows of a gathered matrix: rows x cols values, row r being
+// row gather[r] of x (cols a multiple of 8); ws as for launch_amax(.., 1, ..).
+hipError_t launch_amax_gather(const bf16_t* x, const int32_t* gather, int64_t rows, int64_t cols,
+                              void* ws, float* amax, hipStream_t s, const char* name);
 // The final reduction alone, over per-workgroup partials written elsewhere
 // (the FP8 SwiGLU GEMM epilogues): amax[0] = the largest of part[0..nparts).
 hipError_t launch_amax_final(const uint32_t* part, int nparts, float* amax, hipStream_t s,

@@ -283,11 +283,17 @@ size_t moe_saved_bytes(int precision, int member, int64_t rows, int H, int I, in
     return mlp_saved_bytes(precision, member, rows, H, I, E);
 }
 
-int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint16_t* xp,
-                    const int32_t* split_sizes, const uint16_t* const* w_gate_up,
-                    const uint16_t* const* w_down, const float* prob_perm, uint16_t* yp,
-                    const moe_saved* saved, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward of grouped_mlp_fwd (gather == NULL: xp holds the grouped rows)
+// and of grouped_mlp_fwd_gather (grouped row r is row gather[r] of xp; 8-bit
+// modes only, where xp is read only by the quantizer).
+int mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint16_t* xp,
+            const int32_t* gather, const int32_t* split_sizes, const uint16_t* const* w_gate_up,
+            const uint16_t* const* w_down, const float* prob_perm, uint16_t* yp,
+            const moe_saved* saved, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     int st = check_common(precision, E, H, I, rows);
     if (st != MOE_OK) return st;
     if (!split_sizes || !w_gate_up || !w_down || !saved || !workspace) return MOE_ERR_NULL;
@@ -353,10 +359,14 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     sc.p[0] = w.xq_s;
     ccd.p[0] = saved->xp_col_codes;
     csc.p[0] = saved->xp_col_scales;
-    if (fp8) MOE_TRY(launch_amax(src, 1, rows * H, w.amax_ws, w.amax, stream, "fp8_amax_xp"));
+    if (fp8 && gather)
+        MOE_TRY(launch_amax_gather(xp, gather, rows, H, w.amax_ws, w.amax, stream, "fp8_amax_xp"));
+    else if (fp8)
+        MOE_TRY(launch_amax(src, 1, rows * H, w.amax_ws, w.amax, stream, "fp8_amax_xp"));
     const int64_t rpad = padded_rows(rows, E);
     MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, H, &cd, &sc, true, &ccd, &csc, true, stream,
-                         fp8 ? "fp8_quant_xp" : "mx_quant_xp", fp8 ? w.amax : nullptr, rpad));
+                         fp8 ? "fp8_quant_xp" : "mx_quant_xp", fp8 ? w.amax : nullptr, rpad,
+                         gather));
     // weights: rowwise (along H for W1, along I for W2) for these GEMMs; with
     // the saved columnwise buffers, also the backward's copies from the same read
     MatTable w1t{}, w1c{}, w1s{}, w2t{}, w2c{}, w2s{};
@@ -449,12 +459,15 @@ int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint
     return MOE_OK;
 }
 
-int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint16_t* dyp,
-                    const uint16_t* xp, const int32_t* split_sizes,
-                    const uint16_t* const* w_gate_up, const uint16_t* const* w_down,
-                    const float* prob_perm, const moe_saved* saved, uint16_t* dxp,
-                    uint16_t* const* dw_gate_up, uint16_t* const* dw_down, float* dprob_perm,
-                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// The backward of grouped_mlp_bwd (gather == NULL) and grouped_mlp_bwd_gather
+// (grouped row r of dY is row gather[r] of dyp; 8-bit modes only).  xp is
+// read by the BF16 weight gradient only.
+int mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint16_t* dyp,
+            const int32_t* gather, const uint16_t* xp, const int32_t* split_sizes,
+            const uint16_t* const* w_gate_up, const uint16_t* const* w_down,
+            const float* prob_perm, const moe_saved* saved, uint16_t* dxp,
+            uint16_t* const* dw_gate_up, uint16_t* const* dw_down, float* dprob_perm,
+            void* workspace, size_t workspace_bytes, hipStream_t stream) {
     int st = check_common(precision, E, H, I, rows);
     if (st != MOE_OK) return st;
     if (!split_sizes || !w_gate_up || !w_down || !saved || !workspace || !dw_gate_up ||
@@ -463,7 +476,8 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     for (int e = 0; e < E; ++e)
         if (!w_gate_up[e] || !w_down[e] || !dw_gate_up[e] || !dw_down[e]) return MOE_ERR_NULL;
     if (rows > 0) {
-        if (!dyp || !xp || !prob_perm || !dxp || !dprob_perm || !saved->a1) return MOE_ERR_NULL;
+        if (!dyp || !prob_perm || !dxp || !dprob_perm || !saved->a1) return MOE_ERR_NULL;
+        if (precision == MOE_BF16 && !xp) return MOE_ERR_NULL;
         if (precision == MOE_BF16 && !saved->a2) return MOE_ERR_NULL;
         if (precision != MOE_BF16 && (!saved->a2_col_codes || !saved->a2_col_scales ||
                                       !saved->xp_col_codes || !saved->xp_col_scales))
@@ -579,10 +593,14 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
         sc.p[0] = w.dyq_s;
         ccd.p[0] = w.dyc;
         csc.p[0] = w.dyc_s;
-        if (fp8) MOE_TRY(launch_amax(src, 1, rows * H, w.amax_ws, w.amax, stream, "fp8_amax_dyp"));
+        if (fp8 && gather)
+            MOE_TRY(launch_amax_gather(dyp, gather, rows, H, w.amax_ws, w.amax, stream,
+                                       "fp8_amax_dyp"));
+        else if (fp8)
+            MOE_TRY(launch_amax(src, 1, rows * H, w.amax_ws, w.amax, stream, "fp8_amax_dyp"));
         MOE_TRY(launch_quant(src, 1, split_sizes, E, rows, H, &cd, &sc, true, &ccd, &csc, true,
                              stream, fp8 ? "fp8_quant_dyp" : "mx_quant_dyp",
-                             fp8 ? w.amax : nullptr, rpad));
+                             fp8 ? w.amax : nullptr, rpad, gather));
     }
     MatTable w1t{}, w1c{}, w1s{}, w2t{}, w2c{}, w2s{};
     for (int e = 0; e < E; ++e) {
@@ -718,6 +736,55 @@ int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint
     wg1.name = fp8 ? "gemm_fp8_gateup_wgrad" : "gemm_mx_gateup_wgrad";
     MOE_TRY(launch_gemm(dt8, U_GATEUP_WGRAD, wg1, stream));
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int grouped_mlp_fwd(int precision, int E, int H, int I, int64_t rows, const uint16_t* xp,
+                    const int32_t* split_sizes, const uint16_t* const* w_gate_up,
+                    const uint16_t* const* w_down, const float* prob_perm, uint16_t* yp,
+                    const moe_saved* saved, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+    return mlp_fwd(precision, E, H, I, rows, xp, nullptr, split_sizes, w_gate_up, w_down,
+                   prob_perm, yp, saved, workspace, workspace_bytes, stream);
+}
+
+int grouped_mlp_fwd_gather(int precision, int E, int H, int I, int64_t rows, const uint16_t* x,
+                           const int32_t* src_token, const int32_t* split_sizes,
+                           const uint16_t* const* w_gate_up, const uint16_t* const* w_down,
+                           const float* prob_perm, uint16_t* yp, const moe_saved* saved,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (precision == MOE_BF16) return MOE_ERR_ARG;
+    if (rows > 0 && !src_token) return MOE_ERR_NULL;
+    return mlp_fwd(precision, E, H, I, rows, x, src_token, split_sizes, w_gate_up, w_down,
+                   prob_perm, yp, saved, workspace, workspace_bytes, stream);
+}
+
+int grouped_mlp_bwd(int precision, int E, int H, int I, int64_t rows, const uint16_t* dyp,
+                    const uint16_t* xp, const int32_t* split_sizes,
+                    const uint16_t* const* w_gate_up, const uint16_t* const* w_down,
+                    const float* prob_perm, const moe_saved* saved, uint16_t* dxp,
+                    uint16_t* const* dw_gate_up, uint16_t* const* dw_down, float* dprob_perm,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return mlp_bwd(precision, E, H, I, rows, dyp, nullptr, xp, split_sizes, w_gate_up, w_down,
+                   prob_perm, saved, dxp, dw_gate_up, dw_down, dprob_perm, workspace,
+                   workspace_bytes, stream);
+}
+
+int grouped_mlp_bwd_gather(int precision, int E, int H, int I, int64_t rows, const uint16_t* dy,
+                           const int32_t* src_token, const int32_t* split_sizes,
+                           const uint16_t* const* w_gate_up, const uint16_t* const* w_down,
+                           const float* prob_perm, const moe_saved* saved, uint16_t* dxp,
+                           uint16_t* const* dw_gate_up, uint16_t* const* dw_down,
+                           float* dprob_perm, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+    if (precision == MOE_BF16) return MOE_ERR_ARG;
+    if (rows > 0 && !src_token) return MOE_ERR_NULL;
+    return mlp_bwd(precision, E, H, I, rows, dy, src_token, nullptr, split_sizes, w_gate_up,
+                   w_down, prob_perm, saved, dxp, dw_gate_up, dw_down, dprob_perm, workspace,
+                   workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -154,6 +154,7 @@ struct QuantTileArgs {
     int64_t rows_pad;
     const float* amax;          // per-tensor mode: amax of matrix m (one scale for all
                                 // its blocks, still written to every scale slot)
+    const int32_t* gather;      // one matrix: row r is read from source row gather[r]
 };
 
 typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
@@ -202,13 +203,21 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
     if ((c0 & ~(int64_t)15) >= cols) return;
     const bool live = c0 < cols;
 
-    const char* in = (const char*)a.src.p[m] + r0 * cols * 2;
+    // the block's source rows: r0 + j, or the gather table's entries (the
+    // same for the whole wave: scalar loads)
+    const char* in = (const char*)a.src.p[m];
+    int64_t srow[kMxBlock];
+#pragma unroll
+    for (int j = 0; j < kMxBlock; ++j) {
+        srow[j] = r0 + j;
+        if (a.gather && j < valid) srow[j] = a.gather[r0 + j];
+    }
     u32x4 v[kMxBlock];
 #pragma unroll
     for (int j = 0; j < kMxBlock; ++j) {
         v[j] = (u32x4){0u, 0u, 0u, 0u};
         if (j < valid && live)
-            v[j] = __builtin_nontemporal_load((const u32x4*)(in + (j * cols + c0) * 2));
+            v[j] = __builtin_nontemporal_load((const u32x4*)(in + (srow[j] * cols + c0) * 2));
     }
 
     uint32_t Sfix = 0;
@@ -453,6 +462,26 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(MatTable src, int64_t
     if (threadIdx.x == 0) part[(int64_t)m * gridDim.x + blockIdx.x] = am;
 }
 
+// The same partials over the rows of a gathered matrix (row r of it is source
+// row gather[r]): workgroup b takes rows b, b + gridDim.x, ...
+__global__ __launch_bounds__(256) void amax_gather_partial_kernel(const u32x4* __restrict__ x,
+                                                                  const int32_t* __restrict__ gather,
+                                                                  int64_t rows, int64_t cpr,
+                                                                  uint32_t* __restrict__ part) {
+    __shared__ uint32_t red[4];
+    uint32_t mw = 0;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const u32x4* p = x + (int64_t)gather[r] * cpr;
+        for (int64_t c = threadIdx.x; c < cpr; c += 256) {
+            const u32x4 v = __builtin_nontemporal_load(p + c);
+            mw = pk_max_u16(mw, pk_max_u16(pk_max_u16(abs2(v[0]), abs2(v[1])),
+                                           pk_max_u16(abs2(v[2]), abs2(v[3]))));
+        }
+    }
+    const uint32_t am = block_max_u32(max(mw & 0xffffu, mw >> 16), red);
+    if (threadIdx.x == 0) part[blockIdx.x] = am;
+}
+
 __global__ __launch_bounds__(256) void amax_final_kernel(const uint32_t* __restrict__ part,
                                                          int nparts, float* __restrict__ amax) {
     __shared__ uint32_t red[4];
@@ -488,6 +517,19 @@ hipError_t launch_amax(const MatTable& src, int nmat, int64_t n, void* ws, float
     return hipGetLastError();
 }
 
+hipError_t launch_amax_gather(const bf16_t* x, const int32_t* gather, int64_t rows, int64_t cols,
+                              void* ws, float* amax, hipStream_t s, const char* name) {
+    int64_t parts = rows < kAmaxParts ? rows : kAmaxParts;
+    if (parts < 1) parts = 1;
+    TraceScope ts(name, s);
+    amax_gather_partial_kernel<<<(unsigned)parts, 256, 0, s>>>((const u32x4*)x, gather, rows,
+                                                              cols / 8, (uint32_t*)ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    amax_final_kernel<<<1, 256, 0, s>>>((const uint32_t*)ws, (int)parts, amax);
+    return hipGetLastError();
+}
+
 static unsigned grid_1d(int64_t n, int threads) {
     int64_t b = (n + threads - 1) / threads;
     int64_t cap = 256 * 32;
@@ -504,10 +546,13 @@ hipError_t launch_quant(const MatTable& src, int nmat, const int32_t* sizes, int
                         int64_t rows, int64_t cols, const MatTable* rcodes,
                         const MatTable* rscales, bool rscales_t, const MatTable* ccodes,
                         const MatTable* cscales, bool cscales_t, hipStream_t s,
-                        const char* name, const float* fixed_amax, int64_t p2_rows_pad) {
+                        const char* name, const float* fixed_amax, int64_t p2_rows_pad,
+                        const int32_t* gather) {
     if (rows == 0 || cols == 0 || nmat == 0 || (!rcodes && !ccodes)) return hipSuccess;
+    if (gather && nmat != 1) return hipErrorInvalidValue;
     QuantTileArgs a{};
     a.src = src;
+    a.gather = gather;
     if (rcodes) a.rcodes = *rcodes, a.rscales = *rscales;
     if (ccodes) a.ccodes = *ccodes, a.cscales = *cscales;
     a.sizes = sizes;

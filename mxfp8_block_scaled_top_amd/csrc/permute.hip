@@ -36,6 +36,15 @@ __global__ __launch_bounds__(256) void permute_kernel(const u32x4* __restrict__ 
     }
 }
 
+// The probabilities alone (the rows are gathered by their consumer).
+__global__ __launch_bounds__(256) void permute_prob_kernel(int64_t picks,
+                                                           const int32_t* __restrict__ dest_row,
+                                                           const float* __restrict__ topk_prob,
+                                                           float* __restrict__ prob_perm) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < picks) prob_perm[dest_row[i]] = topk_prob[i];
+}
+
 __global__ __launch_bounds__(256) void unpermute_kernel(const u32x4* __restrict__ yp, int T,
                                                         int cpr, int k,
                                                         const int32_t* __restrict__ dest_row,
@@ -80,6 +89,13 @@ hipError_t launch_permute(const bf16_t* x, int T, int H, int k, const int32_t* d
                           hipStream_t s) {
     size_t n = (size_t)T * (H / 8);
     if (n == 0) return hipSuccess;
+    if (!x) {   // probabilities only
+        const int64_t picks = (int64_t)T * k;
+        TraceScope ts("permute_prob", s);
+        permute_prob_kernel<<<(unsigned)((picks + 255) / 256), 256, 0, s>>>(picks, dest_row,
+                                                                            topk_prob, prob_perm);
+        return hipGetLastError();
+    }
     TraceScope ts("permute", s);
     permute_kernel<<<grid_for(n, 256), 256, 0, s>>>((const u32x4*)x, T, H / 8, k, dest_row,
                                                     topk_prob, (u32x4*)xp,

@@ -13,10 +13,10 @@ name bench.py's launch trace uses for it.
 
 traffic: bytes per dispatch of every grouped GEMM and memory-bound kernel
 from two counter passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch).  Each
-counter is scaled by what it reads for the token permute / unpermute of the
-same run, plain copies whose bytes are known exactly: fetch factor =
-unpermute's algorithmic read bytes / its FETCH_SIZE, write factor = permute's
-algorithmic write bytes / its WRITE_SIZE.  (FETCH_SIZE, a derived counter,
+counter is scaled by what it reads for the token unpermute of the same run,
+a plain copy whose bytes are known exactly: fetch factor = its algorithmic
+read bytes / its FETCH_SIZE, write factor = its algorithmic write bytes / its
+WRITE_SIZE.  (FETCH_SIZE, a derived counter,
 counts the L2-to-memory read requests at 64 bytes unless they are flagged as
 128-byte requests; the fetch factor of about 2 says that the reads of this
 chip's 128-byte requests are counted at half their size.)  With the dispatch
@@ -78,8 +78,11 @@ def kernel_work(name: str, T: int, H: int, I: int, E: int, k: int):
         "route_scatter": (0, A * 16),
         "route_bwd": (0, A * 16 + T * E * 4),
         "permute": (0, T * H * 2 + A * H * 2 + A * 8),
+        "permute_prob": (0, A * 12),
         "unpermute": (0, A * H * 2 + T * H * 2),
-        # both orientations from one read: 2 B in, twice 1 + 1/32 B out
+        # both orientations from one read: 2 B in, twice 1 + 1/32 B out (xp and
+        # dyp gather their rows from the token matrices: each token row is read
+        # once per pick, the repeats mostly from the caches)
         "mx_quant_xp": (0, A * H * (2 + 2 * mx)),
         "mx_quant_dyp": (0, A * H * (2 + 2 * mx)),
         "mx_quant_w1": (0, E * 2 * I * H * (2 + 2 * mx)),
@@ -242,12 +245,12 @@ def traffic(args) -> None:
                 return sum(vals) / len(vals)
         raise KeyError(key)
 
-    # copy kernels of known size: unpermute reads A*H*2 (+ dest_row), permute
-    # writes A*H*2 (+ prob_perm)
+    # a copy kernel of known size: unpermute reads A*H*2 (+ dest_row) and
+    # writes T*H*2
     un_read = A * H * 2 + A * 4
-    pe_write = A * H * 2 + A * 4
+    un_write = T * H * 2
     f_fetch = un_read / (pick(fetch, "unpermute_kernel") * 1024)
-    f_write = pe_write / (pick(write, "moe::permute_kernel") * 1024)
+    f_write = un_write / (pick(write, "unpermute_kernel") * 1024)
 
     rows, gemm_tab, mem_tab = {}, [], []
     for (sym, grid), vals in sorted(fetch.items(), key=lambda kv: trace_name(kv[0][0])):
@@ -288,7 +291,7 @@ def traffic(args) -> None:
            "values are KiB per dispatch, averaged over the dispatches of a kernel.", "",
            "Calibration with plain copies of known size from the same runs: "
            f"FETCH_SIZE x {f_fetch:.3f} (unpermute reads {un_read / 1e6:.1f} MB per launch), "
-           f"WRITE_SIZE x {f_write:.3f} (permute writes {pe_write / 1e6:.1f} MB per launch).  "
+           f"WRITE_SIZE x {f_write:.3f} (unpermute writes {un_write / 1e6:.1f} MB per launch).  "
            "FETCH_SIZE counts the L2-to-memory read requests at 64 bytes unless they are "
            "flagged as 128-byte ones; a factor near 2 says that this chip's 128-byte reads "
            "are counted at half their size.  Reads served by the last-level cache count as "

@@ -188,3 +188,31 @@ def test_no_gpu_means_unsupported(L):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert L.moe_device_supported() == 0
+
+
+def test_gather_entry_points_reject_bf16():
+    """The gathering grouped-MLP calls serve the 8-bit precisions only (BF16
+    GEMMs read the grouped rows themselves): MOE_ERR_ARG before any launch."""
+    import ctypes
+    L = moe.lib()
+    z = ctypes.c_void_p(0)
+    st = moe._Saved()
+    assert L.grouped_mlp_fwd_gather(moe.MOE_BF16, 8, 4096, 14336, 16, z, z, z, z, z, z, z,
+                                    ctypes.byref(st), z, 0, z) == 7
+    assert L.grouped_mlp_bwd_gather(moe.MOE_BF16, 8, 4096, 14336, 16, z, z, z, z, z, z,
+                                    ctypes.byref(st), z, z, z, z, z, 0, z) == 7
+    # 8-bit precisions need the index table when there are rows
+    assert L.grouped_mlp_fwd_gather(moe.MOE_MXFP8, 8, 4096, 14336, 16, z, z, z, z, z, z, z,
+                                    ctypes.byref(st), z, 0, z) == 1
+
+
+def test_permute_prob_only_arguments():
+    """moe_permute: x and xp both NULL or both given; the probability-only
+    mode needs topk_prob and prob_perm."""
+    import ctypes
+    L = moe.lib()
+    z = ctypes.c_void_p(0)
+    p = ctypes.c_void_p(4096)
+    assert L.moe_permute(p, 4, 8, 2, p, p, z, p, z) == 1      # x without xp
+    assert L.moe_permute(z, 4, 8, 2, p, z, z, p, z) == 1      # no topk_prob
+    assert L.moe_permute(z, 4, 8, 2, p, p, z, z, z) == 1      # no prob_perm
