@@ -113,6 +113,9 @@ __device__ __forceinline__ void grouped_order(int t, int mt, int nt, int& m, int
 
 // Builds the per-expert prefix tables in LDS and decodes the tile.  Returns
 // false when this workgroup has no tile (uniform over the workgroup).
+// sched: [0, 64) tile prefix, [64, 128) row prefix, [128, 192) rows,
+// [192, 256) and [256, 320) prefixes of the 32- and 64-padded sizes,
+// [320, 384) the weight gradients' expert order.
 template <int GRP>
 __device__ bool decode_tile(const GemmArgs& g, int ntn, int mtm, int t, int* sched, Tile& tl) {
     if (threadIdx.x < 64) {
@@ -124,6 +127,17 @@ __device__ bool decode_tile(const GemmArgs& g, int ntn, int mtm, int t, int* sch
         sched[128 + lane] = n;
         sched[192 + lane] = wave_incl_scan((n + 31) / 32);
         sched[256 + lane] = wave_incl_scan((n + 63) / 64);
+        if (GRP == G_K) {
+            // weight gradients: experts in decreasing order of rows (ties by
+            // index), so the longest tiles start first and the short ones fill
+            // in behind them instead of trailing at the end of the grid
+            int rank = 0;
+            for (int j = 0; j < g.E; ++j) {
+                const int m = __shfl(n, j);
+                rank += (m > n || (m == n && j < lane)) ? 1 : 0;
+            }
+            if (lane < g.E) sched[320 + rank] = lane;
+        }
     }
     __syncthreads();
     int e;
@@ -135,9 +149,10 @@ __device__ bool decode_tile(const GemmArgs& g, int ntn, int mtm, int t, int* sch
         // and only the smaller one is read by all XCDs.
         const int x = blockIdx.x & 7, i = blockIdx.x >> 3, mt8 = mtm >> 3;
         const int per = mt8 * ntn;
-        e = i / per;
-        if (e >= g.E) return false;
-        tloc = i - e * per;
+        const int q = i / per;
+        if (q >= g.E) return false;
+        e = sched[320 + q];
+        tloc = i - q * per;
         int m8;
         grouped_order(tloc, mt8, ntn, m8, tl.n_tile);
         tl.m0 = (m8 * 8 + x) * kGemmBM;
@@ -158,9 +173,10 @@ __device__ bool decode_tile(const GemmArgs& g, int ntn, int mtm, int t, int* sch
             mt = (sched[128 + e] + kGemmBM - 1) / kGemmBM;
         } else {
             const int per = mtm * nt8;
-            e = i / per;
-            if (e >= g.E) return false;
-            tloc = i - e * per;
+            const int q = i / per;
+            if (q >= g.E) return false;
+            e = sched[320 + q];
+            tloc = i - q * per;
             mt = mtm;
         }
         int m, n8;
@@ -178,9 +194,10 @@ __device__ bool decode_tile(const GemmArgs& g, int ntn, int mtm, int t, int* sch
         tl.m0 = m * kGemmBM;
     } else {
         int per = mtm * ntn;
-        e = t / per;
-        if (e >= g.E) return false;
-        tloc = t - e * per;
+        const int q = t / per;
+        if (q >= g.E) return false;
+        e = sched[320 + q];
+        tloc = t - q * per;
         int m;
         grouped_order(tloc, mtm, ntn, m, tl.n_tile);
         tl.m0 = m * kGemmBM;
@@ -809,7 +826,7 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     __shared__ __attribute__((aligned(16))) uint8_t lds3[kStageB];
     __shared__ __attribute__((aligned(16))) uint8_t ssc[kStages][2][2][kGemmBM];   // MXFP8 scales
     __shared__ float red[2 * kGemmBM];                  // probability-gradient row partials
-    __shared__ int sched[320];
+    __shared__ int sched[384];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // uniform
