@@ -29,8 +29,8 @@
 //   * Epilogues: each wave stages its 128 x 128 result through its own LDS
 //     region, 32 rows at a time (last slice first), and syncs only on its
 //     own LDS accesses.  Outputs that a wave owns whole lines of (the plain
-//     stores, the saved A1, bf16 dA1, the backward's MXFP8 row codes) leave
-//     in whole 128-byte lines with streaming stores.
+//     stores, the saved A1, bf16 dA1) leave in whole 128-byte lines with
+//     streaming stores.
 //   * M/N-contiguous bf16 operands (the dgrad weights and both weight-gradient
 //     operands) are staged in LDS in their natural [k][m] order (16-byte
 //     chunks of a 512-byte row XOR-ed with 4*(k&3)) and turned into K-packed
@@ -654,12 +654,17 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
     {
         // phase 1, 8 values at a time: dg replaces the staged dA2 in R, du
         // replaces the staged gate/up pairs in R2 (rows past the expert stay
-        // zero for the column blocks)
+        // zero for the column blocks).  MXFP8: each 32-column block of dg and
+        // of du is also held in registers and quantized rowwise right away,
+        // its 32 codes stored as one 32-byte run of the row-pair layout.
         const bool live = slab && row < valid;
         const float p = live ? c.pr[fi] : 0.f;
+        const int64_t rp = tl.pbase + frow0 + row;           // expert-padded row
+        const int64_t ps = p2_stride(2 * I);
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             const int cb = 64 * h + 32 * blk;
+            float gq[32], uq[32];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 float d[8], pr8[8], dg[8], du[8];
@@ -687,6 +692,24 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
                 }
                 store_row8(R, row, cb + 8 * b, dg);
                 store_row8(R2, row, cb + 8 * b, du);
+                if (DT == DT_MX)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        gq[8 * b + i] = dg[i];
+                        uq[8 * b + i] = du[i];
+                    }
+            }
+            if (DT == DT_MX && live) {
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int64_t j = (s2 ? I : 0) + jw + cb;   // first column of the block
+                    u32x4 c0, c1;
+                    const uint32_t S = quant32(s2 ? uq : gq, c0, c1);
+                    u32x4* o = (u32x4*)(g.q_row + p2_off(rp, j, ps));
+                    o[0] = c0;
+                    o[1] = c1;
+                    g.q_row_s[(j / 32) * g.rows_pad + rp] = (uint8_t)S;
+                }
             }
         }
     }
@@ -720,9 +743,8 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
             }
         }
     } else {
-        // columnwise MXFP8 first (lane = column, its 32 rows; phase 1 staged
-        // zeros for the rows past the expert), while every staged value is
-        // still in place
+        // columnwise MXFP8 (lane = column, its 32 rows; phase 1 staged zeros
+        // for the rows past the expert)
         wave_lds_sync();
         if (slab && valid > 0) {
 #pragma unroll 1
@@ -733,55 +755,6 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
                 col_quant(col < 128 ? R : R2, cc,
                           g.q_col + tl.pbase64 * 2 * I + p2_off(j, frow0, 2 * tl.pad64_e),
                           g.q_col_s + tl.pbase / 32 * 2 * I + (frow0 / 32) * 2 * I + j);
-            }
-        }
-        wave_lds_sync();
-        // rowwise MXFP8 of the lane's own 32-column blocks: the block's 32
-        // code bytes replace its first 8 staged values (the lane has read all
-        // 32 of them)
-        if (slab && row < valid) {
-            const int64_t rp = tl.pbase + frow0 + row;       // expert-padded row
-#pragma unroll 1
-            for (int q = 0; q < 4; ++q) {
-                const int cb = 64 * h + 32 * (q & 1);
-                float* src = q < 2 ? R : R2;
-                float x[32];
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    float y[8];
-                    load_row8(src, row, cb + 8 * b, y);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) x[8 * b + i] = y[i];
-                }
-                u32x4 c0, c1;
-                uint32_t S = quant32(x, c0, c1);
-                *(float4*)(src + st_idx(row, cb)) = __builtin_bit_cast(float4, c0);
-                *(float4*)(src + st_idx(row, cb + 4)) = __builtin_bit_cast(float4, c1);
-                const int64_t j = (q < 2 ? 0 : I) + jw + cb;
-                g.q_row_s[(j / 32) * g.rows_pad + rp] = (uint8_t)S;
-            }
-        }
-        wave_lds_sync();
-        // the row codes in whole 128-byte lines of the row-pair layout (dg
-        // codes of the wave's 128 j, then du's): line (pair p, chunk ch)
-        // holds 64 codes of row 2p, then of row 2p+1; 8 lanes per line (the
-        // row's parity c8/4, 16 codes each), 8 lines per instruction, streamed
-        if (slab) {
-            const int c8 = lane & 7, half = c8 >> 2, piece = c8 & 3;
-            const int64_t ps = p2_stride(2 * I);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int slot = (lane >> 3) + 8 * i;        // (pair, chunk) of 16 x 2
-                const int r = 2 * (slot >> 1) + half, ch = slot & 1;
-                if (r < valid) {
-                    const int bo = 64 * ch + 16 * piece;      // code byte in the wave's 128
-                    const int scol = 32 * (bo >> 5) + 4 * ((bo >> 4) & 1);
-                    const int64_t rp = tl.pbase + frow0 + r;
-                    const u32x4 cg = __builtin_bit_cast(u32x4, *(const float4*)(R + st_idx(r, scol)));
-                    const u32x4 cu = __builtin_bit_cast(u32x4, *(const float4*)(R2 + st_idx(r, scol)));
-                    __builtin_nontemporal_store(cg, (u32x4*)(g.q_row + p2_off(rp, jw + bo, ps)));
-                    __builtin_nontemporal_store(cu, (u32x4*)(g.q_row + p2_off(rp, I + jw + bo, ps)));
-                }
             }
         }
     }
