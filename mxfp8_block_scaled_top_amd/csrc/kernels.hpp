@@ -67,8 +67,9 @@ hipError_t launch_quant(const MatTable& src, int nmat, const int32_t* sizes, int
                         int64_t p2_rows_pad = 0, const int32_t* gather = nullptr);
 // Per-tensor FP8: fixed_amax (device, one float per matrix) replaces the block
 // maxima, so every block of matrix m gets the scale of amax[m].
-// gather (one matrix only): row r of the quantized matrix is row gather[r] of
-// src, so a permutation of token rows and their quantization are one pass.
+// gather (one matrix, both orientations): row r of the quantized matrix is
+// row gather[r] of src, so a permutation of token rows and their
+// quantization are one pass.
 // amax[m] = max |x| over matrix m's n values (n a multiple of 8); ws holds
 // amax_workspace_bytes(nmat) bytes.
 size_t amax_workspace_bytes(int nmat);

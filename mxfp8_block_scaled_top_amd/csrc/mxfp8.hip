@@ -167,7 +167,7 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
 // magnitude bits of the two bf16 halves of w
 __device__ __forceinline__ uint32_t abs2(uint32_t w) { return w & 0x7fff7fffu; }
 
-template <bool ROWS, bool COLS, bool FIXED>
+template <bool ROWS, bool COLS, bool FIXED, bool GATHER>
 __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
     __shared__ int lds[256];
     const int m = blockIdx.z;
@@ -203,21 +203,28 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
     if ((c0 & ~(int64_t)15) >= cols) return;
     const bool live = c0 < cols;
 
-    // the block's source rows: r0 + j, or the gather table's entries (the
-    // same for the whole wave: scalar loads)
-    const char* in = (const char*)a.src.p[m];
-    int64_t srow[kMxBlock];
-#pragma unroll
-    for (int j = 0; j < kMxBlock; ++j) {
-        srow[j] = r0 + j;
-        if (a.gather && j < valid) srow[j] = a.gather[r0 + j];
-    }
     u32x4 v[kMxBlock];
+    if constexpr (GATHER) {
+        // row r0 + j of the block is source row gather[r0 + j] (the same for
+        // the whole wave: scalar loads)
+        const char* in = (const char*)a.src.p[m] + c0 * 2;
+        int64_t srow[kMxBlock];
 #pragma unroll
-    for (int j = 0; j < kMxBlock; ++j) {
-        v[j] = (u32x4){0u, 0u, 0u, 0u};
-        if (j < valid && live)
-            v[j] = __builtin_nontemporal_load((const u32x4*)(in + (srow[j] * cols + c0) * 2));
+        for (int j = 0; j < kMxBlock; ++j) srow[j] = j < valid ? a.gather[r0 + j] : 0;
+#pragma unroll
+        for (int j = 0; j < kMxBlock; ++j) {
+            v[j] = (u32x4){0u, 0u, 0u, 0u};
+            if (j < valid && live)
+                v[j] = __builtin_nontemporal_load((const u32x4*)(in + srow[j] * cols * 2));
+        }
+    } else {
+        const char* in = (const char*)a.src.p[m] + r0 * cols * 2;
+#pragma unroll
+        for (int j = 0; j < kMxBlock; ++j) {
+            v[j] = (u32x4){0u, 0u, 0u, 0u};
+            if (j < valid && live)
+                v[j] = __builtin_nontemporal_load((const u32x4*)(in + (j * cols + c0) * 2));
+        }
     }
 
     uint32_t Sfix = 0;
@@ -567,14 +574,18 @@ hipError_t launch_quant(const MatTable& src, int nmat, const int32_t* sizes, int
     const int64_t nblk = colwise_block_bound(rows, a.ngroups);
     dim3 grid((unsigned)((cols + 511) / 512), (unsigned)((nblk + 3) / 4), (unsigned)nmat);
     TraceScope ts(name, s);
-    if (fixed_amax) {
-        if (rcodes && ccodes) quant_tile_kernel<true, true, true><<<grid, 256, 0, s>>>(a);
-        else if (rcodes) quant_tile_kernel<true, false, true><<<grid, 256, 0, s>>>(a);
-        else quant_tile_kernel<false, true, true><<<grid, 256, 0, s>>>(a);
+    if (gather) {   // the routed activations: both orientations
+        if (!rcodes || !ccodes) return hipErrorInvalidValue;
+        if (fixed_amax) quant_tile_kernel<true, true, true, true><<<grid, 256, 0, s>>>(a);
+        else quant_tile_kernel<true, true, false, true><<<grid, 256, 0, s>>>(a);
+    } else if (fixed_amax) {
+        if (rcodes && ccodes) quant_tile_kernel<true, true, true, false><<<grid, 256, 0, s>>>(a);
+        else if (rcodes) quant_tile_kernel<true, false, true, false><<<grid, 256, 0, s>>>(a);
+        else quant_tile_kernel<false, true, true, false><<<grid, 256, 0, s>>>(a);
     } else {
-        if (rcodes && ccodes) quant_tile_kernel<true, true, false><<<grid, 256, 0, s>>>(a);
-        else if (rcodes) quant_tile_kernel<true, false, false><<<grid, 256, 0, s>>>(a);
-        else quant_tile_kernel<false, true, false><<<grid, 256, 0, s>>>(a);
+        if (rcodes && ccodes) quant_tile_kernel<true, true, false, false><<<grid, 256, 0, s>>>(a);
+        else if (rcodes) quant_tile_kernel<true, false, false, false><<<grid, 256, 0, s>>>(a);
+        else quant_tile_kernel<false, true, false, false><<<grid, 256, 0, s>>>(a);
     }
     return hipGetLastError();
 }

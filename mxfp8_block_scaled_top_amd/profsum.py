@@ -153,7 +153,8 @@ def label(symbol: str, grid: int, sh) -> str:
     if name != "quant_tile":
         return name
     A = sh.T * sh.k
-    fixed = symbol.split("quant_tile_kernel<", 1)[1].split(">", 1)[0].replace(" ", "").endswith("true")
+    targs = symbol.split("quant_tile_kernel<", 1)[1].split(">", 1)[0].replace(" ", "").split(",")
+    fixed = len(targs) > 2 and targs[2] == "true"           # <ROWS, COLS, FIXED, GATHER>
     pre = "fp8_quant_" if fixed else "mx_quant_"
     cands = {"xp/dyp": _quant_grid(A, sh.H, sh.E, 1), "w1": _quant_grid(2 * sh.I, sh.H, 1, sh.E),
              "w2": _quant_grid(sh.H, sh.I, 1, sh.E), "a2": _quant_grid(A, sh.I, sh.E, 1),
