@@ -33,6 +33,16 @@ def test_quant_workload_full():
     _rows_check(synth.quant_matrix(8192, 4096))
 
 
+def test_quant_rows_more_chunks_than_waves():
+    """A matrix with more 4-row x 512-column chunks than the rowwise kernel
+    has waves (300,001 x 96: every wave loops, the last chunk is ragged in
+    rows, and the columns fill only part of a chunk), bit-exact."""
+    g = torch.Generator().manual_seed(7)
+    x = (torch.randn((300001, 96), generator=g) *
+         torch.exp2(torch.randint(-12, 13, (300001, 1), generator=g).float())).to(torch.bfloat16)
+    _rows_check(x)
+
+
 def test_quant_all_bf16_patterns():
     bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
     v = bits.view(torch.bfloat16)
