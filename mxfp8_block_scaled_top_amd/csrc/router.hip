@@ -7,7 +7,7 @@
 //
 //   router_logits  the contraction over H on the matrix cores (bf16 MFMA
 //                  32x32x16): a workgroup owns 32 tokens and all E <= 64
-//                  experts; its 4 waves take the 64-value K steps round robin
+//                  experts; its 8 waves take the 64-value K steps round robin
 //                  and meet in LDS.  Each lane loads 64 contiguous bytes of its
 //                  token row per K step (both halves of the wave: the row's
 //                  whole 128 bytes), and the same K positions of the W_r row
@@ -31,15 +31,15 @@ typedef __attribute__((ext_vector_type(8))) __bf16 rt_bf16x8;
 typedef __attribute__((ext_vector_type(16))) float rt_f32x16;
 
 constexpr int kRtTok = 32;          // tokens per logits workgroup
+constexpr int kRtWaves = 8;         // waves per logits workgroup (K steps round robin)
 constexpr int kDxTok = 32;          // tokens per dx workgroup
 constexpr int kDxCols = 256;        // columns per dx / dw workgroup
 constexpr int kDwExperts = 16;      // experts per dw register pass
 
-__global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __restrict__ x,
-                                                            const bf16_t* __restrict__ w,
-                                                            int T, int H, int E,
-                                                            float* __restrict__ logits) {
-    __shared__ float red[4][kRtTok][65];
+__global__ __launch_bounds__(64 * kRtWaves) void router_logits_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int T, int H, int E,
+    float* __restrict__ logits) {
+    __shared__ float red[kRtWaves][kRtTok][65];
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     const int r = lane & 31, h = lane >> 5;
@@ -84,11 +84,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __rest
     };
     // two of the wave's K steps per iteration, both loaded before either is
     // used (twice the bytes in flight)
-    for (int ks = wave; ks < nks; ks += 8) {
+    for (int ks = wave; ks < nks; ks += 2 * kRtWaves) {
         u32x4 xa[4], wa[4], wb[4], xb[4], va[4], vb[4];
-        const bool second = ks + 4 < nks;
+        const bool second = ks + kRtWaves < nks;
         load(ks, xa, wa, wb);
-        if (second) load(ks + 4, xb, va, vb);
+        if (second) load(ks + kRtWaves, xb, va, vb);
         mma(xa, wa, wb);
         if (second) mma(xb, va, vb);
     }
@@ -100,11 +100,14 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __rest
         red[wave][row][32 + r] = two ? acc1[v] : 0.f;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < kRtTok * E; i += 256) {
+    for (int i = threadIdx.x; i < kRtTok * E; i += 64 * kRtWaves) {
         const int row = i / E, e = i - row * E;
-        if (t0 + row < T)
-            logits[(int64_t)(t0 + row) * E + e] =
-                ((red[0][row][e] + red[1][row][e]) + red[2][row][e]) + red[3][row][e];
+        if (t0 + row < T) {
+            float sum = red[0][row][e];
+#pragma unroll
+            for (int q = 1; q < kRtWaves; ++q) sum += red[q][row][e];
+            logits[(int64_t)(t0 + row) * E + e] = sum;
+        }
     }
 }
 
@@ -366,7 +369,8 @@ hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w, int T, int H, 
                                 float* logits, hipStream_t s) {
     if (T == 0) return hipSuccess;
     TraceScope ts("router_logits", s);
-    router_logits_kernel<<<(T + kRtTok - 1) / kRtTok, 256, 0, s>>>(x, w, T, H, E, logits);
+    router_logits_kernel<<<(T + kRtTok - 1) / kRtTok, 64 * kRtWaves, 0, s>>>(x, w, T, H, E,
+                                                                            logits);
     return hipGetLastError();
 }
 
