@@ -164,7 +164,7 @@ int moe_permute(const uint16_t* x, int64_t T, int H, int k, const int32_t* dest_
         return MOE_ERR_SHAPE;
     // x and xp both NULL: only the probabilities move (the rows are gathered
     // by the consumer, grouped_mlp_*_gather)
-    if ((x == nullptr) != (xp == nullptr)) return MOE_ERR_NULL;
+    if (T > 0 && (x == nullptr) != (xp == nullptr)) return MOE_ERR_NULL;
     if (T > 0 && !dest_row) return MOE_ERR_NULL;
     if (T > 0 && !x && (!topk_prob || !prob_perm)) return MOE_ERR_NULL;
     if (T > 0 && topk_prob && !prob_perm) return MOE_ERR_NULL;
