@@ -166,6 +166,15 @@ def test_single_expert_dense(precision):
 
 
 @pytest.mark.parametrize("precision", ALL, ids=IDS)
+def test_smallest_sizes(precision):
+    """H = I = 128, the smallest sizes the grouped MLP takes: one N tile of
+    128 gate + 128 up columns in the forward, half an N tile in the SwiGLU
+    backward, and K of two MXFP8 steps; three experts, one of them empty."""
+    inp = _inputs(T=100, H=128, I=128, E=3, seed=8, dead=(1,))
+    _layer_compare(inp, 2, precision, "smallest")
+
+
+@pytest.mark.parametrize("precision", ALL, ids=IDS)
 def test_many_experts_topk8(precision):
     inp = _inputs(T=512, H=256, I=384, E=64, seed=3)
     _layer_compare(inp, 8, precision, "e64k8")
