@@ -71,7 +71,6 @@ constexpr int kStageB = 2 * kTileB;           // A + B
 constexpr int kLdsB = kStages * kStageB;      // 128 KiB
 constexpr int kMNRowB = kGemmBM * 2;          // M/N-contiguous LDS row: 256 bf16 = 512 B
 constexpr uint32_t kOob = 0x80000000u;        // buffer offset that reads zeros
-constexpr int kTailRows = 2;                  // fragment rows of a K step computed after its barrier
 
 // K-contiguous tile: row r, 16-byte chunk c (4 per row); XOR with (r>>2)&3
 // makes the 16-byte reads of 16 consecutive rows hit 16 distinct bank groups.
@@ -283,10 +282,15 @@ __device__ __forceinline__ void dma4(const i32x4& rs, uint32_t voff, uint32_t ld
 // of later K steps) are outstanding and all LDS accesses are done, then
 // synchronize the workgroup.  __syncthreads() would also fence global memory,
 // which waits for every outstanding load and so drains the look-ahead.
+// The compiler does not see the waits inside the asm: the trailing
+// s_waitcnt lgkmcnt(0) (free, the counter is already zero) tells it that
+// every earlier LDS read has completed, so it does not hold back the MFMAs
+// after the barrier for reads that landed long ago.
 template <int N>
 __device__ __forceinline__ void pipe_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt(63) expcnt(7) lgkmcnt(0)
 }
 
 // LDS-DMA of one K step of a K-contiguous tile: the wave's 4 instructions
@@ -1025,7 +1029,9 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     using I3 = std::integral_constant<int, 3>;
     using I4 = std::integral_constant<int, 4>;
     // fragment rows whose MFMAs run after the barrier, under the next step's
-    // LDS reads
+    // LDS reads: 8 of the 16 scaled MFMAs, 8 of the 32 bf16 ones (measured
+    // best; the bf16 step has 16 fragment reads against the 8-bit step's 24)
+    constexpr int kTailRows = DT == DT_BF16 ? 1 : 2;
     using ISplit = std::integral_constant<int, 4 - kTailRows>;
     // One K step kt whose fragments are in Fc (read from stage S): prefetch
     // step kt+3 into stage S+3 (whose reads all finished before the previous
@@ -1043,6 +1049,27 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         __builtin_amdgcn_sched_barrier(0);
         load(std::integral_constant<int, (st + 1) % kStages>{}, Fn);
         mma(ISplit{}, I4{}, Fc);
+        // The next step's LDS reads spread between the MFMAs after the
+        // barrier, the first MFMA ahead of them: the matrix pipe stays busy
+        // while the reads trickle into LDS, and every read has several MFMAs
+        // to land behind.  (Left to itself the compiler put all reads after
+        // the sixth MFMA, two MFMAs before their first use; all 24 reads up
+        // front, ahead of the MFMAs, was slower still.)
+        if constexpr (DT == DT_BF16) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+            }
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
 
