@@ -420,17 +420,24 @@ __device__ __forceinline__ int st_idx(int row, int col) {
     return row * 128 + ((((col >> 2) ^ (row & 7))) << 2) + (col & 3);
 }
 
+// Value v of a lane's 32x32 fragment is row 4*hi + 8*(v>>2) + (v&3), column
+// fr.  Its row & 7 is 4*hi + (v&3), so st_idx(row, 32f + fr) is one of four
+// per-lane bases plus 1024*(v>>2) + 32*f: every write takes an immediate
+// offset instead of its own swizzle arithmetic.
 __device__ __forceinline__ void stage_fragments(float* R, const f32x16& f0, const f32x16& f1,
                                                 const f32x16& f2, const f32x16& f3,
                                                 int lane = threadIdx.x & 63) {
     const int fr = lane & 31, hi = lane >> 5;
+    float* base[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) base[r] = R + st_idx(4 * hi + r, fr);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-        int row = 4 * hi + 8 * (v >> 2) + (v & 3);
-        R[st_idx(row, fr)] = f0[v];
-        R[st_idx(row, 32 + fr)] = f1[v];
-        R[st_idx(row, 64 + fr)] = f2[v];
-        R[st_idx(row, 96 + fr)] = f3[v];
+        float* b = base[v & 3] + 1024 * (v >> 2);
+        b[0] = f0[v];
+        b[32] = f1[v];
+        b[64] = f2[v];
+        b[96] = f3[v];
     }
 }
 
@@ -594,25 +601,37 @@ __device__ __forceinline__ void swiglu_fwd_rows(const EpiCtx& c, float* R, const
 // read in whole 128-byte lines (8 lanes per line of a row, streamed past L2)
 // and staged as (gate, up) bf16 pairs, one pair per fp32 slot of R2, where
 // the row-per-lane arithmetic reads them.  Rows past the expert stage zeros.
+// load_a1 only issues the loads: the first slice's right after the K loop,
+// each next slice's as soon as the current one is staged, so that they are
+// in flight through a whole slice of work instead of stalling its start.
 // (float4 accesses throughout, like the du stores that later reuse the
 // slots, so the compiler keeps their order.)
-__device__ __forceinline__ void stage_a1_pairs(const GemmArgs& g, const Tile& tl, float* R2,
-                                               int frow0, int valid, int jw, int lane) {
+struct A1Words { u32x4 g[4][2], u[4][2]; };
+
+__device__ __forceinline__ void load_a1(const GemmArgs& g, const Tile& tl, int wm, int wn, int fi,
+                                        int lane, A1Words& w) {
     const int64_t I = g.I;
+    const int frow0 = tl.m0 + wm * 128 + fi * 32;
+    const int valid = min(32, tl.rows_e - frow0);
+    const int jw = tl.n0 + wn * 128;
+    const bool slab = jw < I;
     const int c8 = lane & 7;
-    u32x4 wg[4][2], wu[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int row = (lane >> 3) + 8 * i, col = 64 * s + 8 * c8;
-            wg[i][s] = wu[i][s] = (u32x4){0u, 0u, 0u, 0u};
-            if (row < valid) {
+            w.g[i][s] = w.u[i][s] = (u32x4){0u, 0u, 0u, 0u};
+            if (slab && row < valid) {
                 const bf16_t* a = g.a1 + (tl.row0 + frow0 + row) * 2 * I + jw + col;
-                wg[i][s] = __builtin_nontemporal_load((const u32x4*)a);
-                wu[i][s] = __builtin_nontemporal_load((const u32x4*)(a + I));
+                w.g[i][s] = __builtin_nontemporal_load((const u32x4*)a);
+                w.u[i][s] = __builtin_nontemporal_load((const u32x4*)(a + I));
             }
         }
+}
+
+__device__ __forceinline__ void stage_a1_pairs(float* R2, const A1Words& w, int lane) {
+    const int c8 = lane & 7;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -621,7 +640,7 @@ __device__ __forceinline__ void stage_a1_pairs(const GemmArgs& g, const Tile& tl
             float x[8];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {      // word k: columns 2k, 2k+1
-                const uint32_t gw = wg[i][s][k], uw = wu[i][s][k];
+                const uint32_t gw = w.g[i][s][k], uw = w.u[i][s][k];
                 x[2 * k] = __uint_as_float((gw & 0xffffu) | (uw << 16));
                 x[2 * k + 1] = __uint_as_float((gw >> 16) | (uw & 0xffff0000u));
             }
@@ -640,7 +659,7 @@ template <int DT>
 __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float* R2,
                                                 float* red, const f32x16& f0, const f32x16& f1,
                                                 const f32x16& f2, const f32x16& f3, int fi,
-                                                uint32_t& amx) {
+                                                uint32_t& amx, A1Words& w) {
     const GemmArgs& g = c.g;
     const Tile& tl = c.tl;
     const int lane = c.lane;
@@ -652,7 +671,8 @@ __device__ __forceinline__ void swiglu_bwd_rows(const EpiCtx& c, float* R, float
     const int jw = tl.n0 + c.wn * 128;                      // first column of the wave
     const bool slab = jw < I;                              // I % 128 == 0: all or nothing
     const int row = lane >> 1, h = lane & 1;
-    if (slab && valid > 0) stage_a1_pairs(g, tl, R2, frow0, valid, jw, lane);
+    if (slab && valid > 0) stage_a1_pairs(R2, w, lane);
+    if (fi > 0) load_a1(g, tl, c.wm, c.wn, fi - 1, lane, w);   // the next slice's, in flight
     wave_lds_sync();
     float part = 0.f;
     {
@@ -1120,6 +1140,11 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         const int ln = lane_after_loop();
         const int c8 = (ln & 15) * 8;
         const int gcol = wn * 128 + c8;             // N is a multiple of 8: all or nothing
+        const int r0 = ln >> 4;
+        // the lane's byte offset from its instruction's first row: the same
+        // for every store, whose row base is uniform (scalar arithmetic)
+        const uint32_t loff = (uint32_t)(r0 * ldc + gcol) * 2u;
+        const bool cok = gcol < col_lim;
         // (slices in reverse order: the compiler then keeps every accumulator
         // in place through the epilogue instead of parking one fragment in
         // scratch memory)
@@ -1130,15 +1155,14 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
             wave_lds_sync();
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int row = (ln >> 4) + 4 * i;
-                const int grow = wm * 128 + fi * 32 + row;
-                if (grow < row_lim && gcol < col_lim) {
+                const int urow = wm * 128 + fi * 32 + 4 * i;      // uniform
+                if (cok && r0 < row_lim - urow) {
                     float x[8];
-                    load_row8(R, row, c8, x);
+                    load_row8(R, r0 + 4 * i, c8, x);
                     // streaming store: the output is not read again by this
                     // kernel, so it should not evict the operands from L2
-                    __builtin_nontemporal_store(pack8_bf16(x),
-                                                (u32x4*)(C + (int64_t)grow * ldc + gcol));
+                    const char* rb = (const char*)C + (int64_t)urow * ldc * 2;
+                    __builtin_nontemporal_store(pack8_bf16(x), (u32x4*)(rb + loff));
                 }
             }
             wave_lds_sync();
@@ -1149,6 +1173,8 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     // the routing probability of the lane's row in each 32-row slice, loaded
     // once for the whole epilogue (rows past the expert are never used)
     const int ln = lane_after_loop();
+    A1Words a1w;
+    if (EPI == EPI_SWIGLU_BWD) load_a1(g, tl, wm, wn, 3, ln, a1w);   // the first slice's saved A1
     float pr[4] = {0.f, 0.f, 0.f, 0.f};
     if (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD) {
 #pragma unroll
@@ -1178,10 +1204,10 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         float* R2 = R + 32 * 128;
         uint32_t amx = 0;
         // (slices in reverse order: no accumulator fragment parked in scratch)
-        swiglu_bwd_rows<DT>(c, R, R2, red, acc[3][0], acc[3][1], acc[3][2], acc[3][3], 3, amx);
-        swiglu_bwd_rows<DT>(c, R, R2, red, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2, amx);
-        swiglu_bwd_rows<DT>(c, R, R2, red, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1, amx);
-        swiglu_bwd_rows<DT>(c, R, R2, red, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0, amx);
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[3][0], acc[3][1], acc[3][2], acc[3][3], 3, amx, a1w);
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[2][0], acc[2][1], acc[2][2], acc[2][3], 2, amx, a1w);
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[1][0], acc[1][1], acc[1][2], acc[1][3], 1, amx, a1w);
+        swiglu_bwd_rows<DT>(c, R, R2, red, acc[0][0], acc[0][1], acc[0][2], acc[0][3], 0, amx, a1w);
         if (kAmax) amax_to_part(amx, (uint32_t*)sched, g.amax_part);
         __syncthreads();                    // red holds both column halves' partials
         const int t = wave * 64 + ln;
