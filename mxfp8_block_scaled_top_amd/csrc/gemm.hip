@@ -612,21 +612,32 @@ __device__ __forceinline__ void load_a1(const GemmArgs& g, const Tile& tl, int w
                                         int lane, A1Words& w) {
     const int64_t I = g.I;
     const int frow0 = tl.m0 + wm * 128 + fi * 32;
-    const int valid = min(32, tl.rows_e - frow0);
+    const int valid = max(0, min(32, tl.rows_e - frow0));
     const int jw = tl.n0 + wn * 128;
     const bool slab = jw < I;
-    const int c8 = lane & 7;
+    // One buffer resource per slice, based at its first row: rows past the
+    // expert (and every row, for a wave whose columns lie past I) are out of
+    // its range and read zero, with no per-row branches or zero fills.
+    // (every field is uniform: readfirstlane says so, else the compiler
+    // wraps each load in a loop over the distinct descriptors of the wave)
+    const int rowb = (int)(4 * I);                             // bytes per A1 row (2I bf16)
+    // (readfirstlane returns int: both halves go through uint32_t, so the
+    // low half is not sign-extended into the high one)
+    const uint64_t base = (uint64_t)(g.a1 + (tl.row0 + frow0) * 2 * I);
+    const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
+    const uint64_t ubase = ((uint64_t)bhi << 32) | (uint64_t)blo;
+    const int nrec = __builtin_amdgcn_readfirstlane(slab ? valid * rowb : 0);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)ubase, (short)0, nrec, 0x00020000);
+    const int voff = (lane >> 3) * rowb + (jw + 8 * (lane & 7)) * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const int row = (lane >> 3) + 8 * i, col = 64 * s + 8 * c8;
-            w.g[i][s] = w.u[i][s] = (u32x4){0u, 0u, 0u, 0u};
-            if (slab && row < valid) {
-                const bf16_t* a = g.a1 + (tl.row0 + frow0 + row) * 2 * I + jw + col;
-                w.g[i][s] = __builtin_nontemporal_load((const u32x4*)a);
-                w.u[i][s] = __builtin_nontemporal_load((const u32x4*)(a + I));
-            }
+            const int o = voff + 8 * i * rowb + 128 * s;           // row lane/8 + 8i
+            w.g[i][s] = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 2);   // nt
+            w.u[i][s] = __builtin_amdgcn_raw_buffer_load_b128(rs, o + 2 * (int)I, 0, 2);
         }
 }
 
@@ -966,6 +977,14 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
     };
 
     const int fr = lane & 31, hi = lane >> 5;
+    // Per-lane byte offsets of the K-contiguous fragment reads inside a stage.
+    // Fragment f covers tile rows base + 32 f + fr; 32 f leaves the chunk
+    // swizzle (row >> 2) & 3 = (fr >> 2) & 3 unchanged, so 16-byte chunk c of
+    // fragment f lies at o_c + 32 f * kRowB: two offsets per operand (chunks
+    // hi and 2 + hi), every read of a stage an immediate offset from them.
+    const int oA0 = lds_off(wm * 128 + fr, hi), oA2 = lds_off(wm * 128 + fr, 2 + hi);
+    const int oB0 = lds_off(wn * 128 + fr, hi), oB2 = lds_off(wn * 128 + fr, 2 + hi);
+    constexpr int kFragB = 32 * kRowB;
     // The operand fragments of one K step, held in registers.  Two sets
     // alternate: while the MFMAs consume step k's set, the LDS reads of step
     // k+1 fill the other, so LDS latency is hidden behind matrix work instead
@@ -985,14 +1004,14 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
 #pragma unroll
                 for (int fj = 0; fj < 4; ++fj) {
                     if (LB == L_KMAJ)
-                        F.b[s][fj] = *(const bf16x8_t*)(B + lds_off(wn * 128 + fj * 32 + fr, s * 2 + hi));
+                        F.b[s][fj] = *(const bf16x8_t*)(B + (s ? oB2 : oB0) + fj * kFragB);
                     else
                         F.b[s][fj] = mn_frag(B, s, wn * 128 + fj * 32);
                 }
 #pragma unroll
                 for (int fi = 0; fi < 4; ++fi) {
                     if (LA == L_KMAJ)
-                        F.a[s][fi] = *(const bf16x8_t*)(A + lds_off(wm * 128 + fi * 32 + fr, s * 2 + hi));
+                        F.a[s][fi] = *(const bf16x8_t*)(A + (s ? oA2 : oA0) + fi * kFragB);
                     else
                         F.a[s][fi] = mn_frag(A, s, wm * 128 + fi * 32);
                 }
@@ -1005,8 +1024,8 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
 #pragma unroll
             for (int fj = 0; fj < 4; ++fj) {
                 int row = wn * 128 + fj * 32 + fr;
-                u32x4 lo = *(const u32x4*)(B + lds_off(row, hi));
-                u32x4 up = *(const u32x4*)(B + lds_off(row, 2 + hi));
+                u32x4 lo = *(const u32x4*)(B + oB0 + fj * kFragB);
+                u32x4 up = *(const u32x4*)(B + oB2 + fj * kFragB);
                 F.b[fj] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                   (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
                 F.sb[fj] = ssc[st][1][hi][row];          // byte -> low 8 bits
@@ -1014,8 +1033,8 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
 #pragma unroll
             for (int fi = 0; fi < 4; ++fi) {
                 int row = wm * 128 + fi * 32 + fr;
-                u32x4 lo = *(const u32x4*)(A + lds_off(row, hi));
-                u32x4 up = *(const u32x4*)(A + lds_off(row, 2 + hi));
+                u32x4 lo = *(const u32x4*)(A + oA0 + fi * kFragB);
+                u32x4 up = *(const u32x4*)(A + oA2 + fi * kFragB);
                 F.a[fi] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                   (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
                 F.sa[fi] = ssc[st][0][hi][row];
