@@ -441,6 +441,27 @@ __device__ __forceinline__ void stage_fragments(float* R, const f32x16& f0, cons
     }
 }
 
+// bf16 staging of one 32-row slice for the plain-store epilogue: dword
+// (p, c) holds rows 2p and 2p+1 of column c (low and high halves), at
+// p * 128 + c.  A lane's fragment values 4g+j (rows 4hi + 8g + j) pair up as
+// j = 0,1 (row pair 2hi + 4g) and j = 2,3 (row pair 2hi + 4g + 1).
+__device__ __forceinline__ void stage_pairs_bf16(uint32_t* P, const f32x16& f0, const f32x16& f1,
+                                                 const f32x16& f2, const f32x16& f3, int lane) {
+    const int fr = lane & 31, hi = lane >> 5;
+    uint32_t* b = P + (2 * hi) * 128 + fr;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int v = 4 * g + 2 * h;
+            uint32_t* d = b + (4 * g + h) * 128;
+            d[0] = pack_bf16x2(f0[v], f0[v + 1]);
+            d[32] = pack_bf16x2(f1[v], f1[v + 1]);
+            d[64] = pack_bf16x2(f2[v], f2[v + 1]);
+            d[96] = pack_bf16x2(f3[v], f3[v + 1]);
+        }
+}
+
 __device__ __forceinline__ void load_row8(const float* R, int row, int col, float (&x)[8]) {
     float4 a = *(const float4*)(R + st_idx(row, col));
     float4 b = *(const float4*)(R + st_idx(row, col + 4));
@@ -1095,9 +1116,12 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         // the sixth MFMA, two MFMAs before their first use; all 24 reads up
         // front, ahead of the MFMAs, was slower still.)
         if constexpr (DT == DT_BF16) {
+            // reads per step: 8 per K-contiguous operand, 16 (transposing
+            // 8-byte reads) per M/N-contiguous one
+            constexpr int kReads = (LA == L_KMAJ ? 8 : 16) + (LB == L_KMAJ ? 8 : 16);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x100, kReads / 8, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
             }
         } else {
@@ -1150,10 +1174,11 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
             row_lim = g.M - tl.m0;
         }
         // Each 32-row slice of the wave's 128 x 128 result goes through the
-        // wave's own LDS region (the pipeline has drained), so that a lane
-        // stores 8 neighbouring columns as one 16-byte write (4 rows x 256
-        // bytes per instruction) instead of 2-byte writes column by column.
-        // (The SwiGLU epilogues keep ordinary stores: their instructions write
+        // wave's own LDS region (the pipeline has drained), converted to bf16
+        // row pairs on the way in, so that a lane stores 8 neighbouring
+        // columns of two rows as two 16-byte writes (4 rows x 256 bytes per
+        // instruction) instead of 2-byte writes column by column.  (The
+        // SwiGLU epilogues keep ordinary stores: their instructions write
         // 16-byte pieces of a line, which L2 must merge.)
         float* R = (float*)(wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3);
         const int ln = lane_after_loop();
@@ -1167,22 +1192,41 @@ void gemm_kernel(GemmArgs g, int ntn, int mtm) {
         // (slices in reverse order: the compiler then keeps every accumulator
         // in place through the epilogue instead of parking one fragment in
         // scratch memory)
+        // slices staged as bf16 row pairs (half the LDS bytes of fp32): a
+        // lane reads 8 columns of one row pair (two 16-byte reads) and
+        // stores them as two 16-byte row pieces
+        uint32_t* P = (uint32_t*)R;
+        // byte offsets of the lane's two rows (2 r0 and 2 r0 + 1 of its
+        // instruction's first row pair) at its 8 columns
+        const uint32_t lo_off = (uint32_t)(2 * r0 * ldc + gcol) * 2u;
+        const uint32_t hi_off = lo_off + (uint32_t)ldc * 2u;
 #pragma unroll
         for (int fr = 0; fr < 4; ++fr) {
             const int fi = 3 - fr;
-            stage_fragments(R, acc[fi][0], acc[fi][1], acc[fi][2], acc[fi][3], ln);
+            stage_pairs_bf16(P, acc[fi][0], acc[fi][1], acc[fi][2], acc[fi][3], ln);
             wave_lds_sync();
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int urow = wm * 128 + fi * 32 + 4 * i;      // uniform
-                if (cok && r0 < row_lim - urow) {
-                    float x[8];
-                    load_row8(R, r0 + 4 * i, c8, x);
-                    // streaming store: the output is not read again by this
-                    // kernel, so it should not evict the operands from L2
-                    const char* rb = (const char*)C + (int64_t)urow * ldc * 2;
-                    __builtin_nontemporal_store(pack8_bf16(x), (u32x4*)(rb + loff));
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int p = r0 + 4 * i;                          // row pair of the slice
+                const int urow = wm * 128 + fi * 32 + 8 * i;       // uniform
+                const u32x4 d0 = *(const u32x4*)(P + p * 128 + c8);
+                const u32x4 d1 = *(const u32x4*)(P + p * 128 + c8 + 4);
+                u32x4 lo, hi2;
+                lo[0] = __builtin_amdgcn_perm(d0[1], d0[0], 0x05040100u);
+                lo[1] = __builtin_amdgcn_perm(d0[3], d0[2], 0x05040100u);
+                lo[2] = __builtin_amdgcn_perm(d1[1], d1[0], 0x05040100u);
+                lo[3] = __builtin_amdgcn_perm(d1[3], d1[2], 0x05040100u);
+                hi2[0] = __builtin_amdgcn_perm(d0[1], d0[0], 0x07060302u);
+                hi2[1] = __builtin_amdgcn_perm(d0[3], d0[2], 0x07060302u);
+                hi2[2] = __builtin_amdgcn_perm(d1[1], d1[0], 0x07060302u);
+                hi2[3] = __builtin_amdgcn_perm(d1[3], d1[2], 0x07060302u);
+                const char* rb = (const char*)C + (int64_t)urow * ldc * 2;
+                // streaming stores: the output is not read again by this
+                // kernel, so it should not evict the operands from L2
+                if (cok && 2 * r0 < row_lim - urow)
+                    __builtin_nontemporal_store(lo, (u32x4*)(rb + lo_off));
+                if (cok && 2 * r0 + 1 < row_lim - urow)
+                    __builtin_nontemporal_store(hi2, (u32x4*)(rb + hi_off));
             }
             wave_lds_sync();
         }
