@@ -206,7 +206,10 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
     u32x4 v[kMxBlock];
     if constexpr (GATHER) {
         // row r0 + j of the block is source row gather[r0 + j] (the same for
-        // the whole wave: scalar loads)
+        // the whole wave: scalar loads).  Ordinary loads, not streaming ones:
+        // each token row is read k times, and with many experts and k = 8
+        // some of the other reads find it still in L2 (E = 64, k = 8: 0.225
+        // -> 0.21 ms per launch; no change at E = 8, k = 2).
         const char* in = (const char*)a.src.p[m] + c0 * 2;
         int64_t srow[kMxBlock];
 #pragma unroll
@@ -214,8 +217,7 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(QuantTileArgs a) {
 #pragma unroll
         for (int j = 0; j < kMxBlock; ++j) {
             v[j] = (u32x4){0u, 0u, 0u, 0u};
-            if (j < valid && live)
-                v[j] = __builtin_nontemporal_load((const u32x4*)(in + srow[j] * cols * 2));
+            if (j < valid && live) v[j] = *(const u32x4*)(in + srow[j] * cols * 2);
         }
     } else {
         const char* in = (const char*)a.src.p[m] + r0 * cols * 2;
