@@ -174,6 +174,37 @@ def test_smallest_sizes(precision):
     _layer_compare(inp, 2, precision, "smallest")
 
 
+BOUNDARY_SPLIT = [0, 1, 31, 32, 33, 63, 64, 65, 255, 256, 257, 513]
+
+
+@pytest.mark.parametrize("precision", ALL, ids=IDS)
+def test_tile_boundary_splits(precision):
+    """Expert sizes on every boundary the kernels pad or tile to: the 32-row
+    MXFP8 block (31, 32, 33), the 64-row K step of the 8-bit weight
+    gradients and the row-pair padding (63, 64, 65), the 256-row tile (255,
+    256, 257, 513), an empty expert and a one-row expert.  k = 1 with one
+    logit lifted per token, so the sizes are exact; the tokens of the
+    experts interleave."""
+    rng = np.random.default_rng(9)
+    choice = np.repeat(np.arange(len(BOUNDARY_SPLIT)), BOUNDARY_SPLIT)
+    rng.shuffle(choice)
+    T, E = choice.size, len(BOUNDARY_SPLIT)
+    inp = _inputs(T=T, H=256, I=256, E=E, seed=9)
+    L = inp["logits"].numpy()
+    L[np.arange(T), choice] += 20.0
+    got, _ = _layer_compare(inp, 1, precision, "tile-boundary splits")
+    assert np.array_equal(np_(got["route"]["split_sizes"]), BOUNDARY_SPLIT)
+
+
+@pytest.mark.parametrize("precision", ALL, ids=IDS)
+def test_one_token_all_experts(precision):
+    """T = 1 with k = E: every expert holds one row, every tile is one row
+    of 256 and every 32-row block one row of 32."""
+    inp = _inputs(T=1, H=128, I=128, E=4, seed=10)
+    got, _ = _layer_compare(inp, 4, precision, "one token, k = E")
+    assert np.array_equal(np_(got["route"]["split_sizes"]), [1, 1, 1, 1])
+
+
 @pytest.mark.parametrize("precision", ALL, ids=IDS)
 def test_many_experts_topk8(precision):
     inp = _inputs(T=512, H=256, I=384, E=64, seed=3)
