@@ -37,7 +37,14 @@
  * argument checks happen before any launch, so a call that returns an error
  * has enqueued nothing.  Device-data preconditions (split sizes summing to
  * the row count, expert ids below E, valid permutations) are the caller's
- * duty and are not checked.  MOE_ERR_HIP reports a failed launch; the HIP
+ * duty and are not checked by these calls (moe_check_routing checks them
+ * on request).  Data that break them give unspecified results, but the
+ * kernels keep every access inside the buffers: split sizes are clamped (a
+ * negative size counts as 0, and sizes whose running total passes the row
+ * count are cut at it); dest_row entries outside [0, T*k) are skipped; an
+ * expert id outside [0, E) receives no gradient.  The one exception is
+ * src_token of the gathered calls, whose source row count they are not
+ * given: it is read as given.  MOE_ERR_HIP reports a failed launch; the HIP
  * error itself is left for the caller's next hipGetLastError().
  *
  * Alignment.  Tensor base pointers must be 16-byte aligned (MOE_ERR_ALIGN).
@@ -173,6 +180,39 @@ int moe_route_noalloc(const float* logits, int64_t T, int E, int k, uint32_t fla
 int moe_route_bwd(const float* topk_prob, const float* dprob_perm, const int32_t* dest_row,
                   const int32_t* topk_expert, const float* logits, int64_t T, int E, int k,
                   uint32_t flags, float* dlogits, hipStream_t stream);
+
+/*
+ * moe_check_routing -- device check of routing data that the grouped calls
+ * take on trust (the optional check of the device-data preconditions above).
+ * [AutoModel, "MoE 微调的痛点": each token goes to a few experts; BioNeMo,
+ *  "GroupedLinear": the grouped call takes the per-expert row counts.]
+ *
+ * Checks, on the device and without a host copy of the data:
+ *   split_sizes  int32 [E]: every size >= 0 (MOE_CHECK_SPLIT_NEGATIVE) and
+ *                their sum == rows (MOE_CHECK_SPLIT_SUM);
+ *   dest_row     int32 [T, k]: every entry in [0, rows) (MOE_CHECK_DEST_RANGE);
+ *   src_token    int32 [rows]: every entry in [0, T) (MOE_CHECK_SRC_RANGE), and
+ *                src_token[dest_row[t][j]] == t (MOE_CHECK_MISMATCH);
+ *   topk_expert  int32 [T, k]: every entry in [0, E) (MOE_CHECK_EXPERT_RANGE),
+ *                and with split_sizes, dest_row[t][j] inside the rows of expert
+ *                topk_expert[t][j] (MOE_CHECK_MISMATCH).
+ * Any of the four arrays may be NULL: its checks are skipped.  What moe_route
+ * writes passes every check.
+ * status       int32 device, out: 0, or the OR of the MOE_CHECK_* bits of the
+ *              violations found.  Written by the stream (read it after
+ *              synchronizing); the call itself does not synchronize.
+ * Errors: MOE_ERR_NULL (status NULL), MOE_ERR_SHAPE (T < 0, rows < 0,
+ * E outside 1..64, k outside 1..E with dest_row or topk_expert given).
+ */
+#define MOE_CHECK_SPLIT_NEGATIVE 1
+#define MOE_CHECK_SPLIT_SUM 2
+#define MOE_CHECK_DEST_RANGE 4
+#define MOE_CHECK_SRC_RANGE 8
+#define MOE_CHECK_MISMATCH 16
+#define MOE_CHECK_EXPERT_RANGE 32
+int moe_check_routing(const int32_t* split_sizes, int E, int64_t rows, const int32_t* dest_row,
+                      const int32_t* src_token, const int32_t* topk_expert, int64_t T, int k,
+                      int32_t* status, hipStream_t stream);
 
 /*
  * moe_router_fwd -- the router linear layer fused with the routing: logits =

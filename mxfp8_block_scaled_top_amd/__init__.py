@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
             "moe_route": (I32, [P, I64, I32, I32, U32, P, P, P, P, P, P, P, SZ, P]),
             "moe_route_bwd": (I32, [P, P, P, P, P, I64, I32, I32, U32, P, P]),
             "moe_route_noalloc": (I32, [P, I64, I32, I32, U32, P, P, P, P, P, P, P]),
+            "moe_check_routing": (I32, [P, I32, I64, P, P, P, I64, I32, P, P]),
             "moe_permute": (I32, [P, I64, I32, I32, P, P, P, P, P]),
             "moe_unpermute": (I32, [P, I64, I32, I32, P, P, P, P]),
             "mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, P, P, P]),
@@ -238,6 +239,33 @@ def moe_route_bwd(topk_prob, dprob_perm, dest_row, topk_expert, E: int, logits=N
                                _ptr(topk_expert), _ptr(logits), T, E, k, int(softmax_all),
                                _ptr(dl), _stream(topk_prob.device)), "moe_route_bwd")
     return dl
+
+
+MOE_CHECK_SPLIT_NEGATIVE = 1
+MOE_CHECK_SPLIT_SUM = 2
+MOE_CHECK_DEST_RANGE = 4
+MOE_CHECK_SRC_RANGE = 8
+MOE_CHECK_MISMATCH = 16
+MOE_CHECK_EXPERT_RANGE = 32
+
+
+def moe_check_routing(split_sizes=None, rows: int = 0, E: int = None, dest_row=None,
+                      src_token=None, topk_expert=None) -> int:
+    """Device check of routing data: 0, or the OR of the MOE_CHECK_* bits of
+    the violations found (synchronizes to read the status word).  T and k
+    come from dest_row or topk_expert ([T, k]) when given."""
+    shaped = dest_row if dest_row is not None else topk_expert
+    T, k = (shaped.shape[0], shaped.shape[1]) if shaped is not None else (0, 1)
+    if src_token is not None and shaped is None:
+        raise MoEError("src_token needs dest_row or topk_expert for the token count")
+    if E is None:
+        E = split_sizes.numel() if split_sizes is not None else k
+    ref = next(t for t in (split_sizes, dest_row, src_token, topk_expert) if t is not None)
+    status = torch.empty(1, dtype=torch.int32, device=ref.device)
+    _check(lib().moe_check_routing(_ptr(split_sizes), E, rows, _ptr(dest_row), _ptr(src_token),
+                                   _ptr(topk_expert), T, k, _ptr(status), _stream(ref.device)),
+           "moe_check_routing")
+    return int(status.item())
 
 
 def moe_permute(x: torch.Tensor, dest_row: torch.Tensor, topk_prob=None):

@@ -24,7 +24,7 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libmoe_mi355x.so")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "router.hip", "permute.hip", "mxfp8.hip", "gemm.hip", "capi.cpp", "mlp.cpp", "linear.cpp", "trace.cpp"]
+SOURCES = ["route.hip", "router.hip", "permute.hip", "mxfp8.hip", "gemm.hip", "check.hip", "capi.cpp", "mlp.cpp", "linear.cpp", "trace.cpp"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -158,6 +158,17 @@ int moe_route_bwd(const float* topk_prob, const float* dprob_perm, const int32_t
                                        (int)T, E, k, flags, dlogits, stream));
 }
 
+int moe_check_routing(const int32_t* split_sizes, int E, int64_t rows, const int32_t* dest_row,
+                      const int32_t* src_token, const int32_t* topk_expert, int64_t T, int k,
+                      int32_t* status, hipStream_t stream) {
+    if (!status) return MOE_ERR_NULL;
+    if (T < 0 || rows < 0 || E < 1 || E > kMaxExperts) return MOE_ERR_SHAPE;
+    if ((dest_row || topk_expert) && (k < 1 || k > E || T * k > INT32_MAX)) return MOE_ERR_SHAPE;
+    if (!device_ok()) return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_check_routing(split_sizes, E, rows, dest_row, src_token, topk_expert,
+                                           T, k, status, stream));
+}
+
 int moe_permute(const uint16_t* x, int64_t T, int H, int k, const int32_t* dest_row,
                 const float* topk_prob, uint16_t* xp, float* prob_perm, hipStream_t stream) {
     if (T < 0 || H < 8 || (H % 8) || k < 1 || k > kMaxTopK || T * k > INT32_MAX)

@@ -137,6 +137,25 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     return v;
 }
 
+// A group's size as the kernels use it, from the size the caller gave (lane
+// g of a full wave holds group g's): a negative size counts as 0, and sizes
+// whose running total passes `rows` are cut at it.  Sizes that are >= 0 and
+// sum to rows come through unchanged; any others still keep every group
+// inside the rows the buffers hold.  (The running total is taken in 64 bits:
+// raw sizes may sum past 2^31.)
+__device__ __forceinline__ int clamp_group_size(int n, int64_t rows) {
+    const int lane = threadIdx.x & 63;
+    const int64_t v = n > 0 ? n : 0;
+    int64_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    const int64_t excl = incl - v;
+    return (int)((incl < rows ? incl : rows) - (excl < rows ? excl : rows));
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
     int lane = threadIdx.x & 63;
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));

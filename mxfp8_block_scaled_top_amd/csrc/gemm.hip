@@ -119,7 +119,7 @@ template <int GRP>
 __device__ bool decode_tile(const GemmArgs& g, int ntn, int mtm, int t, int* sched, Tile& tl) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
-        int n = lane < g.E ? g.split[lane] : 0;
+        const int n = clamp_group_size(lane < g.E ? g.split[lane] : 0, g.rows);
         int tiles = GRP == G_M ? ((n + kGemmBM - 1) / kGemmBM) * ntn : 0;
         sched[lane] = wave_incl_scan(tiles);
         sched[64 + lane] = wave_incl_scan(n);

@@ -40,6 +40,10 @@ hipError_t launch_unpermute(const bf16_t* yp, int T, int H, int k, const int32_t
 
 // ---- router linear layer
 size_t router_bwd_workspace_bytes(int64_t T, int H, int E);
+hipError_t launch_check_routing(const int32_t* split, int E, int64_t rows,
+                                const int32_t* dest_row, const int32_t* src_token,
+                                const int32_t* topk_expert, int64_t T, int k, int32_t* status,
+                                hipStream_t s);
 hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w, int T, int H, int E,
                                 float* logits, hipStream_t s);
 hipError_t launch_router_bwd(const float* dlogits, const bf16_t* x, const bf16_t* w, int T,

@@ -87,6 +87,7 @@ __device__ ColBlock locate_col_block(const int32_t* __restrict__ sizes, int ngro
         int n = 0;
         if (sizes) n = tid < ngroups ? sizes[tid] : 0;
         else n = tid == 0 ? (int)rows : 0;
+        n = clamp_group_size(n, rows);
         int nb = (n + kMxBlock - 1) / kMxBlock;
         int inb = wave_incl_scan(nb);
         int inr = wave_incl_scan(n);

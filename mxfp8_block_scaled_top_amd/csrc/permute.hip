@@ -5,6 +5,10 @@
 // "sending" is a row copy into the expert-grouped order that the grouped GEMM
 // consumes [BioNeMo MoE recipe page, section GroupedLinear].
 //
+// Grouped rows outside [0, T*k) in dest_row are skipped, so routing that does
+// not hold the preconditions gives unspecified rows but no access outside the
+// buffers.
+//
 // Both kernels are HBM-bound row copies: one thread moves one 16-byte chunk
 // (8 bf16) so every wave reads and writes whole 1 KiB row segments.  Permute
 // reads each token row once and writes it to its k grouped rows (the minimum
@@ -22,6 +26,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const u32x4* __restrict__ 
                                                       u32x4* __restrict__ xp,
                                                       float* __restrict__ prob_perm) {
     const size_t total = (size_t)T * cpr;
+    const int64_t rows = (int64_t)T * k;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (size_t)gridDim.x * blockDim.x) {
         size_t t = i / cpr;
@@ -29,7 +34,8 @@ __global__ __launch_bounds__(256) void permute_kernel(const u32x4* __restrict__ 
         u32x4 v = __builtin_nontemporal_load(x + i);
         const int32_t* d = dest_row + t * k;
         for (int j = 0; j < k; ++j) {
-            int r = d[j];
+            const int r = d[j];
+            if ((unsigned)r >= (unsigned)rows) continue;   // out of range: dropped
             xp[(size_t)r * cpr + c] = v;
             if (c == 0 && prob_perm) prob_perm[r] = topk_prob[t * k + j];
         }
@@ -42,7 +48,8 @@ __global__ __launch_bounds__(256) void permute_prob_kernel(int64_t picks,
                                                            const float* __restrict__ topk_prob,
                                                            float* __restrict__ prob_perm) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < picks) prob_perm[dest_row[i]] = topk_prob[i];
+    if (i < picks && (uint64_t)(uint32_t)dest_row[i] < (uint64_t)picks)
+        prob_perm[dest_row[i]] = topk_prob[i];
 }
 
 __global__ __launch_bounds__(256) void unpermute_kernel(const u32x4* __restrict__ yp, int T,
@@ -51,6 +58,7 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const u32x4* __restrict_
                                                         const float* __restrict__ topk_prob,
                                                         u32x4* __restrict__ y) {
     const size_t total = (size_t)T * cpr;
+    const int64_t rows = (int64_t)T * k;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (size_t)gridDim.x * blockDim.x) {
         size_t t = i / cpr;
@@ -58,6 +66,7 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const u32x4* __restrict_
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         const int32_t* d = dest_row + t * k;
         for (int j = 0; j < k; ++j) {
+            if ((unsigned)d[j] >= (unsigned)rows) continue;   // out of range: adds nothing
             u32x4 v = yp[(size_t)d[j] * cpr + c];
             float w = topk_prob ? topk_prob[t * k + j] : 1.f;
 #pragma unroll

@@ -165,6 +165,18 @@ __global__ void route_bwd_kernel(const float* __restrict__ topk_prob,
     if (t >= T) return;
     const size_t base = (size_t)t * k;
     float* out = dlogits + (size_t)t * E;
+    const unsigned rows = (unsigned)T * (unsigned)k;
+    // a grouped row outside [0, T*k) reads gradient 0; an expert outside
+    // [0, E) receives nothing (routing that breaks the preconditions gives
+    // unspecified values, never an access outside the buffers)
+    auto dp = [&](int j) -> float {
+        const unsigned r = (unsigned)dest_row[base + j];
+        return r < rows ? dprob_perm[r] : 0.f;
+    };
+    auto ex = [&](int j) -> int {
+        const int e = topk_expert[base + j];
+        return (unsigned)e < (unsigned)E ? e : -1;
+    };
     if (flags & 1u) {
         const float* row = logits + (size_t)t * E;
         float mx = row[0];
@@ -174,23 +186,27 @@ __global__ void route_bwd_kernel(const float* __restrict__ topk_prob,
         float inv = 1.f / s;
         float dot = 0.f;
         for (int j = 0; j < k; ++j) {
-            float p = expf(row[topk_expert[base + j]] - mx) * inv;
-            dot += p * dprob_perm[dest_row[base + j]];
+            const int e = ex(j);
+            if (e < 0) continue;
+            float p = expf(row[e] - mx) * inv;
+            dot += p * dp(j);
         }
         for (int e = 0; e < E; ++e) {
             float g = 0.f;
             for (int j = 0; j < k; ++j)
-                if (topk_expert[base + j] == e) g = dprob_perm[dest_row[base + j]];
+                if (ex(j) == e) g = dp(j);
             out[e] = expf(row[e] - mx) * inv * (g - dot);
         }
         return;
     }
     float dot = 0.f;
-    for (int j = 0; j < k; ++j) dot += topk_prob[base + j] * dprob_perm[dest_row[base + j]];
+    for (int j = 0; j < k; ++j) dot += topk_prob[base + j] * dp(j);
     for (int e = 0; e < E; ++e) out[e] = 0.f;
     for (int j = 0; j < k; ++j) {
+        const int e = ex(j);
+        if (e < 0) continue;
         float p = topk_prob[base + j];
-        out[topk_expert[base + j]] = p * (dprob_perm[dest_row[base + j]] - dot);
+        out[e] = p * (dp(j) - dot);
     }
 }
 

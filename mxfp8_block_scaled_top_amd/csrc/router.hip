@@ -153,6 +153,11 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict_
 #pragma unroll
                     for (int u = 0; u < 8; ++u)
                         rows[ii][u] = (t < T && j0 + u < k) ? dest_row[(int64_t)t * k + j0 + u] : -1;
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)   // outside [0, T*k): no row (skipped)
+                        if (rows[ii][u] >= (int64_t)T * k) rows[ii][u] = -1;
                 }
                 u32x4 v[2][8];
 #pragma unroll

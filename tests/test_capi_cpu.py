@@ -33,7 +33,7 @@ def test_header_declares_the_path():
               "mxfp8_quantize_both", "mxfp8_dequantize", "moe_router_fwd", "moe_router_bwd",
               "grouped_mlp_fwd", "grouped_mlp_bwd", "grouped_linear_fwd", "grouped_linear_bwd",
               "moe_workspace_bytes", "moe_workspace_region", "moe_status_string",
-              "moe_device_supported", "mxfp8_colwise_bytes"]:
+              "moe_device_supported", "mxfp8_colwise_bytes", "moe_check_routing"]:
         assert n in names, n
 
 
@@ -110,6 +110,17 @@ def test_host_validation_before_launch(L):
                              1 << 30, None) == ARG
     assert L.grouped_mlp_bwd(1, 2, 128, 256, 8, p, p, p, tab, tab, p, ctypes.byref(part), p, tab,
                              tab, p, p, 1 << 30, None) == ARG
+
+
+def test_check_routing_validation(L):
+    N, SHAPE = 1, 2
+    p = ctypes.c_void_p(4096)      # never dereferenced: every call below fails validation
+    assert L.moe_check_routing(p, 4, 20, p, p, p, 10, 2, None, None) == N      # no status word
+    assert L.moe_check_routing(p, 65, 20, p, p, p, 10, 2, p, None) == SHAPE    # E > 64
+    assert L.moe_check_routing(p, 4, -1, p, p, p, 10, 2, p, None) == SHAPE     # rows < 0
+    assert L.moe_check_routing(p, 4, 20, p, p, p, -1, 2, p, None) == SHAPE     # T < 0
+    assert L.moe_check_routing(p, 4, 20, p, p, p, 10, 5, p, None) == SHAPE     # k > E
+    assert L.moe_check_routing(p, 4, 20, None, None, p, 10, 0, p, None) == SHAPE   # k < 1
 
 
 def test_grouped_linear_validation(L):

@@ -128,3 +128,59 @@ def test_identity_k1_and_half_weights():
     r2 = moe.moe_route(torch.zeros((T, 8), dtype=torch.float32, device="cuda"), 2)
     xp2, _ = moe.moe_permute(x, r2["dest_row"])
     assert torch.equal(moe.moe_unpermute(xp2, r2["dest_row"], r2["topk_prob"]), x)
+
+
+# ---------------------------------------------------------------- routing check
+def _routed(T=777, E=8, k=2, seed=4):
+    L = np.random.default_rng(seed).standard_normal((T, E)).astype(np.float32)
+    return moe.moe_route(torch.from_numpy(L).cuda(), k)
+
+
+def _check(r, **over):
+    T, k = r["dest_row"].shape
+    args = {"split_sizes": r["split_sizes"], "rows": T * k, "E": r["split_sizes"].numel(),
+            "dest_row": r["dest_row"], "src_token": r["src_token"],
+            "topk_expert": r["topk_expert"]}
+    args.update(over)
+    return moe.moe_check_routing(**args)
+
+
+def test_check_routing_accepts_what_route_writes():
+    for T, E, k in [(777, 8, 2), (1, 4, 4), (513, 64, 8)]:
+        r = _routed(T, E, k)
+        assert _check(r) == 0, (T, E, k)
+    # every array optional
+    r = _routed()
+    assert moe.moe_check_routing(split_sizes=r["split_sizes"], rows=777 * 2) == 0
+    assert moe.moe_check_routing(dest_row=r["dest_row"], rows=777 * 2, E=8) == 0
+
+
+def test_check_routing_flags_each_violation():
+    """Each corruption of a valid routing sets exactly its bit."""
+    r = _routed()
+    T, k = r["dest_row"].shape
+    split = r["split_sizes"].clone()
+    split[3] += 1                  # (the experts after 3 would also move their rows)
+    assert _check(r, split_sizes=split, topk_expert=None) == moe.MOE_CHECK_SPLIT_SUM
+    split = r["split_sizes"].clone()
+    split[1] -= 5
+    split[2] += 5
+    assert _check(r, split_sizes=split, topk_expert=None) == 0   # sum kept, no expert check
+    split[1] = -1
+    split[2] = r["split_sizes"][1] + r["split_sizes"][2] + 1
+    assert _check(r, split_sizes=split, topk_expert=None) == moe.MOE_CHECK_SPLIT_NEGATIVE
+    dest = r["dest_row"].clone()
+    dest[5, 1] = T * k
+    assert _check(r, dest_row=dest) == moe.MOE_CHECK_DEST_RANGE
+    dest = r["dest_row"].clone()
+    dest[5, 0], dest[6, 0] = r["dest_row"][6, 0].item(), r["dest_row"][5, 0].item()
+    assert _check(r, dest_row=dest) & moe.MOE_CHECK_MISMATCH
+    src = r["src_token"].clone()
+    src[10] = -3
+    assert _check(r, src_token=src) == moe.MOE_CHECK_SRC_RANGE | moe.MOE_CHECK_MISMATCH
+    ex = r["topk_expert"].clone()
+    ex[7, 0] = 8
+    assert _check(r, topk_expert=ex) == moe.MOE_CHECK_EXPERT_RANGE
+    ex = r["topk_expert"].clone()
+    ex[7, 0] = (ex[7, 0] + 1) % 8     # its row stays in the old expert's rows
+    assert _check(r, topk_expert=ex) == moe.MOE_CHECK_MISMATCH
