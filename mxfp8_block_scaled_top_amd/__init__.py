@@ -259,6 +259,8 @@ def moe_check_routing(split_sizes=None, rows: int = 0, E: int = None, dest_row=N
     if src_token is not None and shaped is None:
         raise MoEError("src_token needs dest_row or topk_expert for the token count")
     if E is None:
+        if split_sizes is None and topk_expert is not None:
+            raise MoEError("checking topk_expert needs E (or split_sizes)")
         E = split_sizes.numel() if split_sizes is not None else k
     ref = next(t for t in (split_sizes, dest_row, src_token, topk_expert) if t is not None)
     status = torch.empty(1, dtype=torch.int32, device=ref.device)
