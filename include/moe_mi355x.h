@@ -627,9 +627,14 @@ int grouped_linear_bwd(int precision, int E, int N, int K, int64_t rows, const u
  * launch's stream (at most `capacity` launches; later ones are not traced).
  * After the stream has passed them, moe_trace_read(i, &name, &ms) returns the
  * i-th launch's kernel name (static string) and duration.  Enabling again
- * resets the count.  Not for concurrent use from several host threads.
+ * resets the count.  moe_trace_filter(prefix) restricts the trace to launches
+ * whose name starts with prefix (NULL or "" = every launch; it stays set until
+ * changed): each traced launch adds two event records to its stream, so a
+ * timed loop traces only the kernels it reports.  Not for concurrent use from
+ * several host threads.
  * Returns MOE_OK, MOE_ERR_ARG (bad capacity/index) or MOE_ERR_HIP.
  */
+void moe_trace_filter(const char* prefix);
 int moe_trace_enable(int capacity);
 void moe_trace_disable(void);
 int moe_trace_count(void);

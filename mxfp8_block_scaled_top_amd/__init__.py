@@ -89,6 +89,7 @@ def lib() -> ctypes.CDLL:
             "moe_workspace_region": (I32, [I32, I32, I64, I32, I32, I32, I32,
                                            ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
             "moe_trace_enable": (I32, [I32]),
+            "moe_trace_filter": (None, [ctypes.c_char_p]),
             "moe_trace_disable": (None, []),
             "moe_trace_count": (I32, []),
             "moe_trace_read": (I32, [I32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]),
@@ -526,6 +527,11 @@ def grouped_linear_bwd(dy, x, split_sizes, w, precision=MOE_BF16, want_dx=True, 
 def trace_enable(capacity: int) -> None:
     """Start recording one (name, duration) pair per kernel launch."""
     _check(lib().moe_trace_enable(capacity), "moe_trace_enable")
+
+
+def trace_filter(prefix=None) -> None:
+    """Trace only launches whose name starts with prefix (None: all)."""
+    lib().moe_trace_filter(prefix.encode() if prefix else None)
 
 
 def trace_disable() -> None:

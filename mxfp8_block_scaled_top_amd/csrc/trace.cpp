@@ -5,7 +5,10 @@
 // several host threads.
 #include <hip/hip_runtime.h>
 
+#include <string.h>
+
 #include <mutex>
+#include <string>
 #include <vector>
 
 #include "moe_mi355x.h"
@@ -19,6 +22,7 @@ struct TraceState {
     int count = 0;
     std::vector<hipEvent_t> ev;  // 2 per slot
     std::vector<const char*> names;
+    std::string prefix;          // only launches whose name starts with it
 };
 
 TraceState& st() {
@@ -34,6 +38,7 @@ TraceScope::TraceScope(const char* name, hipStream_t stream) : slot(-1), s(strea
     TraceState& t = st();
     std::lock_guard<std::mutex> g(t.mu);
     if (!t.on || t.count >= (int)t.names.size()) return;
+    if (!t.prefix.empty() && strncmp(name, t.prefix.c_str(), t.prefix.size()) != 0) return;
     slot = t.count++;
     t.names[slot] = name;
     if (hipEventRecord(t.ev[2 * slot], s) != hipSuccess) slot = -1;
@@ -65,6 +70,12 @@ int moe_trace_enable(int capacity) {
     t.count = 0;
     t.on = true;
     return MOE_OK;
+}
+
+void moe_trace_filter(const char* prefix) {
+    TraceState& t = st();
+    std::lock_guard<std::mutex> g(t.mu);
+    t.prefix = prefix ? prefix : "";
 }
 
 void moe_trace_disable(void) {
