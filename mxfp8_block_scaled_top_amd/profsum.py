@@ -174,9 +174,10 @@ def stats(args) -> None:
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     out = ["# Kernel time, rocprofv3 --kernel-trace --stats", "",
            "Command (from the repository root on one MI355X):", "", "```", args.cmd, "```", "",
-           f"Workload: {args.workload} layer step.  bench.py runs the layer step for warmup + "
-           "steps launches in each precision it is given; rows are kernel symbols (a GEMM symbol "
-           "names dtype and use; quant_tile covers every quantizer launch).", "",
+           f"Workload: {args.workload} layer step.  bench.py runs the layer step warmup + steps "
+           "times in each precision it is given, then min(3, steps) more times for the "
+           "non-GEMM kernels' event times; rows are kernel symbols (a GEMM symbol names dtype "
+           "and use; quant_tile covers every quantizer launch).", "",
            "| kernel | trace name | calls | average us | min us | max us | share of GPU time |",
            "|---|---|---|---|---|---|---|"]
     for r in rows:
