@@ -255,3 +255,23 @@ def test_deterministic_bf16_and_mx():
             assert torch.equal(a[key], b[key]), (prec, key)
         for e in range(4):
             assert torch.equal(a_dw1[e], b["dw1"][e])
+
+
+@pytest.mark.parametrize("precision", ALL, ids=IDS)
+def test_forward_only(precision):
+    """The forward alone (an inference step: route, dispatch, grouped MLP,
+    combine; no backward call) gives the oracle's forward."""
+    inp = _inputs(T=700, H=384, I=640, E=6, seed=12, dead=(4,))
+    dev = {n: (v.cuda() if isinstance(v, torch.Tensor) else [w.cuda() for w in v])
+           for n, v in inp.items()}
+    say(f"forward only, prec={PREC[precision]}")
+    got = layer_step(dev["logits"], dev["x"], dev["w1"], dev["w2"], dev["dy"], 2, precision,
+                     with_backward=False)
+    torch.cuda.synchronize()
+    assert "dx" not in got and "dxp" not in got
+    ref = omlp.layer_step(inp["logits"], inp["x"], inp["w1"], inp["w2"], inp["dy"], 2,
+                          PREC[precision], with_backward=False)
+    assert np.array_equal(np_(got["route"]["split_sizes"]), ref["route"]["split_sizes"])
+    err = rel_frob(got["y"], ref["y"])
+    say(f"  y error {err:.2e}")
+    assert err <= TOL[precision]
